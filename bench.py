@@ -1,0 +1,213 @@
+"""Throughput of the SimSD verification hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: the verification
+attention (RoPE copy, in-kernel tau mask, split-KV masked GQA attention and
+the LSE merge when the prompt is split) followed by the tau-ordered
+acceptance walk with its residual draw.  Workload: an SDAR-8B-shaped layer,
+batch 32, 32 query / 8 KV heads, head dim 128, prompt 4096, B = gamma = 8,
+bf16, acceptance over a 151936-token vocabulary.  Inputs are seeded random
+tensors generated on the GPU; two input sets larger than the last-level
+cache alternate so no step reads K/V that a previous step left in cache.
+
+Prints ONE JSON line.  `value` is verified candidates per second
+(batch * gamma per step).  `roofline` prices the verification call against
+the HBM peak using the algorithmic K/V bytes and its HIP-event duration on
+the launch stream; `cpu_baseline` times the fp64 oracle on a bounded sample
+of the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified candidates/sec and achieved HBM TB/s (KV read) at B=8, prompt 4096"
+WORKLOAD = "sdar8b_p4096_b8"
+VOCAB = 151936
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("diffusion_lm_speculative_amd/csrc/verify_mfma.hip",
+                  "diffusion_lm_speculative_amd/csrc/simsd_common.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_mfma_sdar8b_p4096_b8_traffic.json")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from committed rocprofv3 counters, if the kernel is unchanged since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(t_host, a_host, w, budget_s=12.0):
+    """Oracle (fp64 NumPy) over whole sequences until ~budget_s of host time."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from diffusion_lm_speculative_amd.synth import to_numpy64
+    from oracle.acceptance import accept_ref
+    from oracle.attention import verify_attn_ref
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    with threadpool_limits(limits=cores):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        avail = int(t_host["q_blk"].shape[0])
+        done = 0
+        t0 = time.perf_counter()
+        while done < avail and (done == 0 or time.perf_counter() - t0 < budget_s):
+            b = [done]
+            verify_attn_ref(to_numpy64(t_host["q_blk"][b]), to_numpy64(t_host["k_blk"][b]),
+                            to_numpy64(t_host["v_blk"][b]), to_numpy64(t_host["k_cache"][b]),
+                            to_numpy64(t_host["v_cache"][b]), t_host["prompt_len"][b].numpy(),
+                            t_host["tau"][b].numpy(), rope_base=w.rope_base)
+            accept_ref(a_host["p"][b].numpy(), a_host["q"][b].numpy(), a_host["draft_tok"][b].numpy(),
+                       a_host["tau"][b].numpy(), w.B, 1234, 0)
+            done += 1
+        dt = time.perf_counter() - t0
+    return {"value": done * w.B / dt, "unit": "candidates/s", "cores": int(min(used, cores)), "kind": "oracle",
+            "sample": f"{done} of {w.NB} sequences (verification attention of all 32 heads x {2 * w.B} rows over "
+                      f"{w.P}+{2 * w.B} keys, then the acceptance walk), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (this path has no multi-GPU "
+              "mode: each GPU would run its own share of sequences independently)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import diffusion_lm_speculative_amd as sd
+    from diffusion_lm_speculative_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[WORKLOAD]
+    gamma = w.B
+    stream = torch.cuda.current_stream()
+
+    # Two input sets (each ~537 MB of K/V, together > the 256 MB last-level cache).
+    sets = []
+    for i in range(2):
+        t = synth.make_verify_inputs(w, 1002 + 100 * i, device=dev)
+        a = synth.make_accept_inputs(w.NB, w.B, VOCAB, seed=2002 + 100 * i, device=dev)
+        out = torch.empty_like(t["q_blk"])
+        lse = torch.empty((w.NB, 2 * w.B, w.Hq), dtype=torch.float32, device=dev)
+        st = torch.empty((w.NB,), dtype=torch.int32, device=dev)
+        desc = sd.make_desc(t["q_blk"], t["k_blk"], t["k_cache"], rope_base=w.rope_base)
+        ws_bytes = sd.verify_workspace_bytes(desc)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        call = sd.bind_verify(t["q_blk"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], t["tau"],
+                              t["prompt_len"], None, out=out, lse=lse, status=st, workspace=ws, stream=stream,
+                              rope_base=w.rope_base)
+        n_acc = torch.empty((w.NB,), dtype=torch.int32, device=dev)
+        nxt = torch.empty((w.NB,), dtype=torch.int32, device=dev)
+        ast = torch.empty((w.NB,), dtype=torch.int32, device=dev)
+
+        def accept(a=a, n_acc=n_acc, nxt=nxt, ast=ast, i=i):
+            sd.accept_prefix(a["p"], a["q"], a["draft_tok"], a["tau"], gamma, 1234, i, n_accepted=n_acc,
+                             next_token=nxt, status=ast, stream=stream)
+
+        sets.append(dict(t=t, a=a, call=call, accept=accept, out=out, lse=lse, st=st, ws=ws, n_acc=n_acc,
+                         nxt=nxt, ast=ast))
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        s = sets[i % 2]
+        if ev is not None:
+            ev[0].record(stream)
+        s["call"]()
+        if ev is not None:
+            ev[1].record(stream)
+        s["accept"]()
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    for k, s in enumerate(sets):
+        if int(s["st"].abs().sum()) or int(s["ast"].abs().sum()):
+            raise RuntimeError(f"input set {k}: device status flags set: verify {s['st'].tolist()} "
+                               f"accept {s['ast'].tolist()}")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    verify_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    accept_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    v_avg = sum(verify_ms) / len(verify_ms)
+    a_avg = sum(accept_ms) / len(accept_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    kv_bytes = w.kv_bytes()
+    achieved_gbs = kv_bytes / (v_avg * 1e-3) / 1e9
+    desc = sd.make_desc(sets[0]["t"]["q_blk"], sets[0]["t"]["k_blk"], sets[0]["t"]["k_cache"], rope_base=w.rope_base)
+    traffic = measured_traffic()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        nb = min(w.NB, 8)
+        t_host = {k: v[:nb].cpu() for k, v in sets[0]["t"].items()}
+        a_host = {k: v[:nb].cpu() for k, v in sets[0]["a"].items()}
+        cpu = cpu_baseline(t_host, a_host, w)
+
+    rec = {
+        "metric": METRIC,
+        "value": w.NB * gamma / (ms_per_step * 1e-3),
+        "unit": "candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.25) q/k/v/cache, softmax(N(0,2)) p/q, random tau permutations)",
+        "config": {"workload": WORKLOAD, "batch": w.NB, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+                   "prompt_len": w.P, "B": w.B, "gamma": gamma, "vocab": VOCAB, "kv_chunk": 0},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "verify_mfma_kernel (+ lse merge when split)", "algorithmic_bytes": kv_bytes},
+        "kv_tb_per_s": achieved_gbs / 1e3,
+        "verify_us": {"mean": v_avg * 1e3, "median": verify_ms[len(verify_ms) // 2] * 1e3,
+                      "p90": verify_ms[int(len(verify_ms) * 0.9)] * 1e3},
+        "accept_us": {"mean": a_avg * 1e3, "median": accept_ms[len(accept_ms) // 2] * 1e3},
+        "workspace_bytes": sd.verify_workspace_bytes(desc),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

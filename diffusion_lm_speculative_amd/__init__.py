@@ -1,0 +1,17 @@
+"""SimSD verification hot path on MI355X (gfx950).
+
+The target model's single verification pass of SimSD-style speculative
+decoding for block diffusion LMs (page "SimSD - Simple Speculative Decoding
+in Diffusion Language Models"): grouped-query attention of the paired data /
+mask block rows over the prompt KV cache under the tau-driven temporal mask
+with RoPE copy, and the tau-ordered rejection-sampling acceptance.  The
+kernels are HIP for gfx950 behind the C ABI of include/simsd.h
+(libsimsd.so); this package is its thin Python binding.
+"""
+from ._lib import (  # noqa: F401
+    BF16, F32, IMPL_AUTO, IMPL_MFMA, IMPL_VALU, MASK_FULL, MASK_TEMPORAL, SimsdError,
+    ST_POS_NEG, ST_PROMPT_LEN, ST_TAU_NOT_PERM, ST_TAU_RANGE, ST_TOKEN_RANGE,
+)
+from .api import (  # noqa: F401
+    accept_prefix, bind_verify, debug_mask, debug_rope, make_desc, verify_attn, verify_workspace_bytes,
+)

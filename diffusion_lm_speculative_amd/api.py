@@ -1,0 +1,196 @@
+"""Python binding of the SimSD verification hot path (marshalling only).
+
+Each function checks that the torch tensors it is given match the C ABI of
+include/simsd.h (device, dtype, shape, contiguity), allocates outputs and
+workspace with torch when the caller does not pass them, and calls the
+library on the current HIP stream.  All arithmetic happens in the HIP
+kernels; there is no CPU path.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as L
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_DT = {torch.float32: L.F32, torch.bfloat16: L.BF16}
+
+
+def make_desc(q_blk, k_blk, k_cache, *, rope_base, softmax_scale=0.0, mask_mode=L.MASK_TEMPORAL,
+              impl=L.IMPL_AUTO, kv_chunk=0, p_max=None):
+    NB, twoB, Hq, d = q_blk.shape
+    Hkv = k_blk.shape[2]
+    if twoB % 2:
+        raise ValueError("q_blk rows must be 2B (D rows then D~ rows)")
+    if q_blk.dtype not in _DT:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    if p_max is None:
+        p_max = 0 if k_cache is None else k_cache.shape[2]
+    return L.VerifyDesc(NB, Hq, Hkv, d, twoB // 2, p_max, _DT[q_blk.dtype], int(mask_mode), int(impl),
+                        int(kv_chunk), float(rope_base), float(softmax_scale))
+
+
+def verify_workspace_bytes(desc) -> int:
+    n = ctypes.c_size_t(0)
+    L.check(L.load().simsd_verify_attn_workspace(ctypes.byref(desc), ctypes.byref(n)),
+            "simsd_verify_attn_workspace")
+    return int(n.value)
+
+
+def verify_attn(q_blk, k_blk, v_blk, k_cache, v_cache, tau, prompt_len=None, pos_d=None, *,
+                rope_base=10000.0, softmax_scale=0.0, mask_mode=L.MASK_TEMPORAL, impl=L.IMPL_AUTO,
+                kv_chunk=0, out=None, lse=None, status=None, workspace=None, stream=None,
+                with_lse=True, with_status=True):
+    """SimSD verification attention; returns (out, lse, status).
+
+    q_blk [NB][2B][Hq][d], k_blk/v_blk [NB][2B][Hkv][d], k_cache/v_cache
+    [NB][Hkv][P_max][d] (float32 or bfloat16, all the same), tau [NB][B]
+    int32, prompt_len [NB] int32 or None, pos_d [NB][B] int32 or None.
+    """
+    lib = L.load()
+    dt = q_blk.dtype
+    NB, twoB, Hq, d = q_blk.shape
+    Hkv = k_blk.shape[2]
+    B = twoB // 2
+    dev = q_blk.device
+    _need(q_blk, "q_blk", dt)
+    _need(k_blk, "k_blk", dt, (NB, twoB, Hkv, d), dev)
+    _need(v_blk, "v_blk", dt, (NB, twoB, Hkv, d), dev)
+    if k_cache is not None or v_cache is not None:
+        _need(k_cache, "k_cache", dt, None, dev)
+        _need(v_cache, "v_cache", dt, tuple(k_cache.shape), dev)
+        if tuple(k_cache.shape[:2]) != (NB, Hkv) or k_cache.shape[3] != d:
+            raise ValueError(f"k_cache must be [NB][Hkv][P_max][d], got {tuple(k_cache.shape)}")
+    _need(tau, "tau", torch.int32, (NB, B), dev)
+    if prompt_len is not None:
+        _need(prompt_len, "prompt_len", torch.int32, (NB,), dev)
+    if pos_d is not None:
+        _need(pos_d, "pos_d", torch.int32, (NB, B), dev)
+    desc = make_desc(q_blk, k_blk, k_cache, rope_base=rope_base, softmax_scale=softmax_scale,
+                     mask_mode=mask_mode, impl=impl, kv_chunk=kv_chunk)
+    if out is None:
+        out = torch.empty_like(q_blk)
+    _need(out, "out", dt, tuple(q_blk.shape), dev)
+    if lse is None and with_lse:
+        lse = torch.empty((NB, twoB, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (NB, twoB, Hq), dev)
+    if status is None and with_status:
+        status = torch.empty((NB,), dtype=torch.int32, device=dev)
+    if status is not None:
+        _need(status, "status", torch.int32, (NB,), dev)
+    ws_bytes = verify_workspace_bytes(desc)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.simsd_verify_attn(ctypes.byref(desc), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache),
+                               _ptr(v_cache), _ptr(prompt_len), _ptr(tau), _ptr(pos_d), _ptr(out), _ptr(lse),
+                               _ptr(status), _ptr(workspace), ctypes.c_size_t(ws_len), _stream_handle(stream))
+    L.check(rc, "simsd_verify_attn")
+    return out, lse, status
+
+
+@dataclass
+class VerifyCall:
+    """A verify_attn call with every pointer bound once (for timing loops).
+
+    `keep` holds the bound tensors so their memory outlives the call object.
+    """
+    desc: L.VerifyDesc
+    args: tuple
+    keep: tuple = ()
+
+    def __call__(self):
+        rc = L.load().simsd_verify_attn(ctypes.byref(self.desc), *self.args)
+        if rc:
+            L.check(rc, "simsd_verify_attn")
+
+
+def bind_verify(q_blk, k_blk, v_blk, k_cache, v_cache, tau, prompt_len=None, pos_d=None, *, out, lse=None,
+                status=None, workspace=None, stream=None, **desc_kw) -> VerifyCall:
+    desc = make_desc(q_blk, k_blk, k_cache, **desc_kw)
+    ws_bytes = verify_workspace_bytes(desc)
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        raise ValueError(f"workspace of {ws_bytes} bytes required")
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache), _ptr(v_cache), _ptr(prompt_len), _ptr(tau),
+            _ptr(pos_d), _ptr(out), _ptr(lse), _ptr(status), _ptr(workspace), ctypes.c_size_t(ws_len),
+            _stream_handle(stream))
+    keep = (q_blk, k_blk, v_blk, k_cache, v_cache, tau, prompt_len, pos_d, out, lse, status, workspace)
+    return VerifyCall(desc, args, keep)
+
+
+def accept_prefix(p_target, q_draft, draft_tok, tau, gamma, seed, offset=0, *, n_accepted=None, next_token=None,
+                  status=None, stream=None, with_next=True, with_status=True):
+    """tau-ordered rejection-sampling acceptance; returns (n_accepted, next_token, status)."""
+    lib = L.load()
+    NB, B, V = p_target.shape
+    dev = p_target.device
+    _need(p_target, "p_target", torch.float32)
+    _need(q_draft, "q_draft", torch.float32, (NB, B, V), dev)
+    _need(draft_tok, "draft_tok", torch.int32, (NB, B), dev)
+    _need(tau, "tau", torch.int32, (NB, B), dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((NB,), dtype=torch.int32, device=dev)
+    _need(n_accepted, "n_accepted", torch.int32, (NB,), dev)
+    if next_token is None and with_next:
+        next_token = torch.empty((NB,), dtype=torch.int32, device=dev)
+    if status is None and with_status:
+        status = torch.empty((NB,), dtype=torch.int32, device=dev)
+    rc = lib.simsd_accept_prefix(_ptr(p_target), _ptr(q_draft), _ptr(draft_tok), _ptr(tau), NB, B, int(gamma),
+                                 V, ctypes.c_uint64(int(seed)), ctypes.c_uint64(int(offset)), _ptr(n_accepted),
+                                 _ptr(next_token), _ptr(status), None, ctypes.c_size_t(0), _stream_handle(stream))
+    L.check(rc, "simsd_accept_prefix")
+    return n_accepted, next_token, status
+
+
+def debug_mask(tau, mask_mode=L.MASK_TEMPORAL, stream=None):
+    """Block visibility words [NB][2B][2] (int64 view of the uint64 bits)."""
+    lib = L.load()
+    NB, B = tau.shape
+    _need(tau, "tau", torch.int32)
+    bits = torch.zeros((NB, 2 * B, 2), dtype=torch.int64, device=tau.device)
+    L.check(lib.simsd_debug_mask(_ptr(tau), NB, B, int(mask_mode), _ptr(bits), _stream_handle(stream)),
+            "simsd_debug_mask")
+    return bits
+
+
+def debug_rope(q_blk, k_blk, prompt_len=None, pos_d=None, *, rope_base, p_max=0, stream=None):
+    """Rotated block rows (q_rot, k_rot) as the attention kernels use them."""
+    lib = L.load()
+    _need(q_blk, "q_blk", q_blk.dtype)
+    _need(k_blk, "k_blk", q_blk.dtype)
+    desc = make_desc(q_blk, k_blk, None, rope_base=rope_base, p_max=p_max)
+    q_rot = torch.empty_like(q_blk)
+    k_rot = torch.empty_like(k_blk)
+    L.check(lib.simsd_debug_rope(ctypes.byref(desc), _ptr(q_blk), _ptr(k_blk), _ptr(prompt_len), _ptr(pos_d),
+                                 _ptr(q_rot), _ptr(k_rot), _stream_handle(stream)), "simsd_debug_rope")
+    return q_rot, k_rot

@@ -1,0 +1,240 @@
+// Host side of the C ABI declared in include/simsd.h: argument validation
+// (before any HIP call), the split-KV plan, workspace carving and launches.
+#include <cmath>
+#include <cstring>
+
+#include "simsd_common.hpp"
+
+namespace simsd {
+namespace {
+
+constexpr int kKeyTile = 64;     // prompt keys per tile (both kernels iterate in multiples of it)
+constexpr int kTargetWgs = 512;  // default split target: about two resident workgroups per CU
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int make_plan(const simsd_verify_desc& d, Plan& pl) {
+  if (d.batch < 0 || d.n_q_heads < 1 || d.n_kv_heads < 1 || d.n_q_heads % d.n_kv_heads != 0 ||
+      (d.head_dim != 64 && d.head_dim != 128) || d.B < 0 || d.B > 64 || d.p_max < 0)
+    return SIMSD_ERR_SHAPE;
+  if (!(d.rope_base > 0.0) || !std::isfinite(d.rope_base) || !(d.softmax_scale >= 0.0f) ||
+      !std::isfinite(d.softmax_scale))
+    return SIMSD_ERR_SHAPE;
+  if ((d.dtype != SIMSD_F32 && d.dtype != SIMSD_BF16) ||
+      (d.mask_mode != SIMSD_MASK_TEMPORAL && d.mask_mode != SIMSD_MASK_FULL) ||
+      (d.impl != SIMSD_IMPL_AUTO && d.impl != SIMSD_IMPL_VALU && d.impl != SIMSD_IMPL_MFMA))
+    return SIMSD_ERR_DTYPE;
+  if (d.impl == SIMSD_IMPL_MFMA && d.dtype != SIMSD_BF16) return SIMSD_ERR_DTYPE;
+  if (d.kv_chunk < 0 || d.kv_chunk % kKeyTile != 0) return SIMSD_ERR_KV_CHUNK;
+
+  std::memset(&pl, 0, sizeof(pl));
+  pl.NB = d.batch;
+  pl.Hq = d.n_q_heads;
+  pl.Hkv = d.n_kv_heads;
+  pl.G = d.n_q_heads / d.n_kv_heads;
+  pl.d = d.head_dim;
+  pl.B = d.B;
+  pl.twoB = 2 * d.B;
+  pl.M = pl.G * pl.twoB;
+  pl.p_max = d.p_max;
+  pl.dtype = d.dtype;
+  pl.mask_mode = d.mask_mode;
+  pl.rope_base = d.rope_base;
+  const float scale = d.softmax_scale > 0.0f ? d.softmax_scale : 1.0f / std::sqrt(static_cast<float>(d.head_dim));
+  pl.scale_log2 = scale * kLog2e;
+  pl.impl = d.impl == SIMSD_IMPL_AUTO ? (d.dtype == SIMSD_BF16 ? SIMSD_IMPL_MFMA : SIMSD_IMPL_VALU) : d.impl;
+
+  if (pl.impl == SIMSD_IMPL_MFMA) {
+    // 16-row tiles; one wave per tile up to 8 waves, then two tiles per wave.
+    const int tiles = (pl.M + 15) / 16;
+    if (tiles <= 8) {
+      pl.rowt = 1;
+      int nw = 1;
+      while (nw < tiles) nw *= 2;
+      pl.threads = nw * 64;
+    } else {
+      pl.rowt = 2;
+      pl.threads = 8 * 64;
+    }
+    pl.rows_wg = (pl.threads / 64) * pl.rowt * 16;
+  } else {
+    pl.rowt = 1;
+    pl.threads = 256;
+    pl.rows_wg = 16;
+  }
+  pl.nrg = pl.M > 0 ? (pl.M + pl.rows_wg - 1) / pl.rows_wg : 1;
+
+  // Split the prompt so that the grid holds about kTargetWgs workgroups.
+  const int64_t tiles_max = (static_cast<int64_t>(pl.p_max) + kKeyTile - 1) / kKeyTile;
+  int64_t chunk;
+  if (d.kv_chunk > 0) {
+    chunk = d.kv_chunk;
+  } else if (tiles_max == 0) {
+    chunk = kKeyTile;
+  } else {
+    const int64_t per_split = static_cast<int64_t>(pl.NB) * pl.Hkv * pl.nrg;
+    int64_t ns = per_split > 0 ? (kTargetWgs + per_split - 1) / per_split : 1;
+    if (ns < 1) ns = 1;
+    if (ns > tiles_max) ns = tiles_max;
+    chunk = ((tiles_max + ns - 1) / ns) * kKeyTile;
+  }
+  int64_t nsplit = pl.p_max > 0 ? (pl.p_max + chunk - 1) / chunk : 1;
+  if (nsplit < 1) nsplit = 1;
+  if (chunk > (1 << 30) || nsplit > (1 << 20)) return SIMSD_ERR_SHAPE;
+  pl.chunk = static_cast<int>(chunk);
+  pl.nsplit = static_cast<int>(nsplit);
+  const int64_t grid = nsplit * pl.nrg * static_cast<int64_t>(pl.NB) * pl.Hkv;
+  if (grid > 0x7fffffffLL) return SIMSD_ERR_SHAPE;
+  if (pl.nsplit > 1) {
+    pl.part_o_floats = static_cast<size_t>(pl.NB) * pl.Hkv * pl.nsplit * pl.M * pl.d;
+    pl.part_ml_floats = static_cast<size_t>(pl.NB) * pl.Hkv * pl.nsplit * pl.M * 2;
+  }
+  return SIMSD_OK;
+}
+
+size_t workspace_bytes(const Plan& pl) {
+  if (pl.nsplit <= 1 || pl.NB == 0 || pl.B == 0) return 0;
+  return round_up(pl.part_o_floats * sizeof(float), 256) + round_up(pl.part_ml_floats * sizeof(float), 256);
+}
+
+}  // namespace
+}  // namespace simsd
+
+using namespace simsd;
+
+extern "C" {
+
+int simsd_abi_version(void) { return 1; }
+
+const char* simsd_strerror(int code) {
+  switch (code) {
+    case SIMSD_OK: return "ok";
+    case SIMSD_ERR_NULL: return "a required pointer is NULL";
+    case SIMSD_ERR_SHAPE: return "invalid shape or size";
+    case SIMSD_ERR_DTYPE: return "invalid dtype, mask mode or implementation";
+    case SIMSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SIMSD_ERR_GAMMA: return "gamma outside [0, B]";
+    case SIMSD_ERR_ALIGN: return "misaligned pointer";
+    case SIMSD_ERR_HIP: return "HIP error at launch";
+    case SIMSD_ERR_KV_CHUNK: return "kv_chunk must be a non-negative multiple of 64";
+    default: return "unknown error code";
+  }
+}
+
+int simsd_verify_attn_workspace(const simsd_verify_desc* desc, size_t* bytes) {
+  if (!desc || !bytes) return SIMSD_ERR_NULL;
+  Plan pl;
+  const int rc = make_plan(*desc, pl);
+  if (rc) return rc;
+  *bytes = workspace_bytes(pl);
+  return SIMSD_OK;
+}
+
+int simsd_verify_attn(const simsd_verify_desc* desc, const void* q_blk, const void* k_blk, const void* v_blk,
+                      const void* k_cache, const void* v_cache, const int32_t* prompt_len, const int32_t* tau,
+                      const int32_t* pos_d, void* out, float* lse, int32_t* status, void* workspace,
+                      size_t workspace_bytes_in, void* stream) {
+  if (!desc) return SIMSD_ERR_NULL;
+  Plan pl;
+  const int rc = make_plan(*desc, pl);
+  if (rc) return rc;
+  if (pl.NB == 0 || pl.B == 0) return SIMSD_OK;  // nothing to compute
+  if (!q_blk || !k_blk || !v_blk || !tau || !out) return SIMSD_ERR_NULL;
+  if (pl.p_max > 0 && (!k_cache || !v_cache)) return SIMSD_ERR_NULL;
+  if (!aligned(q_blk, 16) || !aligned(k_blk, 16) || !aligned(v_blk, 16) || !aligned(out, 16) ||
+      (k_cache && !aligned(k_cache, 16)) || (v_cache && !aligned(v_cache, 16)) || !aligned(tau, 4) ||
+      (prompt_len && !aligned(prompt_len, 4)) || (pos_d && !aligned(pos_d, 4)) || (lse && !aligned(lse, 4)) ||
+      (status && !aligned(status, 4)))
+    return SIMSD_ERR_ALIGN;
+  const size_t need = workspace_bytes(pl);
+  if (need > 0) {
+    if (!workspace || workspace_bytes_in < need) return SIMSD_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SIMSD_ERR_ALIGN;
+  }
+  VerifyArgs a;
+  a.q_blk = q_blk;
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.prompt_len = prompt_len;
+  a.tau = tau;
+  a.pos_d = pos_d;
+  a.out = out;
+  a.lse = lse;
+  a.status = status;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (need > 0) {
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         round_up(pl.part_o_floats * sizeof(float), 256));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = pl.impl == SIMSD_IMPL_MFMA ? launch_verify_mfma(pl, a, s) : launch_verify_valu(pl, a, s);
+  if (e != hipSuccess) return SIMSD_ERR_HIP;
+  if (pl.nsplit > 1) {
+    e = launch_merge(pl, a, s);
+    if (e != hipSuccess) return SIMSD_ERR_HIP;
+  }
+  return SIMSD_OK;
+}
+
+int simsd_accept_prefix_workspace(int32_t batch, int32_t B, int64_t vocab, size_t* bytes) {
+  if (!bytes) return SIMSD_ERR_NULL;
+  if (batch < 0 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31)) return SIMSD_ERR_SHAPE;
+  *bytes = 0;
+  return SIMSD_OK;
+}
+
+int simsd_accept_prefix(const float* p_target, const float* q_draft, const int32_t* draft_tok, const int32_t* tau,
+                        int32_t batch, int32_t B, int32_t gamma, int64_t vocab, uint64_t seed, uint64_t offset,
+                        int32_t* n_accepted, int32_t* next_token, int32_t* status, void* workspace,
+                        size_t workspace_bytes_in, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes_in;
+  if (batch < 0 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31)) return SIMSD_ERR_SHAPE;
+  if (gamma < 0 || gamma > B) return SIMSD_ERR_GAMMA;
+  if (batch == 0) return SIMSD_OK;
+  if (!n_accepted || (B > 0 && (!p_target || !q_draft || !draft_tok || !tau))) return SIMSD_ERR_NULL;
+  if (!aligned(n_accepted, 4) || (next_token && !aligned(next_token, 4)) || (status && !aligned(status, 4)) ||
+      (p_target && !aligned(p_target, 4)) || (q_draft && !aligned(q_draft, 4)) ||
+      (draft_tok && !aligned(draft_tok, 4)) || (tau && !aligned(tau, 4)))
+    return SIMSD_ERR_ALIGN;
+  const hipError_t e = launch_accept(p_target, q_draft, draft_tok, tau, batch, B, gamma, vocab, seed, offset,
+                                     n_accepted, next_token, status, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
+}
+
+int simsd_debug_mask(const int32_t* tau, int32_t batch, int32_t B, int32_t mask_mode, uint64_t* bits,
+                     void* stream) {
+  if (batch < 0 || B < 0 || B > 64) return SIMSD_ERR_SHAPE;
+  if (mask_mode != SIMSD_MASK_TEMPORAL && mask_mode != SIMSD_MASK_FULL) return SIMSD_ERR_DTYPE;
+  if (batch == 0 || B == 0) return SIMSD_OK;
+  if (!tau || !bits) return SIMSD_ERR_NULL;
+  if (!aligned(tau, 4) || !aligned(bits, 8)) return SIMSD_ERR_ALIGN;
+  return launch_debug_mask(tau, batch, B, mask_mode, bits, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SIMSD_OK
+             : SIMSD_ERR_HIP;
+}
+
+int simsd_debug_rope(const simsd_verify_desc* desc, const void* q_blk, const void* k_blk,
+                     const int32_t* prompt_len, const int32_t* pos_d, void* q_rot, void* k_rot, void* stream) {
+  if (!desc) return SIMSD_ERR_NULL;
+  Plan pl;
+  const int rc = make_plan(*desc, pl);
+  if (rc) return rc;
+  if (pl.NB == 0 || pl.B == 0) return SIMSD_OK;
+  if (!q_blk || !k_blk || !q_rot || !k_rot) return SIMSD_ERR_NULL;
+  if (!aligned(q_blk, 16) || !aligned(k_blk, 16) || !aligned(q_rot, 16) || !aligned(k_rot, 16) ||
+      (prompt_len && !aligned(prompt_len, 4)) || (pos_d && !aligned(pos_d, 4)))
+    return SIMSD_ERR_ALIGN;
+  return launch_debug_rope(pl, q_blk, k_blk, prompt_len, pos_d, q_rot, k_rot, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? SIMSD_OK
+             : SIMSD_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+// Device helpers shared by the verification kernels, the merge and the debug
+// exports: the tau-driven mask rows, per-sequence validation, RoPE-copy
+// angles, bf16 conversion and the split-KV plan.  Page: "SimSD - Simple
+// Speculative Decoding in Diffusion Language Models" (sections 1-3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/simsd.h"
+
+namespace simsd {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  __device__ static __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ static __forceinline__ float load(const uint16_t* p, size_t i) { return bf16_bits_to_f32(p[i]); }
+  __device__ static __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+};
+
+// ---------------------------------------------------------------- temporal mask
+// Visibility of the block columns for block row r (0 <= r < 2B), as two
+// B-bit words: dbits bit j = the row sees data token D_j, mbits bit j = the
+// row sees mask slot D~_j.  Section 2 of the page gives the mask-slot rows
+// (D_j when tau_j < tau_i, D~_j when tau_j >= tau_i); data rows see D_j with
+// tau_j <= tau_i and no slot.  `tau` may live in LDS or global memory.
+__device__ __forceinline__ void mask_row_bits(const int32_t* tau, int B, int r, int mode,
+                                              uint64_t& dbits, uint64_t& mbits) {
+  const uint64_t all = (B >= 64) ? ~0ull : ((1ull << B) - 1ull);
+  if (mode == SIMSD_MASK_FULL) {
+    dbits = all;
+    mbits = all;
+    return;
+  }
+  const bool slot_row = r >= B;
+  const int i = slot_row ? r - B : r;
+  const int ti = tau[i];
+  uint64_t d = 0, m = 0;
+  for (int j = 0; j < B; ++j) {
+    const int tj = tau[j];
+    const uint64_t bit = 1ull << j;
+    if (slot_row) {
+      if (tj < ti) d |= bit;
+      if (tj >= ti) m |= bit;
+    } else if (tj <= ti) {
+      d |= bit;
+    }
+  }
+  dbits = d;
+  mbits = m;
+}
+
+// Per-sequence validation of a verification call (flags of simsd.h).
+__device__ __forceinline__ int verify_seq_status(const int32_t* tau_b, int B, int plen, int p_max,
+                                                 const int32_t* pos_b) {
+  int st = 0;
+  for (int j = 0; j < B; ++j) {
+    const int t = tau_b[j];
+    if (t < 1 || t > B) st |= SIMSD_ST_TAU_RANGE;
+    if (pos_b && pos_b[j] < 0) st |= SIMSD_ST_POS_NEG;
+  }
+  if (plen < 0 || plen > p_max) st |= SIMSD_ST_PROMPT_LEN;
+  return st;
+}
+
+// ---------------------------------------------------------------- RoPE copy
+// Rotate-half RoPE: pair (x_f, x_{f+d/2}) turns by pos * base^(-2f/d).  The
+// angle and its sine/cosine are taken in fp64 (positions reach 1e4..1e5,
+// where an fp32 angle is off by ~1e-3 rad), then rounded to fp32.
+__device__ __forceinline__ float2 rope_cos_sin(int pos, int f, int d, double base) {
+  const double inv_freq = pow(base, -2.0 * static_cast<double>(f) / static_cast<double>(d));
+  const double theta = static_cast<double>(pos) * inv_freq;
+  double s, c;
+  sincos(theta, &s, &c);
+  return make_float2(static_cast<float>(c), static_cast<float>(s));
+}
+
+// Rotate one pair with a (cos, sin) from rope_cos_sin.  Written with explicit
+// fmas so every kernel and the debug export round identically.
+__device__ __forceinline__ void rope_apply(float x, float y, float2 cs, float& xo, float& yo) {
+  xo = fmaf(x, cs.x, -(y * cs.y));
+  yo = fmaf(y, cs.x, x * cs.y);
+}
+
+// Position of response position k of sequence b (D_k and D~_k share it).
+__device__ __forceinline__ int block_pos(const int32_t* pos_b, int plen, int k) {
+  return pos_b ? pos_b[k] : plen + k;
+}
+
+// ---------------------------------------------------------------- split-KV plan
+// Work of one launch: grid = nsplit * nrg * NB * Hkv workgroups.  Split s of
+// (b, kvh) covers prompt keys [s*chunk, min((s+1)*chunk, P_b)); split 0 also
+// owns the 2B block keys, so every row has at least one visible key in it.
+// With nsplit == 1 the kernel writes the final output; otherwise it writes
+// unnormalised partials (o, m, l) that the merge combines.
+struct Plan {
+  int NB, Hq, Hkv, G, d, B, twoB, M;  // M = G * 2B rows per KV head
+  int p_max, chunk, nsplit;
+  int rows_wg, nrg;                   // rows per workgroup, row groups per KV head
+  int threads;                        // threads per workgroup
+  int rowt;                           // MFMA: 16-row tiles per wave
+  int impl;                           // SIMSD_IMPL_VALU or SIMSD_IMPL_MFMA
+  int dtype, mask_mode;
+  double rope_base;
+  float scale_log2;                   // softmax scale * log2(e)
+  size_t part_o_floats, part_ml_floats;
+};
+
+struct VerifyArgs {
+  const void* q_blk;
+  const void* k_blk;
+  const void* v_blk;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* prompt_len;
+  const int32_t* tau;
+  const int32_t* pos_d;
+  void* out;
+  float* lse;
+  int32_t* status;
+  float* part_o;   // [NB*Hkv*nsplit][M][d]
+  float* part_ml;  // [NB*Hkv*nsplit][M][2]  (running max in log2 units, sum)
+};
+
+// Number of splits of (b) that hold a partial: split 0 always, split s >= 1
+// when it starts inside the prompt.
+__device__ __forceinline__ int valid_splits(int plen, int chunk, int nsplit) {
+  int n = (plen + chunk - 1) / chunk;
+  if (n < 1) n = 1;
+  return n < nsplit ? n : nsplit;
+}
+
+// Host-side launchers (one per translation unit).
+hipError_t launch_verify_valu(const Plan& pl, const VerifyArgs& a, hipStream_t s);
+hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s);
+hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s);
+hipError_t launch_accept(const float* p, const float* q, const int32_t* draft, const int32_t* tau,
+                         int NB, int B, int gamma, int64_t V, uint64_t seed, uint64_t offset,
+                         int32_t* n_acc, int32_t* next_tok, int32_t* status, hipStream_t s);
+hipError_t launch_debug_mask(const int32_t* tau, int NB, int B, int mode, uint64_t* bits, hipStream_t s);
+hipError_t launch_debug_rope(const Plan& pl, const void* q_blk, const void* k_blk,
+                             const int32_t* prompt_len, const int32_t* pos_d,
+                             void* q_rot, void* k_rot, hipStream_t s);
+
+}  // namespace simsd

@@ -1,0 +1,197 @@
+/*
+ * simsd.h -- C ABI of the SimSD verification hot path on MI355X (gfx950).
+ *
+ * The method (page "SimSD - Simple Speculative Decoding in Diffusion
+ * Language Models", gist.science summary of arXiv 2606.02544):
+ *   - section 1, input layout: after the prompt come a data section D of B
+ *     reference tokens and a mask section D~ of B [MASK] slots; D_k and D~_k
+ *     stand for the same response position, D_k gives context and D~_k is
+ *     where the logit is read;
+ *   - section 2, temporal attention mask: a permutation assigns every
+ *     response position a stage tau in 1..B; D~_i attends to D_j only when
+ *     tau(j) < tau(i) and to D~_j when tau(j) >= tau(i);
+ *   - section 3, position encoding alignment: D~_k reuses the RoPE index of
+ *     D_k;
+ *   - section 4, pipeline: one target forward computes the logits of all
+ *     candidates under that mask; acceptance is standard rejection sampling
+ *     walked in the drafted temporal order, committing the longest accepted
+ *     prefix.
+ *
+ * Conventions where the page is silent: every block row sees the whole
+ * prompt prefix [0, P_b); a data row D_i sees D_j when tau(j) <= tau(i) and
+ * no mask slot; RoPE is rotate-half with frequencies base^(-2f/d); the
+ * softmax scale defaults to 1/sqrt(d); query head h reads KV head
+ * h / (Hq/Hkv).
+ *
+ * General rules for every entry point:
+ *   - All array arguments are device pointers to contiguous, caller-owned
+ *     memory, 16-byte aligned (4-byte for int32 arrays), except the
+ *     descriptor and the size outputs of the *_workspace queries, which are
+ *     host pointers.  Inputs are never written; in particular the KV cache is
+ *     read-only.
+ *   - The library allocates nothing.  Scratch memory is a caller-provided
+ *     workspace sized by the matching *_workspace query.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the legacy
+ *     default stream) and never synchronise.  The library holds no state,
+ *     so concurrent calls on different streams with disjoint buffers are
+ *     safe.
+ *   - A negative return code means the host rejected the arguments before
+ *     any HIP call: nothing was launched.  SIMSD_ERR_HIP means a launch was
+ *     attempted and HIP reported an error.
+ *   - Per-sequence faults found on the device are written to status[b]
+ *     (0 = valid) when `status` is not NULL; a faulted sequence's outputs
+ *     are defined below.
+ */
+#ifndef SIMSD_H
+#define SIMSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---------------------------------------------------------------- */
+#define SIMSD_OK               0
+#define SIMSD_ERR_NULL        (-1) /* a required pointer is NULL */
+#define SIMSD_ERR_SHAPE       (-2) /* negative size, Hq % Hkv != 0, head_dim not 64/128, B > 64 */
+#define SIMSD_ERR_DTYPE       (-3) /* unknown dtype, mask mode or implementation */
+#define SIMSD_ERR_WORKSPACE   (-4) /* workspace NULL or smaller than the query says */
+#define SIMSD_ERR_GAMMA       (-5) /* gamma outside [0, B] */
+#define SIMSD_ERR_ALIGN       (-6) /* pointer not aligned as documented */
+#define SIMSD_ERR_HIP         (-7) /* HIP reported an error at launch */
+#define SIMSD_ERR_KV_CHUNK    (-8) /* kv_chunk not a non-negative multiple of 64 */
+
+/* ---- per-sequence device status flags (OR-ed together) --------------------------- */
+#define SIMSD_ST_TAU_RANGE     1   /* a stage label outside 1..B */
+#define SIMSD_ST_TAU_NOT_PERM  2   /* stage labels repeat (acceptance only) */
+#define SIMSD_ST_PROMPT_LEN    4   /* prompt_len[b] outside [0, p_max] */
+#define SIMSD_ST_TOKEN_RANGE   8   /* a walked draft token outside [0, vocab) */
+#define SIMSD_ST_POS_NEG      16   /* a negative RoPE position in pos_d */
+
+typedef enum { SIMSD_F32 = 0, SIMSD_BF16 = 1 } simsd_dtype;
+
+/* SIMSD_MASK_FULL makes every prompt and block column visible (plain
+ * bidirectional attention over [prompt; D; D~]); it exists to test the
+ * temporal mask against that special case. */
+typedef enum { SIMSD_MASK_TEMPORAL = 0, SIMSD_MASK_FULL = 1 } simsd_mask_mode;
+
+/* Kernel family.  AUTO picks the MFMA kernel for bf16 and the VALU kernel for
+ * fp32.  VALU works for both dtypes (it is the fp32 path and a cross-check). */
+typedef enum { SIMSD_IMPL_AUTO = 0, SIMSD_IMPL_VALU = 1, SIMSD_IMPL_MFMA = 2 } simsd_impl;
+
+typedef struct {
+  int32_t batch;        /* NB >= 0 */
+  int32_t n_q_heads;    /* Hq >= 1 */
+  int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;     /* d: 64 or 128 */
+  int32_t B;            /* section length 0..64; B == 0 is a valid no-op */
+  int32_t p_max;        /* KV-cache capacity per (sequence, KV head), >= 0 */
+  int32_t dtype;        /* simsd_dtype of q/k/v, cache and out */
+  int32_t mask_mode;    /* simsd_mask_mode */
+  int32_t impl;         /* simsd_impl */
+  int32_t kv_chunk;     /* prompt keys per split, multiple of 64; 0 = library picks */
+  double rope_base;     /* RoPE base, > 0 (1e4, 1e6, ...) */
+  float softmax_scale;  /* 0 => 1/sqrt(d) */
+} simsd_verify_desc;
+
+/* Workspace bytes that simsd_verify_attn needs for `desc` (may be 0).
+ * Host only; no HIP call.  Returns SIMSD_OK or a negative code. */
+int simsd_verify_attn_workspace(const simsd_verify_desc* desc, size_t* bytes);
+
+/* The verification attention of the SimSD pass (sections 1-3 above).
+ *
+ *  q_blk   [NB][2B][Hq][d]   rows 0..B-1 are D_0..D_{B-1}, rows B..2B-1 are
+ *                            D~_0..D~_{B-1}; not yet rotated.
+ *  k_blk   [NB][2B][Hkv][d]  same row order, not yet rotated.
+ *  v_blk   [NB][2B][Hkv][d]
+ *  k_cache [NB][Hkv][p_max][d] prompt keys at positions 0..P_b-1, already
+ *                            rotated (RoPE applied when they were cached).
+ *  v_cache [NB][Hkv][p_max][d]
+ *          (the caches may be NULL when p_max == 0)
+ *  prompt_len [NB] int32 P_b in [0, p_max], or NULL meaning p_max.
+ *  tau     [NB][B] int32 stage labels 1..B (a permutation; ties are
+ *                            tolerated: the mask rules stay well defined).
+ *  pos_d   [NB][B] int32 RoPE position of D_k, or NULL meaning P_b + k;
+ *                            D~_k always takes the same position.
+ *  out     [NB][2B][Hq][d]   softmax-weighted values, in `dtype`.
+ *  lse     [NB][2B][Hq] fp32 natural-log sum of exp of the scaled scores over
+ *                            the visible set, or NULL.
+ *  status  [NB] int32, or NULL: SIMSD_ST_TAU_RANGE, SIMSD_ST_PROMPT_LEN,
+ *                            SIMSD_ST_POS_NEG.  A faulted sequence gets zero
+ *                            `out` rows and lse = -inf.
+ *  workspace / workspace_bytes: scratch of at least the queried size (may be
+ *                            NULL when the query returned 0).
+ *
+ * Errors: SIMSD_ERR_NULL, _SHAPE, _DTYPE, _WORKSPACE, _ALIGN, _KV_CHUNK,
+ * _HIP as described above. */
+int simsd_verify_attn(const simsd_verify_desc* desc,
+                      const void* q_blk, const void* k_blk, const void* v_blk,
+                      const void* k_cache, const void* v_cache,
+                      const int32_t* prompt_len, const int32_t* tau, const int32_t* pos_d,
+                      void* out, float* lse, int32_t* status,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that simsd_accept_prefix needs (host only, no HIP call). */
+int simsd_accept_prefix_workspace(int32_t batch, int32_t B, int64_t vocab, size_t* bytes);
+
+/* Acceptance walk in tau order (section 4 above, read as textbook rejection
+ * sampling with residual resampling).
+ *
+ *  p_target [NB][B][V] fp32  target probabilities read at the D~_k slot,
+ *                            row k = response position k.
+ *  q_draft  [NB][B][V] fp32  draft probabilities for position k.
+ *  draft_tok [NB][B] int32   token placed in D_k.
+ *  tau      [NB][B] int32    permutation of 1..B.
+ *  gamma    0..B             stages walked: stage t = 1..gamma is position
+ *                            k_t with tau[k_t] = t.
+ *  seed, offset              Philox4x64-10 (Salmon et al., SC'11) key
+ *                            (seed, 0); the acceptance uniform of stage t of
+ *                            sequence b is the top 24 bits of word 0 at
+ *                            counter (b, t, 0, offset); stage t accepts iff
+ *                            u * q[x] < p[x], evaluated exactly in fp64.
+ *  n_accepted [NB] int32     accepted prefix length 0..gamma.
+ *  next_token [NB] int32     or NULL: at the first rejected stage n+1, a
+ *                            draw from max(0, p - q) (fp64 prefix sums; the
+ *                            uniform is the top 53 bits of word 0 at counter
+ *                            (b, n+1, 1, offset)); from p itself when that
+ *                            residual is all zero; -1 when n == gamma.
+ *  status   [NB] int32 or NULL: SIMSD_ST_TAU_RANGE, SIMSD_ST_TAU_NOT_PERM,
+ *                            SIMSD_ST_TOKEN_RANGE; a faulted sequence gets
+ *                            n_accepted = next_token = -1.
+ *
+ * Errors: SIMSD_ERR_NULL, _SHAPE (negative sizes, B > 64, vocab < 1 or
+ * >= 2^31), _GAMMA, _WORKSPACE, _ALIGN, _HIP. */
+int simsd_accept_prefix(const float* p_target, const float* q_draft,
+                        const int32_t* draft_tok, const int32_t* tau,
+                        int32_t batch, int32_t B, int32_t gamma, int64_t vocab,
+                        uint64_t seed, uint64_t offset,
+                        int32_t* n_accepted, int32_t* next_token, int32_t* status,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Export the block visibility that the attention kernels compute from tau,
+ * through the same device function (section 2 rules plus the data-row
+ * convention).  bits [NB][2B][2] uint64: word 0 bit j = row sees D_j, word 1
+ * bit j = row sees D~_j.  Errors: SIMSD_ERR_NULL, _SHAPE, _DTYPE, _HIP. */
+int simsd_debug_mask(const int32_t* tau, int32_t batch, int32_t B, int32_t mask_mode,
+                     uint64_t* bits, void* stream);
+
+/* Export the RoPE-copy rotation of the block rows exactly as the attention
+ * kernels feed it to their dot products (section 3): q_rot [NB][2B][Hq][d]
+ * and k_rot [NB][2B][Hkv][d] in desc->dtype.  Uses desc's shape, dtype and
+ * rope_base.  Errors as for simsd_verify_attn. */
+int simsd_debug_rope(const simsd_verify_desc* desc, const void* q_blk, const void* k_blk,
+                     const int32_t* prompt_len, const int32_t* pos_d,
+                     void* q_rot, void* k_rot, void* stream);
+
+/* Human-readable text for a return code (static storage). */
+const char* simsd_strerror(int code);
+
+/* ABI version of this header: 1. */
+int simsd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SIMSD_H */

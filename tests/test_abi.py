@@ -1,0 +1,180 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/simsd.h declares, and rejects invalid arguments on the host before
+any HIP call (so nothing is launched).
+
+Calls with made-up pointer values run only where no GPU is visible: they
+must never reach a launch, and on a machine without a GPU a launch could not
+touch memory anyway.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from diffusion_lm_speculative_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "simsd.h")
+
+no_gpu_only = pytest.mark.skipif(torch.cuda.is_available(),
+                                 reason="fake-pointer validation calls run only where no GPU is visible")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libsimsd.so is not built (run __graft_entry__.build())")
+    return L.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^\s*(?:int|const char\*)\s+(simsd_\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_declarations_match_binding():
+    decl = _declared()
+    assert decl == set(L.SIGNATURES), decl ^ set(L.SIGNATURES)
+    assert len(decl) == 8
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    raw = ctypes.CDLL(L.LIB_PATH)
+    for name in _declared():
+        assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
+
+
+def test_abi_version_and_strerror(lib):
+    assert lib.simsd_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+        assert lib.simsd_strerror(code)
+    assert lib.simsd_strerror(-99) == b"unknown error code"
+
+
+def _desc(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, B=4, p_max=256, dtype=L.BF16,
+                mask_mode=L.MASK_TEMPORAL, impl=L.IMPL_AUTO, kv_chunk=0, rope_base=1e6, softmax_scale=0.0)
+    base.update(kw)
+    return L.VerifyDesc(*[base[f] for f, _ in L.VerifyDesc._fields_])
+
+
+def _ws(lib, **kw):
+    n = ctypes.c_size_t(12345)
+    rc = lib.simsd_verify_attn_workspace(ctypes.byref(_desc(**kw)), ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=6, n_kv_heads=4), L.ERR_SHAPE),
+    (dict(head_dim=96), L.ERR_SHAPE),
+    (dict(B=65), L.ERR_SHAPE),
+    (dict(B=-1), L.ERR_SHAPE),
+    (dict(batch=-3), L.ERR_SHAPE),
+    (dict(p_max=-1), L.ERR_SHAPE),
+    (dict(rope_base=0.0), L.ERR_SHAPE),
+    (dict(rope_base=float("nan")), L.ERR_SHAPE),
+    (dict(softmax_scale=-1.0), L.ERR_SHAPE),
+    (dict(dtype=7), L.ERR_DTYPE),
+    (dict(mask_mode=2), L.ERR_DTYPE),
+    (dict(impl=3), L.ERR_DTYPE),
+    (dict(impl=L.IMPL_MFMA, dtype=L.F32), L.ERR_DTYPE),
+    (dict(kv_chunk=100), L.ERR_KV_CHUNK),
+    (dict(kv_chunk=-64), L.ERR_KV_CHUNK),
+])
+def test_workspace_query_rejects(lib, kw, code):
+    assert _ws(lib, **kw)[0] == code
+
+
+def test_workspace_query_sizes(lib):
+    # one split: no workspace
+    assert _ws(lib, kv_chunk=256) == (0, 0)
+    assert _ws(lib, p_max=0) == (0, 0)
+    assert _ws(lib, B=0) == (0, 0)
+    # two splits of 128 keys: partial o [NB*Hkv*2][M][d] and (m, l) [..][M][2], 256-byte aligned
+    NB, Hkv, M, d = 2, 2, 4 * 8, 128
+    rc, n = _ws(lib, kv_chunk=128)
+    ru = lambda x: (x + 255) // 256 * 256
+    assert rc == 0 and n == ru(NB * Hkv * 2 * M * d * 4) + ru(NB * Hkv * 2 * M * 2 * 4)
+    # default plan splits a long prompt; the size grows with the split count
+    rc1, n1 = _ws(lib, p_max=8192, batch=1)
+    assert rc1 == 0 and n1 > 0
+    assert lib.simsd_verify_attn_workspace(None, ctypes.byref(ctypes.c_size_t())) == L.ERR_NULL
+    assert lib.simsd_accept_prefix_workspace(4, 8, 151936, None) == L.ERR_NULL
+    n = ctypes.c_size_t(7)
+    assert lib.simsd_accept_prefix_workspace(4, 8, 151936, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.simsd_accept_prefix_workspace(4, 65, 151936, ctypes.byref(n)) == L.ERR_SHAPE
+    assert lib.simsd_accept_prefix_workspace(4, 8, 0, ctypes.byref(n)) == L.ERR_SHAPE
+
+
+A = 0x10000  # an aligned made-up address; never dereferenced
+
+
+def _verify(lib, desc, ptrs=None, ws=None, ws_bytes=0):
+    p = dict(q=A, k=A, v=A, kc=A, vc=A, plen=None, tau=A, pos=None, out=A, lse=None, st=None)
+    if ptrs:
+        p.update(ptrs)
+    return lib.simsd_verify_attn(ctypes.byref(desc) if desc is not None else None, p["q"], p["k"], p["v"],
+                                 p["kc"], p["vc"], p["plen"], p["tau"], p["pos"], p["out"], p["lse"], p["st"],
+                                 ws, ctypes.c_size_t(ws_bytes), None)
+
+
+@no_gpu_only
+def test_verify_rejects_on_host(lib):
+    d = _desc(kv_chunk=256)
+    assert _verify(lib, None) == L.ERR_NULL
+    assert _verify(lib, _desc(head_dim=80)) == L.ERR_SHAPE
+    for k in ("q", "k", "v", "tau", "out", "kc", "vc"):
+        assert _verify(lib, d, {k: None}) == L.ERR_NULL, k
+    for k, off in (("q", 8), ("k", 4), ("v", 2), ("kc", 8), ("vc", 8), ("out", 8), ("tau", 2), ("lse", 2),
+                   ("st", 1), ("plen", 2), ("pos", 3)):
+        assert _verify(lib, d, {k: A + off}) == L.ERR_ALIGN, k
+    # two splits need a workspace
+    d2 = _desc(kv_chunk=128)
+    assert _verify(lib, d2) == L.ERR_WORKSPACE
+    assert _verify(lib, d2, ws=A, ws_bytes=64) == L.ERR_WORKSPACE
+    rc, need = _ws(lib, kv_chunk=128)
+    assert _verify(lib, d2, ws=A + 16, ws_bytes=need) == L.ERR_ALIGN
+
+
+@no_gpu_only
+def test_verify_empty_is_noop(lib):
+    # B == 0 or batch == 0: valid, nothing to launch, pointers may be NULL
+    assert _verify(lib, _desc(B=0), dict(q=None, k=None, v=None, tau=None, out=None)) == 0
+    assert _verify(lib, _desc(batch=0), dict(q=None, k=None, v=None, tau=None, out=None)) == 0
+    # no prompt: caches may be NULL (still rejected here for a NULL output)
+    assert _verify(lib, _desc(p_max=0), dict(kc=None, vc=None, out=None)) == L.ERR_NULL
+
+
+@no_gpu_only
+def test_accept_rejects_on_host(lib):
+    def call(p=A, q=A, x=A, tau=A, NB=4, B=8, gamma=8, V=1000, n=A, nx=None, st=None):
+        return lib.simsd_accept_prefix(p, q, x, tau, NB, B, gamma, V, 1, 0, n, nx, st, None,
+                                       ctypes.c_size_t(0), None)
+    assert call(gamma=9) == L.ERR_GAMMA
+    assert call(gamma=-1) == L.ERR_GAMMA
+    assert call(B=65, gamma=1) == L.ERR_SHAPE
+    assert call(V=0) == L.ERR_SHAPE
+    assert call(V=1 << 31) == L.ERR_SHAPE
+    assert call(NB=-1) == L.ERR_SHAPE
+    assert call(NB=0, p=None, q=None, x=None, tau=None, n=None) == 0
+    for k in ("p", "q", "x", "tau", "n"):
+        assert call(**{k: None}) == L.ERR_NULL, k
+    for k in ("p", "q", "x", "tau", "n", "nx", "st"):
+        assert call(**{k: A + 2}) == L.ERR_ALIGN, k
+
+
+@no_gpu_only
+def test_debug_entry_points_reject_on_host(lib):
+    assert lib.simsd_debug_mask(A, 2, 65, 0, A, None) == L.ERR_SHAPE
+    assert lib.simsd_debug_mask(A, 2, 4, 5, A, None) == L.ERR_DTYPE
+    assert lib.simsd_debug_mask(None, 2, 4, 0, A, None) == L.ERR_NULL
+    assert lib.simsd_debug_mask(A, 2, 4, 0, A + 4, None) == L.ERR_ALIGN
+    assert lib.simsd_debug_mask(None, 0, 4, 0, None, None) == 0
+    d = _desc()
+    assert lib.simsd_debug_rope(None, A, A, None, None, A, A, None) == L.ERR_NULL
+    assert lib.simsd_debug_rope(ctypes.byref(d), None, A, None, None, A, A, None) == L.ERR_NULL
+    assert lib.simsd_debug_rope(ctypes.byref(d), A + 8, A, None, None, A, A, None) == L.ERR_ALIGN

@@ -1,0 +1,103 @@
+"""GPU parity of simsd_accept_prefix (through the C ABI) against the oracle.
+
+The accepted prefix length must match bit for bit (both sides draw the same
+Philox4x64-10 uniforms and make the exact fp64 comparison).  The replacement
+token must match, or, when the two sides' fp64 prefix sums round
+differently, sit on the same CDF boundary within 1e-12 of the total.
+"""
+import numpy as np
+import pytest
+import torch
+
+import diffusion_lm_speculative_amd as sd
+from diffusion_lm_speculative_amd import synth
+from oracle.acceptance import accept_ref
+from oracle.philox import philox4x64_10, uniform53
+from tests.gpu_helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _residual_draw_ok(p, q, kinv, n, b, seed, offset, got):
+    """True when `got` is a valid inverse-CDF pick at the oracle's threshold up to 1e-12 * total."""
+    ks = kinv[n + 1]
+    p64 = p[b, ks].astype(np.float64)
+    r = np.maximum(0.0, p64 - q[b, ks].astype(np.float64))
+    if not r.sum() > 0:
+        r = p64
+    c = np.cumsum(r)
+    s = c[-1]
+    thr = uniform53(philox4x64_10((b, n + 1, 1, offset), (seed, 0))[0]) * s
+    if got < 0 or got >= r.size or r[got] <= 0:
+        return False
+    lo = c[got - 1] if got > 0 else 0.0
+    return lo <= thr + 1e-12 * s and c[got] > thr - 1e-12 * s
+
+
+def _check(inp, gamma, seed, offset):
+    p, q, x, tau = inp["p"], inp["q"], inp["draft_tok"], inp["tau"]
+    NB, B, V = p.shape
+    print(f"accept NB={NB} B={B} V={V} gamma={gamma} seed={seed} offset={offset}", flush=True)
+    n, nx, st = sd.accept_prefix(p.to(dev()), q.to(dev()), x.to(dev()), tau.to(dev()), gamma, seed, offset)
+    torch.cuda.synchronize()
+    pn, qn = p.cpu().numpy(), q.cpu().numpy()
+    rn, rnx, rst = accept_ref(pn, qn, x.cpu().numpy(), tau.cpu().numpy(), gamma, seed, offset)
+    n, nx, st = n.cpu().numpy(), nx.cpu().numpy(), st.cpu().numpy()
+    assert np.array_equal(st, rst)
+    assert np.array_equal(n, rn), (n, rn)
+    ties = 0
+    for b in range(NB):
+        if nx[b] == rnx[b]:
+            continue
+        kinv = {int(t): k for k, t in enumerate(tau[b].tolist())}
+        assert _residual_draw_ok(pn, qn, kinv, int(n[b]), b, seed, offset, int(nx[b])), (b, nx[b], rnx[b])
+        ties += 1
+    print(f"  n histogram {np.bincount(n[n >= 0], minlength=gamma + 1).tolist()} boundary ties {ties}", flush=True)
+    return n, nx
+
+
+@pytest.mark.parametrize("NB,B,V,gamma", [(64, 8, 1000, 8), (40, 8, 1000, 3), (16, 4, 7, 4), (8, 64, 300, 64),
+                                          (5, 3, 100000, 0), (33, 16, 4099, 16)])
+def test_small(NB, B, V, gamma):
+    inp = synth.make_accept_inputs(NB, B, V, seed=NB * 100 + B)
+    for seed, offset in ((1, 0), (20261202, 7)):
+        _check(inp, gamma, seed, offset)
+
+
+def test_full_size_vocab():
+    # batch 64, B = gamma = 16, V = 151936, p and q softmax of N(0, 2) logits
+    w = synth.WORKLOADS["sdar8b_var16k_b16_accept"]
+    inp = synth.make_accept_inputs(w.NB, w.B, w.vocab, seed=1004, device=dev())
+    n, _ = _check(inp, w.gamma, seed=1004, offset=3)
+    assert n.max() >= 1
+
+
+def test_greedy_and_equal_distributions():
+    NB, B, V = 32, 8, 50
+    g = torch.Generator().manual_seed(3)
+    am = torch.randint(0, V, (NB, B), generator=g)
+    p = torch.zeros(NB, B, V)
+    p.scatter_(2, am[..., None], 1.0)
+    q = torch.full((NB, B, V), 1.0 / V)
+    x = torch.where(torch.rand(NB, B, generator=g) < 0.8, am, (am + 1) % V).to(torch.int32)
+    tau = torch.stack([torch.randperm(B, generator=g) + 1 for _ in range(NB)]).to(torch.int32)
+    n, nx = _check(dict(p=p, q=q, draft_tok=x, tau=tau), B, 5, 0)
+    order = torch.argsort(tau, dim=1)
+    for b in range(NB):
+        run = 0
+        for k in order[b].tolist():
+            if x[b, k] != am[b, k]:
+                break
+            run += 1
+        assert n[b] == run
+    n2, nx2 = _check(dict(p=p, q=p.clone(), draft_tok=am.to(torch.int32), tau=tau), B, 5, 0)
+    assert np.all(n2 == B) and np.all(nx2 == -1)
+
+
+def test_status_flags():
+    inp = synth.make_accept_inputs(4, 3, 20, seed=9)
+    inp["tau"] = torch.tensor([[1, 2, 3], [0, 2, 3], [1, 1, 3], [3, 2, 1]], dtype=torch.int32)
+    inp["draft_tok"] = inp["draft_tok"].clone()
+    inp["draft_tok"][3, 2] = 20
+    n, nx = _check(inp, 3, 1, 0)
+    assert n.tolist()[1:] == [-1, -1, -1]

@@ -1,0 +1,176 @@
+"""GPU parity of simsd_verify_attn (through the C ABI) against the fp64 oracle.
+
+Small cases cover several key tiles, ragged tails, forced prompt splits,
+every MFMA row-tiling variant, d = 64 and 128, B = 1 .. 64, variable prompt
+lengths (including 0), custom RoPE positions, the all-visible mode and
+faulted sequences.  The SDAR-shaped workloads run at full size in the
+launch configuration the benchmark times, compared on sampled sequences.
+Block-dominated cases (P = 0, 1, 17) and fp32 runs at SDAR head shapes make
+mask and RoPE mistakes visible despite the bf16 tolerance.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_lm_speculative_amd as sd
+from diffusion_lm_speculative_amd import synth
+from tests.gpu_helpers import compare, dev, gpu_inputs, oracle_for
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _w(name=None, **kw):
+    base = W[name] if name else W["sdar8b_p1024_b4"]
+    return dataclasses.replace(base, **kw)
+
+
+def _run(t, w, **kw):
+    out, lse, st = sd.verify_attn(t["q_blk"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], t["tau"],
+                                  t["prompt_len"], kw.pop("pos_d", None), rope_base=w.rope_base, **kw)
+    torch.cuda.synchronize()
+    return out, lse, st
+
+
+def _check(t, w, label, impl=0, kv_chunk=0, pos_d=None, mask_mode=0, b_idx=None):
+    print(f"case {label}: NB={t['q_blk'].shape[0]} Hq={w.Hq} Hkv={w.Hkv} d={w.d} P={t['k_cache'].shape[2]} "
+          f"B={w.B} {w.dtype} impl={impl} kv_chunk={kv_chunk}", flush=True)
+    out, lse, st = _run(t, w, impl=impl, kv_chunk=kv_chunk, pos_d=pos_d, mask_mode=mask_mode)
+    ref, ref_lse, ref_st = oracle_for(t, w, b_idx=b_idx, pos_d=pos_d, mask_mode=mask_mode)
+    sel = slice(None) if b_idx is None else list(b_idx)
+    assert np.array_equal(st[sel].cpu().numpy(), ref_st)
+    compare(out[sel], ref, w.dtype, label)
+    lse_ok = np.isfinite(ref_lse)
+    got_lse = lse[sel].double().cpu().numpy()
+    tol = 1e-5 if w.dtype == torch.float32 else 2e-2
+    assert np.all(np.isneginf(got_lse[~lse_ok]))
+    assert np.abs(got_lse[lse_ok] - ref_lse[lse_ok]).max(initial=0.0) <= tol
+    return out, lse, ref
+
+
+# ---------------------------------------------------------------- fp32 (VALU kernel)
+
+def test_tiny_fp32_workload():
+    w = W["tiny_fp32"]
+    _check(gpu_inputs(w, 1000), w, "tiny_fp32")
+
+
+@pytest.mark.parametrize("P,B,kv_chunk", [(300, 8, 0), (0, 8, 0), (17, 4, 0), (200, 5, 64)])
+def test_fp32_sdar_heads(P, B, kv_chunk):
+    w = _w(dtype=torch.float32, B=B, P=P, NB=2)
+    _check(gpu_inputs(w, 11 + P), w, f"fp32 sdar P={P} B={B}", kv_chunk=kv_chunk)
+
+
+# ---------------------------------------------------------------- bf16, both kernels
+
+SMALL = [
+    # (label, overrides)
+    ("ragged", dict(NB=3, Hq=8, Hkv=2, P=333, B=5)),
+    ("block_only", dict(NB=2, P=0, B=8)),
+    ("p1", dict(NB=2, P=1, B=8)),
+    ("p17", dict(NB=2, P=17, B=8)),
+    ("d64_g1", dict(NB=2, Hq=4, Hkv=4, d=64, P=200, B=3)),
+    ("b1", dict(NB=3, P=130, B=1)),
+    ("b64_g1", dict(NB=1, Hq=2, Hkv=2, P=100, B=64)),
+    ("b32_g4", dict(NB=1, Hq=8, Hkv=2, P=150, B=32)),       # 256 rows: two row tiles per wave
+    ("b64_g4", dict(NB=1, Hq=4, Hkv=1, P=70, B=64)),        # 512 rows: two row groups
+    ("g8_b2", dict(NB=2, Hq=16, Hkv=2, P=64, B=2)),
+    ("var_len", dict(NB=6, P=500, B=4, p_lo=0)),
+]
+
+
+@pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
+@pytest.mark.parametrize("label,ov", SMALL, ids=[s[0] for s in SMALL])
+def test_bf16_small(label, ov, impl):
+    w = _w(**ov)
+    _check(gpu_inputs(w, 7 + len(label)), w, f"{label} impl={impl}", impl=impl)
+
+
+@pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
+@pytest.mark.parametrize("kv_chunk", [64, 128, 192])
+def test_bf16_forced_splits(kv_chunk, impl):
+    w = _w(NB=5, Hq=8, Hkv=2, P=450, B=4, p_lo=0)
+    t = gpu_inputs(w, 31)
+    t["prompt_len"][0] = 0
+    t["prompt_len"][1] = 450
+    t["prompt_len"][2] = kv_chunk
+    _check(t, w, f"split {kv_chunk}", impl=impl, kv_chunk=kv_chunk)
+
+
+@pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
+def test_custom_positions_and_full_mode(impl):
+    w = _w(NB=3, Hq=8, Hkv=2, P=96, B=6)
+    t = gpu_inputs(w, 41)
+    g = torch.Generator().manual_seed(5)
+    pos_d = torch.stack([torch.randperm(6, generator=g) * 3 + 1000 for _ in range(3)]).to(torch.int32).to(dev())
+    _check(t, w, "pos_d", impl=impl, pos_d=pos_d)
+    _check(t, w, "full mode", impl=impl, mask_mode=sd.MASK_FULL)
+
+
+@pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
+def test_faulted_sequences(impl):
+    w = _w(NB=4, Hq=8, Hkv=2, P=80, B=4)
+    t = gpu_inputs(w, 51)
+    t["tau"][1, 2] = 9
+    t["prompt_len"][2] = 81
+    pos_d = (t["prompt_len"][:, None].long() + torch.arange(4, device=dev())).to(torch.int32)
+    pos_d[3, 0] = -5
+    for kv_chunk in (0, 64):
+        _check(t, w, f"faults chunk={kv_chunk}", impl=impl, kv_chunk=kv_chunk, pos_d=pos_d)
+    _, _, st = _run(t, w, impl=impl, pos_d=pos_d)
+    assert st.cpu().tolist() == [0, sd.ST_TAU_RANGE, sd.ST_PROMPT_LEN, sd.ST_POS_NEG]
+
+
+def test_mask_mistake_is_visible_in_block_dominated_case():
+    # With no prompt the block mask decides the result: the kernel must sit far
+    # closer to the temporal-mask oracle than to the all-visible one.
+    w = _w(NB=2, P=0, B=8)
+    t = gpu_inputs(w, 61)
+    out, _, _ = _run(t, w)
+    good, _, _ = oracle_for(t, w)
+    wrong, _, _ = oracle_for(t, w, mask_mode=sd.MASK_FULL)
+    g = synth.to_numpy64(out)
+    assert np.abs(g - good).mean() * 10 < np.abs(g - wrong).mean()
+
+
+def test_mfma_and_valu_agree_and_runs_are_deterministic():
+    w = _w(NB=2, Hq=32, Hkv=8, P=700, B=8)
+    t = gpu_inputs(w, 71)
+    a1, _, _ = _run(t, w, impl=sd.IMPL_MFMA)
+    a2, _, _ = _run(t, w, impl=sd.IMPL_MFMA)
+    v1, _, _ = _run(t, w, impl=sd.IMPL_VALU)
+    assert torch.equal(a1, a2)
+    assert (a1.float() - v1.float()).abs().max().item() < 2e-2
+
+
+def test_empty_inputs_are_noops():
+    w = _w(NB=2, P=64, B=0)
+    t = gpu_inputs(w, 81)
+    out, lse, st = _run(t, w)
+    assert out.numel() == 0
+    w = _w(NB=0, P=64, B=4)
+    t = gpu_inputs(w, 82)
+    out, lse, st = _run(t, w)
+    assert out.numel() == 0
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+FULL = [
+    ("sdar8b_p1024_b4", None),
+    ("sdar8b_p4096_b8", [0, 17, 31]),
+    ("sdar8b_p8192_b32", [0, 5]),
+    ("sdar8b_var16k_b16_accept", [0, 33, 63]),
+]
+
+
+@pytest.mark.parametrize("name,b_idx", FULL, ids=[f[0] for f in FULL])
+def test_full_size_workload(name, b_idx):
+    w = W[name]
+    t = gpu_inputs(w, 1000 + list(W).index(name), on_device=True)
+    _check(t, w, name, b_idx=b_idx)
+    del t
+    torch.cuda.empty_cache()
