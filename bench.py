@@ -128,13 +128,14 @@ def main():
         n_acc = torch.empty((w.NB,), dtype=torch.int32, device=dev)
         nxt = torch.empty((w.NB,), dtype=torch.int32, device=dev)
         ast = torch.empty((w.NB,), dtype=torch.int32, device=dev)
+        aws = torch.empty(max(sd.accept_workspace_bytes(w.NB, w.B, VOCAB), 256), dtype=torch.uint8, device=dev)
 
-        def accept(a=a, n_acc=n_acc, nxt=nxt, ast=ast, i=i):
+        def accept(a=a, n_acc=n_acc, nxt=nxt, ast=ast, aws=aws, i=i):
             sd.accept_prefix(a["p"], a["q"], a["draft_tok"], a["tau"], gamma, 1234, i, n_accepted=n_acc,
-                             next_token=nxt, status=ast, stream=stream)
+                             next_token=nxt, status=ast, workspace=aws, stream=stream)
 
         sets.append(dict(t=t, a=a, call=call, accept=accept, out=out, lse=lse, st=st, ws=ws, n_acc=n_acc,
-                         nxt=nxt, ast=ast))
+                         nxt=nxt, ast=ast, aws=aws))
     torch.cuda.synchronize()
 
     def step(i, ev=None):

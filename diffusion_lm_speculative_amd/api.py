@@ -148,8 +148,15 @@ def bind_verify(q_blk, k_blk, v_blk, k_cache, v_cache, tau, prompt_len=None, pos
     return VerifyCall(desc, args, keep)
 
 
+def accept_workspace_bytes(batch, B, vocab) -> int:
+    n = ctypes.c_size_t(0)
+    L.check(L.load().simsd_accept_prefix_workspace(int(batch), int(B), int(vocab), ctypes.byref(n)),
+            "simsd_accept_prefix_workspace")
+    return int(n.value)
+
+
 def accept_prefix(p_target, q_draft, draft_tok, tau, gamma, seed, offset=0, *, n_accepted=None, next_token=None,
-                  status=None, stream=None, with_next=True, with_status=True):
+                  status=None, workspace=None, stream=None, with_next=True, with_status=True):
     """tau-ordered rejection-sampling acceptance; returns (n_accepted, next_token, status)."""
     lib = L.load()
     NB, B, V = p_target.shape
@@ -163,11 +170,21 @@ def accept_prefix(p_target, q_draft, draft_tok, tau, gamma, seed, offset=0, *, n
     _need(n_accepted, "n_accepted", torch.int32, (NB,), dev)
     if next_token is None and with_next:
         next_token = torch.empty((NB,), dtype=torch.int32, device=dev)
+    if next_token is not None:
+        _need(next_token, "next_token", torch.int32, (NB,), dev)
     if status is None and with_status:
         status = torch.empty((NB,), dtype=torch.int32, device=dev)
+    if status is not None:
+        _need(status, "status", torch.int32, (NB,), dev)
+    if next_token is not None and workspace is None:
+        ws_bytes = accept_workspace_bytes(NB, B, V)
+        if ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib.simsd_accept_prefix(_ptr(p_target), _ptr(q_draft), _ptr(draft_tok), _ptr(tau), NB, B, int(gamma),
                                  V, ctypes.c_uint64(int(seed)), ctypes.c_uint64(int(offset)), _ptr(n_accepted),
-                                 _ptr(next_token), _ptr(status), None, ctypes.c_size_t(0), _stream_handle(stream))
+                                 _ptr(next_token), _ptr(status), _ptr(workspace), ctypes.c_size_t(ws_len),
+                                 _stream_handle(stream))
     L.check(rc, "simsd_accept_prefix")
     return n_accepted, next_token, status
 

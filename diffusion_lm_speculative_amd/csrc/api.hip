@@ -8,8 +8,10 @@
 namespace simsd {
 namespace {
 
-constexpr int kKeyTile = 64;     // prompt keys per tile (both kernels iterate in multiples of it)
-constexpr int kTargetWgs = 512;  // default split target: about two resident workgroups per CU
+constexpr int kKeyTile = 64;        // prompt keys per tile (both kernels iterate in multiples of it)
+constexpr int kNumCUs = 256;        // MI355X compute units
+constexpr size_t kLdsPerCu = 163840;  // bytes of LDS per CU (and per workgroup at most)
+constexpr int kMaxChunk = 4096;     // default split length cap (load balance of ragged prompts)
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -42,23 +44,25 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   pl.dtype = d.dtype;
   pl.mask_mode = d.mask_mode;
   pl.rope_base = d.rope_base;
+  for (int f = 0; f < d.head_dim / 2; ++f)
+    pl.inv_freq[f] = std::pow(d.rope_base, -2.0 * static_cast<double>(f) / static_cast<double>(d.head_dim));
   const float scale = d.softmax_scale > 0.0f ? d.softmax_scale : 1.0f / std::sqrt(static_cast<float>(d.head_dim));
   pl.scale_log2 = scale * kLog2e;
   pl.impl = d.impl == SIMSD_IMPL_AUTO ? (d.dtype == SIMSD_BF16 ? SIMSD_IMPL_MFMA : SIMSD_IMPL_VALU) : d.impl;
 
   if (pl.impl == SIMSD_IMPL_MFMA) {
-    // 16-row tiles; one wave per tile up to 8 waves, then two tiles per wave.
+    // Row waves of 16 rows each, up to 8 (128 rows; more rows take more row
+    // groups, which read the same K/V split at about the same time).  With
+    // fewer than 8 row waves each tile's keys are split over 2 or 4 waves so
+    // that every workgroup runs 4 to 8 waves.
     const int tiles = (pl.M + 15) / 16;
-    if (tiles <= 8) {
-      pl.rowt = 1;
-      int nw = 1;
-      while (nw < tiles) nw *= 2;
-      pl.threads = nw * 64;
-    } else {
-      pl.rowt = 2;
-      pl.threads = 8 * 64;
-    }
-    pl.rows_wg = (pl.threads / 64) * pl.rowt * 16;
+    int rw = 1;
+    while (rw < tiles && rw < 8) rw *= 2;
+    pl.ksplit = rw >= 8 ? 1 : (rw == 4 ? 2 : 4);
+    pl.rowt = 1;
+    pl.threads = rw * pl.ksplit * 64;
+    pl.rows_wg = rw * 16;
+    pl.nstage = (mfma_lds_bytes(pl.d, 4, pl.B) + 1024 > kLdsPerCu) ? 3 : 4;
   } else {
     pl.rowt = 1;
     pl.threads = 256;
@@ -66,7 +70,15 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   }
   pl.nrg = pl.M > 0 ? (pl.M + pl.rows_wg - 1) / pl.rows_wg : 1;
 
-  // Split the prompt so that the grid holds about kTargetWgs workgroups.
+  // Split the prompt so that the grid fills every CU about once: one MFMA
+  // workgroup per CU for head dim 128 (its LDS ring takes most of the CU),
+  // two for 64; the VALU kernel aims at two per CU.  Splits are capped at
+  // kMaxChunk keys so ragged prompt lengths still spread evenly.
+  int64_t target = 2 * kNumCUs;
+  if (pl.impl == SIMSD_IMPL_MFMA) {
+    const size_t per_wg = mfma_lds_bytes(pl.d, pl.nstage, pl.B) + 1024;
+    target = kNumCUs * static_cast<int64_t>(kLdsPerCu / per_wg);
+  }
   const int64_t tiles_max = (static_cast<int64_t>(pl.p_max) + kKeyTile - 1) / kKeyTile;
   int64_t chunk;
   if (d.kv_chunk > 0) {
@@ -75,10 +87,11 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
     chunk = kKeyTile;
   } else {
     const int64_t per_split = static_cast<int64_t>(pl.NB) * pl.Hkv * pl.nrg;
-    int64_t ns = per_split > 0 ? (kTargetWgs + per_split - 1) / per_split : 1;
+    int64_t ns = per_split > 0 ? (target + per_split - 1) / per_split : 1;
     if (ns < 1) ns = 1;
     if (ns > tiles_max) ns = tiles_max;
     chunk = ((tiles_max + ns - 1) / ns) * kKeyTile;
+    if (chunk > kMaxChunk) chunk = kMaxChunk;
   }
   int64_t nsplit = pl.p_max > 0 ? (pl.p_max + chunk - 1) / chunk : 1;
   if (nsplit < 1) nsplit = 1;
@@ -92,6 +105,15 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
     pl.part_ml_floats = static_cast<size_t>(pl.NB) * pl.Hkv * pl.nsplit * pl.M * 2;
   }
   return SIMSD_OK;
+}
+
+// Acceptance: fp64 (residual, target) sums per row segment.
+size_t accept_workspace_bytes(int NB, int B, int64_t V) {
+  if (NB == 0 || B == 0) return 0;
+  int nseg;
+  int64_t segsz;
+  accept_plan(NB, V, nseg, segsz);
+  return round_up(static_cast<size_t>(NB) * nseg * 2 * sizeof(double), 256);
 }
 
 size_t workspace_bytes(const Plan& pl) {
@@ -185,7 +207,7 @@ int simsd_verify_attn(const simsd_verify_desc* desc, const void* q_blk, const vo
 int simsd_accept_prefix_workspace(int32_t batch, int32_t B, int64_t vocab, size_t* bytes) {
   if (!bytes) return SIMSD_ERR_NULL;
   if (batch < 0 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31)) return SIMSD_ERR_SHAPE;
-  *bytes = 0;
+  *bytes = accept_workspace_bytes(batch, B, vocab);
   return SIMSD_OK;
 }
 
@@ -193,8 +215,6 @@ int simsd_accept_prefix(const float* p_target, const float* q_draft, const int32
                         int32_t batch, int32_t B, int32_t gamma, int64_t vocab, uint64_t seed, uint64_t offset,
                         int32_t* n_accepted, int32_t* next_token, int32_t* status, void* workspace,
                         size_t workspace_bytes_in, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes_in;
   if (batch < 0 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31)) return SIMSD_ERR_SHAPE;
   if (gamma < 0 || gamma > B) return SIMSD_ERR_GAMMA;
   if (batch == 0) return SIMSD_OK;
@@ -203,8 +223,14 @@ int simsd_accept_prefix(const float* p_target, const float* q_draft, const int32
       (p_target && !aligned(p_target, 4)) || (q_draft && !aligned(q_draft, 4)) ||
       (draft_tok && !aligned(draft_tok, 4)) || (tau && !aligned(tau, 4)))
     return SIMSD_ERR_ALIGN;
+  const size_t need = next_token ? accept_workspace_bytes(batch, B, vocab) : 0;
+  if (need > 0) {
+    if (!workspace || workspace_bytes_in < need) return SIMSD_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SIMSD_ERR_ALIGN;
+  }
   const hipError_t e = launch_accept(p_target, q_draft, draft_tok, tau, batch, B, gamma, vocab, seed, offset,
-                                     n_accepted, next_token, status, static_cast<hipStream_t>(stream));
+                                     n_accepted, next_token, status, static_cast<double*>(workspace),
+                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
 }
 

@@ -7,7 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/simsd.h"
+#include "simsd.h"
 
 namespace simsd {
 
@@ -42,9 +42,11 @@ template <> struct Elem<uint16_t> {
 // B-bit words: dbits bit j = the row sees data token D_j, mbits bit j = the
 // row sees mask slot D~_j.  Section 2 of the page gives the mask-slot rows
 // (D_j when tau_j < tau_i, D~_j when tau_j >= tau_i); data rows see D_j with
-// tau_j <= tau_i and no slot.  `tau` may live in LDS or global memory.
-__device__ __forceinline__ void mask_row_bits(const int32_t* tau, int B, int r, int mode,
-                                              uint64_t& dbits, uint64_t& mbits) {
+// tau_j <= tau_i and no slot.  `tau_at(j)` returns the stage of position j
+// (from memory, or from another lane's register).
+template <class TauAt>
+__device__ __forceinline__ void mask_row_bits_at(TauAt tau_at, int B, int r, int mode, uint64_t& dbits,
+                                                 uint64_t& mbits) {
   const uint64_t all = (B >= 64) ? ~0ull : ((1ull << B) - 1ull);
   if (mode == SIMSD_MASK_FULL) {
     dbits = all;
@@ -53,10 +55,10 @@ __device__ __forceinline__ void mask_row_bits(const int32_t* tau, int B, int r, 
   }
   const bool slot_row = r >= B;
   const int i = slot_row ? r - B : r;
-  const int ti = tau[i];
+  const int ti = tau_at(i);
   uint64_t d = 0, m = 0;
   for (int j = 0; j < B; ++j) {
-    const int tj = tau[j];
+    const int tj = tau_at(j);
     const uint64_t bit = 1ull << j;
     if (slot_row) {
       if (tj < ti) d |= bit;
@@ -67,6 +69,11 @@ __device__ __forceinline__ void mask_row_bits(const int32_t* tau, int B, int r, 
   }
   dbits = d;
   mbits = m;
+}
+
+__device__ __forceinline__ void mask_row_bits(const int32_t* tau, int B, int r, int mode, uint64_t& dbits,
+                                              uint64_t& mbits) {
+  mask_row_bits_at([tau](int j) { return tau[j]; }, B, r, mode, dbits, mbits);
 }
 
 // Per-sequence validation of a verification call (flags of simsd.h).
@@ -84,13 +91,22 @@ __device__ __forceinline__ int verify_seq_status(const int32_t* tau_b, int B, in
 
 // ---------------------------------------------------------------- RoPE copy
 // Rotate-half RoPE: pair (x_f, x_{f+d/2}) turns by pos * base^(-2f/d).  The
-// angle and its sine/cosine are taken in fp64 (positions reach 1e4..1e5,
-// where an fp32 angle is off by ~1e-3 rad), then rounded to fp32.
-__device__ __forceinline__ float2 rope_cos_sin(int pos, int f, int d, double base) {
-  const double inv_freq = pow(base, -2.0 * static_cast<double>(f) / static_cast<double>(d));
+// frequencies base^(-2f/d) are computed once on the host (fp64, in the
+// plan).  The angle is formed and reduced to [-pi, pi] in fp64 (positions
+// reach 1e4..1e5, where an fp32 angle is off by ~1e-3 rad): a two-constant
+// Cody-Waite reduction by 2*pi, exact to ~1e-16 rad for positions below
+// ~1e6, keeps the fp64 sine and cosine on their short path.  The results are
+// rounded to fp32.
+constexpr double kTwoPiHi = 6.28318530717958623200e+00;  // 2*pi rounded to double
+constexpr double kTwoPiLo = 2.44929359829470635445e-16;  // 2*pi - kTwoPiHi
+constexpr double kInvTwoPi = 1.59154943091895335769e-01;
+
+__device__ __forceinline__ float2 rope_cos_sin(int pos, double inv_freq) {
   const double theta = static_cast<double>(pos) * inv_freq;
+  const double k = rint(theta * kInvTwoPi);
+  const double red = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, theta));
   double s, c;
-  sincos(theta, &s, &c);
+  sincos(red, &s, &c);
   return make_float2(static_cast<float>(c), static_cast<float>(s));
 }
 
@@ -117,10 +133,13 @@ struct Plan {
   int p_max, chunk, nsplit;
   int rows_wg, nrg;                   // rows per workgroup, row groups per KV head
   int threads;                        // threads per workgroup
-  int rowt;                           // MFMA: 16-row tiles per wave
+  int rowt;                           // 16-row tiles per wave
+  int ksplit;                         // MFMA: waves sharing the keys of a tile
+  int nstage;                         // MFMA: LDS ring stages
   int impl;                           // SIMSD_IMPL_VALU or SIMSD_IMPL_MFMA
   int dtype, mask_mode;
   double rope_base;
+  double inv_freq[64];                // base^(-2f/d) for f < d/2
   float scale_log2;                   // softmax scale * log2(e)
   size_t part_o_floats, part_ml_floats;
 };
@@ -152,10 +171,12 @@ __device__ __forceinline__ int valid_splits(int plen, int chunk, int nsplit) {
 // Host-side launchers (one per translation unit).
 hipError_t launch_verify_valu(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s);
+size_t mfma_lds_bytes(int hd, int nstage, int B);
 hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s);
+void accept_plan(int NB, int64_t V, int& nseg, int64_t& segsz);
 hipError_t launch_accept(const float* p, const float* q, const int32_t* draft, const int32_t* tau,
                          int NB, int B, int gamma, int64_t V, uint64_t seed, uint64_t offset,
-                         int32_t* n_acc, int32_t* next_tok, int32_t* status, hipStream_t s);
+                         int32_t* n_acc, int32_t* next_tok, int32_t* status, double* seg_sums, hipStream_t s);
 hipError_t launch_debug_mask(const int32_t* tau, int NB, int B, int mode, uint64_t* bits, hipStream_t s);
 hipError_t launch_debug_rope(const Plan& pl, const void* q_blk, const void* k_blk,
                              const int32_t* prompt_len, const int32_t* pos_d,

@@ -133,7 +133,8 @@ int simsd_verify_attn(const simsd_verify_desc* desc,
                       void* out, float* lse, int32_t* status,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes that simsd_accept_prefix needs (host only, no HIP call). */
+/* Workspace bytes that simsd_accept_prefix needs when next_token is not NULL
+ * (host only, no HIP call): fp64 partial sums of the rejected rows. */
 int simsd_accept_prefix_workspace(int32_t batch, int32_t B, int64_t vocab, size_t* bytes);
 
 /* Acceptance walk in tau order (section 4 above, read as textbook rejection
@@ -160,6 +161,8 @@ int simsd_accept_prefix_workspace(int32_t batch, int32_t B, int64_t vocab, size_
  *  status   [NB] int32 or NULL: SIMSD_ST_TAU_RANGE, SIMSD_ST_TAU_NOT_PERM,
  *                            SIMSD_ST_TOKEN_RANGE; a faulted sequence gets
  *                            n_accepted = next_token = -1.
+ *  workspace / workspace_bytes: at least simsd_accept_prefix_workspace bytes,
+ *                            256-byte aligned, when next_token is not NULL.
  *
  * Errors: SIMSD_ERR_NULL, _SHAPE (negative sizes, B > 64, vocab < 1 or
  * >= 2^31), _GAMMA, _WORKSPACE, _ALIGN, _HIP. */

@@ -105,7 +105,10 @@ def test_workspace_query_sizes(lib):
     assert lib.simsd_verify_attn_workspace(None, ctypes.byref(ctypes.c_size_t())) == L.ERR_NULL
     assert lib.simsd_accept_prefix_workspace(4, 8, 151936, None) == L.ERR_NULL
     n = ctypes.c_size_t(7)
-    assert lib.simsd_accept_prefix_workspace(4, 8, 151936, ctypes.byref(n)) == 0 and n.value == 0
+    # fp64 (residual, target) sums per row segment: 512 / 4 = 128 segments per row (>= 4096 entries each)
+    assert lib.simsd_accept_prefix_workspace(4, 8, 151936, ctypes.byref(n)) == 0
+    assert n.value == (4 * 38 * 2 * 8 + 255) // 256 * 256
+    assert lib.simsd_accept_prefix_workspace(4, 0, 151936, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.simsd_accept_prefix_workspace(4, 65, 151936, ctypes.byref(n)) == L.ERR_SHAPE
     assert lib.simsd_accept_prefix_workspace(4, 8, 0, ctypes.byref(n)) == L.ERR_SHAPE
 
@@ -165,6 +168,8 @@ def test_accept_rejects_on_host(lib):
         assert call(**{k: None}) == L.ERR_NULL, k
     for k in ("p", "q", "x", "tau", "n", "nx", "st"):
         assert call(**{k: A + 2}) == L.ERR_ALIGN, k
+    # the residual draw (next_token != NULL) needs the workspace
+    assert call(nx=A) == L.ERR_WORKSPACE
 
 
 @no_gpu_only
