@@ -57,8 +57,7 @@ def measured_traffic():
 
 
 def cpu_baseline(t_host, a_host, w, budget_s=12.0):
-    """Oracle (fp64 NumPy) over whole sequences until ~budget_s of host time."""
-    import numpy as np
+    """Oracle (fp64 NumPy) over whole sequences until every sequence ran once and ~budget_s of host time passed."""
     from threadpoolctl import threadpool_info, threadpool_limits
 
     from diffusion_lm_speculative_amd.synth import to_numpy64
@@ -71,8 +70,8 @@ def cpu_baseline(t_host, a_host, w, budget_s=12.0):
         avail = int(t_host["q_blk"].shape[0])
         done = 0
         t0 = time.perf_counter()
-        while done < avail and (done == 0 or time.perf_counter() - t0 < budget_s):
-            b = [done]
+        while done < avail or time.perf_counter() - t0 < budget_s:
+            b = [done % avail]
             verify_attn_ref(to_numpy64(t_host["q_blk"][b]), to_numpy64(t_host["k_blk"][b]),
                             to_numpy64(t_host["v_blk"][b]), to_numpy64(t_host["k_cache"][b]),
                             to_numpy64(t_host["v_cache"][b]), t_host["prompt_len"][b].numpy(),
@@ -82,8 +81,28 @@ def cpu_baseline(t_host, a_host, w, budget_s=12.0):
             done += 1
         dt = time.perf_counter() - t0
     return {"value": done * w.B / dt, "unit": "candidates/s", "cores": int(min(used, cores)), "kind": "oracle",
-            "sample": f"{done} of {w.NB} sequences (verification attention of all 32 heads x {2 * w.B} rows over "
-                      f"{w.P}+{2 * w.B} keys, then the acceptance walk), {dt:.1f} s"}
+            "sample": f"{done} sequence passes cycling over the {avail} sequences of one input set (each: "
+                      f"verification attention of {w.Hq} heads x {2 * w.B} rows over {w.P}+{2 * w.B} keys, then the "
+                      f"acceptance walk with its residual draw), {dt:.1f} s"}
+
+
+def copy_calibration(torch, dev, mib, steps, warmup):
+    """A plain copy of known size: each launch reads and writes mib MiB once."""
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / max(steps, 1)
+    print(json.dumps({"copy_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4, "us_per_copy": us,
+                      "gbs_read_plus_write": 2 * n * 4 / (us * 1e-6) / 1e9}), flush=True)
 
 
 def main():
@@ -92,6 +111,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the bench, time a plain device-to-device copy of MIB MiB (the known-size "
+                         "reference that HBM byte counters are scaled by)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (this path has no multi-GPU "
@@ -107,6 +129,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, dev, args.copy_calibration, args.steps, args.warmup)
+        return
     w = synth.WORKLOADS[WORKLOAD]
     gamma = w.B
     stream = torch.cuda.current_stream()
@@ -149,13 +174,16 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
-    for i in range(args.warmup):
+    # one validation pass over each input set, then the untimed warmup
+    for i in range(len(sets)):
         step(i)
     torch.cuda.synchronize()
     for k, s in enumerate(sets):
         if int(s["st"].abs().sum()) or int(s["ast"].abs().sum()):
             raise RuntimeError(f"input set {k}: device status flags set: verify {s['st'].tolist()} "
                                f"accept {s['ast'].tolist()}")
+    for i in range(args.warmup):
+        step(i)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -177,7 +205,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        nb = min(w.NB, 8)
+        nb = w.NB
         t_host = {k: v[:nb].cpu() for k, v in sets[0]["t"].items()}
         a_host = {k: v[:nb].cpu() for k, v in sets[0]["a"].items()}
         cpu = cpu_baseline(t_host, a_host, w)
