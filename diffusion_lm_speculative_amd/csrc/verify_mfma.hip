@@ -10,7 +10,8 @@
 // Work decomposition.  One workgroup = (sequence b, KV head, prompt split,
 // row group).  All G query heads of the KV head and all 2B block rows share
 // every K/V byte, so the G*2B rows are packed into the M dimension and each
-// K/V tile crosses HBM once per split.  Each wave owns ROWT tiles of 16 rows.
+// K/V tile crosses HBM once per split.  The waves form RW row tiles of 16
+// rows times KSPLIT key splits of every tile.
 //
 // MFMA formulation (v_mfma_f32_16x16x32_bf16, wave64).  Scores are computed
 // transposed, S^T = K * Q^T, and the output as O^T += V^T * P^T.  In the
