@@ -44,8 +44,7 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   pl.dtype = d.dtype;
   pl.mask_mode = d.mask_mode;
   pl.rope_base = d.rope_base;
-  for (int f = 0; f < d.head_dim / 2; ++f)
-    pl.inv_freq[f] = std::pow(d.rope_base, -2.0 * static_cast<double>(f) / static_cast<double>(d.head_dim));
+  pl.log2_base = std::log2(d.rope_base);
   const float scale = d.softmax_scale > 0.0f ? d.softmax_scale : 1.0f / std::sqrt(static_cast<float>(d.head_dim));
   pl.scale_log2 = scale * kLog2e;
   pl.impl = d.impl == SIMSD_IMPL_AUTO ? (d.dtype == SIMSD_BF16 ? SIMSD_IMPL_MFMA : SIMSD_IMPL_VALU) : d.impl;
@@ -62,7 +61,16 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
     pl.rowt = 1;
     pl.threads = rw * pl.ksplit * 64;
     pl.rows_wg = rw * 16;
-    pl.nstage = (mfma_lds_bytes(pl.d, 4, pl.B) + 1024 > kLdsPerCu) ? 3 : 4;
+    // Four ring stages with the query rows staged in their own LDS region
+    // when that fits; else the query rows borrow the last stage during the
+    // prologue; else three stages.
+    if (mfma_lds_bytes(pl.d, 4, pl.B, pl.rows_wg, true) + 1024 <= kLdsPerCu) {
+      pl.nstage = 4;
+      pl.qsep = 1;
+    } else {
+      pl.nstage = mfma_lds_bytes(pl.d, 4, pl.B, pl.rows_wg, false) + 1024 <= kLdsPerCu ? 4 : 3;
+      pl.qsep = 0;
+    }
   } else {
     pl.rowt = 1;
     pl.threads = 256;
@@ -76,7 +84,7 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   // kMaxChunk keys so ragged prompt lengths still spread evenly.
   int64_t target = 2 * kNumCUs;
   if (pl.impl == SIMSD_IMPL_MFMA) {
-    const size_t per_wg = mfma_lds_bytes(pl.d, pl.nstage, pl.B) + 1024;
+    const size_t per_wg = mfma_lds_bytes(pl.d, pl.nstage, pl.B, pl.rows_wg, pl.qsep != 0) + 1024;
     target = kNumCUs * static_cast<int64_t>(kLdsPerCu / per_wg);
   }
   const int64_t tiles_max = (static_cast<int64_t>(pl.p_max) + kKeyTile - 1) / kKeyTile;

@@ -34,7 +34,7 @@ __global__ void debug_rope_kernel(Plan pl, const T* q_blk, const T* k_blk, const
   const size_t krow = (static_cast<size_t>(b) * pl.twoB + c) * pl.Hkv;
   for (int i = threadIdx.x; i < (pl.Hq + pl.Hkv) * half; i += blockDim.x) {
     const int h = i / half, f = i % half;
-    const float2 cs = rope_cos_sin(pos, pl.inv_freq[f]);
+    const float2 cs = rope_cos_sin(pos, rope_inv_freq(f, pl.d, pl.log2_base));
     const T* src;
     T* dst;
     if (h < pl.Hq) {

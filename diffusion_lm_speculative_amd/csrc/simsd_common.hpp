@@ -19,12 +19,10 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN).
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN): the language's
+// float -> __bf16 conversion, one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 template <typename T> struct Elem;
@@ -91,8 +89,9 @@ __device__ __forceinline__ int verify_seq_status(const int32_t* tau_b, int B, in
 
 // ---------------------------------------------------------------- RoPE copy
 // Rotate-half RoPE: pair (x_f, x_{f+d/2}) turns by pos * base^(-2f/d).  The
-// frequencies base^(-2f/d) are computed once on the host (fp64, in the
-// plan).  The angle is formed and reduced to [-pi, pi] in fp64 (positions
+// frequency is exp2(-(2f/d) * log2(base)) in fp64 (log2(base) from the host;
+// within a few ulp of base^(-2f/d), i.e. ~1e-10 rad at position 1e5).  The
+// angle is formed and reduced to [-pi, pi] in fp64 (positions
 // reach 1e4..1e5, where an fp32 angle is off by ~1e-3 rad): a two-constant
 // Cody-Waite reduction by 2*pi, exact to ~1e-16 rad for positions below
 // ~1e6, keeps the fp64 sine and cosine on their short path.  The results are
@@ -100,6 +99,10 @@ __device__ __forceinline__ int verify_seq_status(const int32_t* tau_b, int B, in
 constexpr double kTwoPiHi = 6.28318530717958623200e+00;  // 2*pi rounded to double
 constexpr double kTwoPiLo = 2.44929359829470635445e-16;  // 2*pi - kTwoPiHi
 constexpr double kInvTwoPi = 1.59154943091895335769e-01;
+
+__device__ __forceinline__ double rope_inv_freq(int f, int d, double log2_base) {
+  return exp2(-(2.0 * f / d) * log2_base);
+}
 
 __device__ __forceinline__ float2 rope_cos_sin(int pos, double inv_freq) {
   const double theta = static_cast<double>(pos) * inv_freq;
@@ -139,7 +142,8 @@ struct Plan {
   int impl;                           // SIMSD_IMPL_VALU or SIMSD_IMPL_MFMA
   int dtype, mask_mode;
   double rope_base;
-  double inv_freq[64];                // base^(-2f/d) for f < d/2
+  double log2_base;                   // log2(rope_base)
+  int qsep;                           // MFMA: query rows staged in their own LDS region
   float scale_log2;                   // softmax scale * log2(e)
   size_t part_o_floats, part_ml_floats;
 };
@@ -171,7 +175,7 @@ __device__ __forceinline__ int valid_splits(int plen, int chunk, int nsplit) {
 // Host-side launchers (one per translation unit).
 hipError_t launch_verify_valu(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s);
-size_t mfma_lds_bytes(int hd, int nstage, int B);
+size_t mfma_lds_bytes(int hd, int nstage, int B, int rows_wg, bool qsep);
 hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 void accept_plan(int NB, int64_t V, int& nseg, int64_t& segsz);
 hipError_t launch_accept(const float* p, const float* q, const int32_t* draft, const int32_t* tau,

@@ -100,25 +100,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Two transposed LDS reads (ds_read_b64_tr_b16) at byte addresses a0, a1.
-// Written as inline asm: the compiler treats the builtin as possibly aliasing
-// the in-flight direct-to-LDS loads and would drain them all (vmcnt 0) before
-// it.  The results must not be used before lds_read_wait().
+// Transposed LDS read (ds_read_b64_tr_b16) of the 8 bytes at byte address
+// a + OFF.  The ring loads are invisible to the compiler, so it waits only
+// for its own LDS traffic before the result is used.
 template <int OFF>
-__device__ __forceinline__ void tr_read_pair(uint32_t a0, uint32_t a1, bf16x4& lo, bf16x4& hi) {
-  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%4\n\tds_read_b64_tr_b16 %1, %3 offset:%4"
-               : "=&v"(lo), "=&v"(hi)
-               : "v"(a0), "v"(a1), "i"(OFF)
-               : "memory");
-}
-
-// Wait for every outstanding LDS read of this wave; tying the registers makes
-// the compiler keep their uses after the wait.
-__device__ __forceinline__ void lds_read_wait(bf16x4& a, bf16x4& b, bf16x4& c, bf16x4& d) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-}
-__device__ __forceinline__ void lds_read_wait(bf16x4& a, bf16x4& b) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+__device__ __forceinline__ bf16x4 tr_read(uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS immediate offset");
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<SIMSD_LDS bf16x4*>(static_cast<uintptr_t>(a + OFF)));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -134,9 +122,61 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
-template <int HD, int RW, int KSPLIT, int NSTAGE>
+// The same load from the wave-uniform base `base` (kept in SGPRs) plus the
+// per-lane byte offset `voff`.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// One direct-to-LDS load of 4 bytes per lane into LDS at m0 + 4*lane.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_bits(lo)) | (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Rotate the 8 pairs (x[e], y[e]) held as bf16 in wx / wy with the table
+// entries c4 (entry e: cos, sin at c4[e/2].xy or .zw) and round back to bf16.
+__device__ __forceinline__ void rotate8(const uint32_t (&wx)[4], const uint32_t (&wy)[4], const float4 (&c4)[4],
+                                        uint32_t (&ox)[4], uint32_t (&oy)[4]) {
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    float x0, y0, x1, y1;
+    rope_apply(bf16_lo(wx[e2]), bf16_lo(wy[e2]), make_float2(c4[e2].x, c4[e2].y), x0, y0);
+    rope_apply(bf16_hi(wx[e2]), bf16_hi(wy[e2]), make_float2(c4[e2].z, c4[e2].w), x1, y1);
+    ox[e2] = pack_bf16x2(x0, x1);
+    oy[e2] = pack_bf16x2(y0, y1);
+  }
+}
+
+// LDS layout of one workgroup (bytes): NSTAGE K tiles, NSTAGE V tiles, the
+// stage labels and positions (2 x 256), the query rows when they have their
+// own region, then the RoPE table of the B block positions.
+template <int HD, int NSTAGE, bool QSEP>
+struct Smem {
+  static constexpr int KREG = 0;
+  static constexpr int VREG = NSTAGE * Layout<HD>::TILEB;
+  static constexpr int TPREG = 2 * NSTAGE * Layout<HD>::TILEB;
+  static constexpr int QREG = TPREG + 512;
+  static constexpr int tab(int rows_wg) { return QREG + (QSEP ? rows_wg * Layout<HD>::ROWB : 0); }
+  // Byte offset of query row lr (0 <= lr < rows per workgroup) of the staging area.
+  static constexpr int qrow(int lr) {
+    return QSEP ? QREG + lr * Layout<HD>::ROWB
+                : (lr < KT ? KREG : VREG - KT * Layout<HD>::ROWB) + (NSTAGE - 1) * Layout<HD>::TILEB +
+                      lr * Layout<HD>::ROWB;
+  }
+};
+
+template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP>
 __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, VerifyArgs a) {
   using L = Layout<HD>;
+  using S = Smem<HD, NSTAGE, QSEP>;
   constexpr int NW = RW * KSPLIT;                // waves: RW row waves x KSPLIT key splits
   constexpr int NT = NW * 64;
   constexpr int HALF = HD / 2;
@@ -145,15 +185,20 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   constexpr int NSUB = 4 / KSPLIT;               // 16-key subtiles of a tile per wave
   constexpr int NU = (NSUB + 1) / 2;             // 32-key k-steps of O^T per wave
   constexpr int LPW = 2 * L::IPT / NW;           // direct-to-LDS loads per wave per tile
-  constexpr int KREG = 0;                        // K tiles of all stages
-  constexpr int VREG = NSTAGE * L::TILEB;        // then V tiles of all stages
+  constexpr int KREG = S::KREG;
+  constexpr int VREG = S::VREG;
+  constexpr int TABREG = S::tab(RW * 16);
+  constexpr int NPRO = QSEP ? NSTAGE : NSTAGE - 1;  // ring tiles issued before the query rows are read
+  constexpr int QI = RW * 16 / L::RPI;           // 1 KiB loads of the workgroup's query rows
   constexpr int XSTR = HD + 4;                   // floats per row of the key-split exchange buffer
   static_assert(KSPLIT == 1 || KSPLIT == 2 || KSPLIT == 4, "key split");
-  static_assert(NSTAGE >= 3, "the pipeline keeps two tiles resident");
+  static_assert(NSTAGE == 3 || NSTAGE == 4, "the pipeline keeps two tiles resident; at most 4 stages");
   static_assert(LPW * NW == 2 * L::IPT, "tile loads must split evenly over waves");
-  static_assert((NSTAGE - 2) * LPW <= 63, "too many loads in flight for vmcnt");
+  static_assert(NSTAGE * LPW <= 63, "too many loads in flight for vmcnt");
   static_assert((NSTAGE - 1) * L::TILEB < 65536, "stage offsets must fit the LDS immediate");
+  static_assert(QSEP || RW * 16 <= 2 * KT, "query rows must fit the last stage");
   static_assert((KSPLIT - 1) * RW * 16 * XSTR * 4 <= 2 * NSTAGE * L::TILEB, "exchange buffer fits the ring");
+  static_assert(NT % HALF == 0, "each lane keeps one RoPE frequency");
   // The running max moves only when a score exceeds it by more than this
   // (log2 units): probabilities stay below 2^8 and the rescale of the
   // accumulators is skipped for most tiles.
@@ -187,106 +232,124 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const size_t rout = (static_cast<size_t>(b) * twoB + r) * pl.Hq + kvh * pl.G + hh;
   const int c0 = s * pl.chunk;
   const bool has_block = (s == 0);
+  const int nbt = has_block ? (twoB + KT - 1) / KT : 0;  // block tiles, streamed after the prompt tiles
+  const int plen = a.prompt_len ? a.prompt_len[b] : pl.p_max;  // scalar load
+  const uint32_t sbase = lds_addr(smem);
 
-  // ---- the prologue's own loads, issued before the ring loads (a wave's
-  //      loads complete in issue order).
-  const int plen = a.prompt_len ? a.prompt_len[b] : pl.p_max;
-  // every wave keeps tau and the block positions in lanes 0..B-1
-  int tau_v = 1, pos_v = 0;
-  if (lane < B) {
-    tau_v = tau_b[lane];
-    if (pos_b) pos_v = pos_b[lane];
+  // ---- prologue loads, all direct to LDS and issued first (a wave's loads
+  //      complete in issue order, so waiting for all but the ring loads
+  //      waits for exactly these): stage labels and positions, then this
+  //      workgroup's query rows (granules swizzled like the ring tiles;
+  //      rows past M re-read row M-1).
+  if (wave == 0) {
+    const int lc = min(lane, B - 1);
+    dma4(tau_b + lc, sbase + S::TPREG);
+    if (pos_b) dma4(pos_b + lc, sbase + S::TPREG + 256);
   }
-  // the table loop below gives this lane frequency tid % HALF on every pass
-  const double lane_inv_freq = pl.inv_freq[tid % HALF];
-  uint4 qraw[KSTEPS];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q_blk) + rout * HD;
-#pragma unroll
-    for (int i = 0; i < KSTEPS; ++i)
-      qraw[i] = rok ? *reinterpret_cast<const uint4*>(qp + 32 * i + 8 * g) : make_uint4(0u, 0u, 0u, 0u);
+    const uint16_t* qg = static_cast<const uint16_t*>(a.q_blk);
+    for (int ins = wave; ins < QI; ins += NW) {
+      const int lr = ins * L::RPI + lane / L::GR;
+      int mq = rg * pl.rows_wg + lr;
+      if (mq >= pl.M) mq = pl.M - 1;
+      const size_t ro = (static_cast<size_t>(b) * twoB + mq % twoB) * pl.Hq + kvh * pl.G + mq / twoB;
+      const int gsrc = (lane % L::GR) ^ (lr & (L::GR - 1));
+      dma16(qg + ro * HD + gsrc * 8, sbase + S::qrow(ins * L::RPI));
+    }
   }
-  // raw block rows of the first block tile: K as (first half, second half)
-  // granule pairs, V as granules
-  constexpr int KITEMS = (KT * (L::GR / 2) + NT - 1) / NT;
-  constexpr int VITEMS = (KT * L::GR + NT - 1) / NT;
-  const uint16_t* kblk = static_cast<const uint16_t*>(a.k_blk);
-  const uint16_t* vblk = static_cast<const uint16_t*>(a.v_blk);
-  auto load_block = [&](int bt, uint4 (&kx)[KITEMS], uint4 (&ky)[KITEMS], uint4 (&vv)[VITEMS]) {
-#pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      const int i = tid + it * NT;
-      const int row = i / (L::GR / 2), j = i % (L::GR / 2), c = bt * KT + row;
-      kx[it] = ky[it] = make_uint4(0u, 0u, 0u, 0u);
-      if (i < KT * (L::GR / 2) && c < twoB) {
-        const uint16_t* kp = kblk + ((static_cast<size_t>(b) * twoB + c) * pl.Hkv + kvh) * HD;
-        kx[it] = *reinterpret_cast<const uint4*>(kp + 8 * j);
-        ky[it] = *reinterpret_cast<const uint4*>(kp + HALF + 8 * j);
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-      const int i = tid + it * NT;
-      const int row = i / L::GR, j = i % L::GR, c = bt * KT + row;
-      vv[it] = make_uint4(0u, 0u, 0u, 0u);
-      if (i < KT * L::GR && c < twoB)
-        vv[it] = *reinterpret_cast<const uint4*>(vblk + ((static_cast<size_t>(b) * twoB + c) * pl.Hkv + kvh) * HD + 8 * j);
-    }
-  };
-  uint4 bkx[KITEMS], bky[KITEMS], bvv[VITEMS];
-  if (has_block) load_block(0, bkx, bky, bvv);
 
+  // ---- ring loads.  Lane `lane` of load instruction `ins` fills LDS
+  //      granule position lane%GR of tile row ins*RPI + lane/GR, i.e. global
+  //      granule (pos ^ row) of that row.  Prompt tile t covers keys
+  //      c0 + 64t ..; in a tile that ends past `lim` the rows beyond it
+  //      re-read key lim-1 (finite values; their scores are masked).  Tile
+  //      ntl + bt is block tile bt: block rows 64bt.. of this KV head's K and
+  //      V (rows past 2B re-read row 2B-1), rotated in LDS once landed.
   const size_t cache_base = (static_cast<size_t>(b) * pl.Hkv + kvh) * static_cast<size_t>(pl.p_max) * HD;
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + cache_base;
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + cache_base;
-
-  // ---- direct-to-LDS loads.  Lane `lane` of load instruction `ins` fills
-  //      LDS granule position lane%GR of tile row ins*RPI + lane/GR, i.e.
-  //      global granule (pos ^ row) of that cache row.  In a tile that ends
-  //      past `lim`, rows beyond it re-read key lim-1 (finite values; their
-  //      scores are masked).  The last stage is the block's until the first
-  //      refill, which follows a barrier.
-  int grow[LPW], gcol[LPW];
+  const uint16_t* kblk = static_cast<const uint16_t*>(a.k_blk);
+  const uint16_t* vblk = static_cast<const uint16_t*>(a.v_blk);
+  // per-lane byte offset of load mm inside a full tile: row grow, granule (pos ^ row)
+  uint32_t goff[LPW];
 #pragma unroll
   for (int mm = 0; mm < LPW; ++mm) {
     const int ins = wave * LPW + mm;
     const int ii = ins >= L::IPT ? ins - L::IPT : ins;
-    grow[mm] = ii * L::RPI + lane / L::GR;
-    gcol[mm] = ((lane % L::GR) ^ (grow[mm] & (L::GR - 1))) * 8;
+    const int grow = ii * L::RPI + lane / L::GR;
+    goff[mm] = grow * L::ROWB + (((lane % L::GR) ^ (grow & (L::GR - 1))) << 4);
   }
-  auto issue = [&](auto st_c, int t, int lim) {
+  const size_t blk_row = static_cast<size_t>(pl.Hkv) * HD;  // elements between block rows
+  const uint16_t* kblk_b = kblk + (static_cast<size_t>(b) * twoB * pl.Hkv + kvh) * HD;
+  const uint16_t* vblk_b = vblk + (static_cast<size_t>(b) * twoB * pl.Hkv + kvh) * HD;
+  auto issue = [&](auto st_c, int t, int ntl, int lim) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
-    const int kb = c0 + t * KT;
-    const bool full = kb + KT <= lim;
+    if (t < ntl) {
+      const int kb = c0 + t * KT;
+      const bool full = kb + KT <= lim;
+      const uint16_t* ktile = kc + static_cast<size_t>(kb) * HD;
+      const uint16_t* vtile = vc + static_cast<size_t>(kb) * HD;
 #pragma unroll
-    for (int mm = 0; mm < LPW; ++mm) {
-      const int ins = wave * LPW + mm;
-      const bool isv = ins >= L::IPT;
-      const int ii = isv ? ins - L::IPT : ins;
-      const uint16_t* tile = (isv ? vc : kc) + static_cast<size_t>(kb) * HD;
-      const uint16_t* src = full ? tile + (grow[mm] * HD + gcol[mm])
-                                 : tile + ((min(kb + grow[mm], lim - 1) - kb) * HD + gcol[mm]);
-      dma16(src, lds_addr(smem) + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024);
+      for (int mm = 0; mm < LPW; ++mm) {
+        const int ins = wave * LPW + mm;
+        const bool isv = ins >= L::IPT;
+        const int ii = isv ? ins - L::IPT : ins;
+        uint32_t off = goff[mm];
+        if (!full) {
+          const int row = static_cast<int>(off / L::ROWB);
+          off = (min(kb + row, lim - 1) - kb) * L::ROWB + off % L::ROWB;
+        }
+        dma16s(isv ? vtile : ktile, off, sbase + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024);
+      }
+    } else {
+      const int bt = t - ntl;
+#pragma unroll
+      for (int mm = 0; mm < LPW; ++mm) {
+        const int ins = wave * LPW + mm;
+        const bool isv = ins >= L::IPT;
+        const int ii = isv ? ins - L::IPT : ins;
+        const int c = min(bt * KT + static_cast<int>(goff[mm] / L::ROWB), twoB - 1);
+        const uint32_t off = static_cast<uint32_t>(c * blk_row * 2) + goff[mm] % L::ROWB;
+        dma16s(isv ? vblk_b : kblk_b, off, sbase + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024);
+      }
     }
   };
+  // tiles [from, to) of the ring, to <= NSTAGE
+  auto issue_range = [&](int from, int to, int ntl, int lim) __attribute__((always_inline)) {
+    if (from <= 0 && 0 < to) issue(IC<0>{}, 0, ntl, lim);
+    if (from <= 1 && 1 < to) issue(IC<1>{}, 1, ntl, lim);
+    if (from <= 2 && 2 < to) issue(IC<2>{}, 2, ntl, lim);
+    if (NSTAGE > 3 && from <= 3 && 3 < to) issue(IC<(NSTAGE > 3 ? 3 : 0)>{}, 3, ntl, lim);
+  };
 
-  // The prologue's loads must be complete before the ring loads go out: the
-  // compiler counts only its own loads, so a wait it placed for them later
-  // would also wait for every ring load issued in between.  Then the first
-  // ring tiles go in flight, before prompt_len is known, assuming the whole
-  // cache capacity (always in bounds); the real length masks them.  Every
-  // exit below drains them first.
-  wait_counts<0, 15>();
-  {
-    const int c1s = min(c0 + pl.chunk, pl.p_max);
-    const int nts = c1s > c0 ? (c1s - c0 + KT - 1) / KT : 0;
-    if (nts > 0) issue(IC<0>{}, 0, c1s);
-    if (nts > 1) issue(IC<1>{}, 1, c1s);
-    if (NSTAGE > 3 && nts > 2) issue(IC<(NSTAGE > 3 ? 2 : 0)>{}, 2, c1s);
+  // The first prompt tiles go in flight before prompt_len is known, assuming
+  // the whole cache capacity (always in bounds).
+  const int c1s = min(c0 + pl.chunk, pl.p_max);
+  const int nts = c1s > c0 ? (c1s - c0 + KT - 1) / KT : 0;
+  const int nspec = min(NPRO, nts);
+  issue_range(0, nspec, nts, c1s);
+  const double lane_inv_freq = rope_inv_freq(tid % HALF, HD, pl.log2_base);
+
+  // ---- wait for the prologue loads only, then share them
+  if (NSTAGE > 3 && nspec >= 4)
+    wait_counts<(NSTAGE > 3 ? 4 : 0) * LPW, 15>();
+  else if (nspec >= 3)
+    wait_counts<3 * LPW, 15>();
+  else if (nspec == 2)
+    wait_counts<2 * LPW, 15>();
+  else if (nspec == 1)
+    wait_counts<LPW, 15>();
+  else
+    wait_counts<0, 15>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  const int32_t* tp = reinterpret_cast<const int32_t*>(smem + S::TPREG);
+  int tau_v = 1, pos_v = 0;  // lanes 0..B-1 of every wave hold tau and the block positions
+  if (lane < B) {
+    tau_v = tp[lane];
+    pos_v = pos_b ? tp[64 + lane] : plen + lane;
   }
-
-  // ---- validation from the lanes' copies of tau and the positions
-  if (!pos_b) pos_v = plen + lane;
   const bool bad_tau = lane < B && (tau_v < 1 || tau_v > B);
   const bool bad_pos = lane < B && pos_v < 0;
   int st = (__any(bad_tau) ? SIMSD_ST_TAU_RANGE : 0) | (__any(bad_pos) ? SIMSD_ST_POS_NEG : 0);
@@ -294,7 +357,8 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const bool status_writer = a.status && kvh == 0 && s == 0 && rg == 0 && tid == 0;
   const int c1 = min(c0 + pl.chunk, plen);
   const int ntiles = c1 > c0 ? (c1 - c0 + KT - 1) / KT : 0;
-  if (st || (ntiles == 0 && !has_block)) {
+  const int T = ntiles + nbt;
+  if (st || T == 0) {
     wait_counts<0, 15>();  // drain the ring loads before the workgroup's LDS is released
     if (status_writer) a.status[b] = st;
     if (st && pl.nsplit == 1 && rok && ks == 0) {
@@ -305,15 +369,22 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     }
     return;
   }
+  // A speculative tile that reaches past the prompt may hold cache rows
+  // beyond P_b (any bits, NaN included, which a zero probability would not
+  // cancel in P V), and its stage may be needed for the block: drop them all
+  // and issue again.  Then fill the remaining prologue stages.
+  int issued = nspec;
+  if (nspec > 0 && c0 + nspec * KT > c1) {
+    wait_counts<0, 15>();
+    issued = 0;
+  }
+  issue_range(issued, min(NPRO, T), ntiles, c1);
 
-  // ---- RoPE table of the B block positions (after the ring in LDS)
-  float2* cs_tab = reinterpret_cast<float2*>(smem + 2 * NSTAGE * L::TILEB);
-  static_assert(NT % HALF == 0, "each lane keeps one frequency");
-  for (int i0 = 0; i0 < B * HALF; i0 += NT) {  // uniform trip count: the shuffle needs every lane
-    const int i = i0 + tid;
-    const int k = min(i / HALF, B - 1);
-    const int pk = __shfl(pos_v, k);
-    if (i < B * HALF) cs_tab[i] = rope_cos_sin(pk, lane_inv_freq);
+  // ---- RoPE table of the B block positions
+  float2* cs_tab = reinterpret_cast<float2*>(smem + TABREG);
+  for (int i = tid; i < B * HALF; i += NT) {
+    const int k = i / HALF;
+    cs_tab[i] = rope_cos_sin(pos_b ? tp[64 + k] : plen + k, lane_inv_freq);
   }
   lds_barrier<63>();
 
@@ -322,30 +393,37 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   uint64_t vis_lo = 0, vis_hi = 0;
   const int tau_row = __shfl(tau_v, r % B);  // stage of this lane's response position
   {
-    uint16_t qb[KSTEPS][8];
+    const int lr = rw * 16 + n;
+    const unsigned char* qrow = smem + S::qrow(lr);
+    uint32_t qw[KSTEPS][4];
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qrow + (((4 * i + g) ^ (lr & (L::GR - 1))) << 4));
+      qw[i][0] = w.x;
+      qw[i][1] = w.y;
+      qw[i][2] = w.z;
+      qw[i][3] = w.w;
+    }
+    const float4* csr = reinterpret_cast<const float4*>(cs_tab + (r % B) * HALF);
+#pragma unroll
+    for (int i = 0; i < KSTEPS / 2; ++i) {
+      float4 c4[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) c4[q4] = csr[(32 * i + 8 * g) / 2 + q4];
+      uint32_t ox[4], oy[4];
+      rotate8(qw[i], qw[i + KSTEPS / 2], c4, ox, oy);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qw[i][e] = rok ? ox[e] : 0u;
+        qw[i + KSTEPS / 2][e] = rok ? oy[e] : 0u;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
+      const uint4 w = make_uint4(qw[i][0], qw[i][1], qw[i][2], qw[i][3]);
+      qop[i] = __builtin_bit_cast(bf16x8, w);
+    }
     if (rok) {
-      float qv[KSTEPS][8];
-#pragma unroll
-      for (int i = 0; i < KSTEPS; ++i) {
-        const uint32_t w[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[i][e] = bf16_bits_to_f32(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))));
-      }
-      const float4* csr = reinterpret_cast<const float4*>(cs_tab + (r % B) * HALF);
-#pragma unroll
-      for (int i = 0; i < KSTEPS / 2; ++i) {
-        float4 c4[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) c4[q4] = csr[(32 * i + 8 * g) / 2 + q4];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float2 cs = (e & 1) ? make_float2(c4[e >> 1].z, c4[e >> 1].w) : make_float2(c4[e >> 1].x, c4[e >> 1].y);
-          float xo, yo;
-          rope_apply(qv[i][e], qv[i + KSTEPS / 2][e], cs, xo, yo);
-          qb[i][e] = f32_to_bf16_bits(xo);
-          qb[i + KSTEPS / 2][e] = f32_to_bf16_bits(yo);
-        }
-      }
       uint64_t dbits, mbits;
       mask_row_bits_at([&](int j) { return j == r % B ? tau_row : __builtin_amdgcn_readlane(tau_v, j); }, B, r,
                        pl.mask_mode, dbits, mbits);
@@ -356,56 +434,50 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
         vis_lo = dbits | (mbits << B);
         vis_hi = mbits >> (64 - B);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KSTEPS; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qb[i][e] = 0;
     }
-#pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) qop[i] = bits_to_bf16x8(qb[i]);
+  }
+  if (!QSEP) {
+    lds_barrier<63>();  // every wave holds its query rows: the last stage is free
+    if (NSTAGE - 1 < T) issue(IC<NSTAGE - 1>{}, NSTAGE - 1, ntiles, c1);
   }
 
   // ---- loop-invariant LDS offsets of this lane's operand reads
-  int kofs[NSUB][KSTEPS];  // K: row 16*t4 + n, granule 4*kk + g
+  // K: row 16*(ks*NSUB + i) + n, granule 4*kk + g.  The swizzle depends on
+  // the row only through n, so subtile i is a constant offset.
+  int kofs[KSTEPS];
 #pragma unroll
-  for (int i = 0; i < NSUB; ++i)
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) kofs[i][kk] = KREG + swz<HD>(16 * (ks * NSUB + i) + n, 4 * kk + g);
+  for (int kk = 0; kk < KSTEPS; ++kk) kofs[kk] = KREG + swz<HD>(16 * ks * NSUB + n, 4 * kk + g);
   // V^T: lane (g, r, c) = (lane/16, (lane%16)/4, lane%4) reads the 8 bytes at
   // row 32u + 4g + r (then + 16), columns 16dt + 4c.., and the transposed read
   // hands lane n the column 16dt + n of those 4 rows.
-  uint32_t vadr[DTILES][NU][2];
+  // Rows +16 and +32u keep the swizzle (it depends on the row mod 16), so
+  // they are immediate offsets of one address per 16-dim tile.
+  uint32_t vadr[DTILES];
   {
-    const uint32_t vbase = lds_addr(smem) + VREG;
+    const uint32_t vbase = sbase + VREG;
     const int vr = 4 * g + ((lane & 15) >> 2);
     const int vc4 = lane & 3;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt)
-#pragma unroll
-      for (int uu = 0; uu < NU; ++uu) {
-        const int r0 = 32 * ((ks * NSUB) / 2 + uu) + vr;
-        const int gran = 2 * dt + (vc4 >> 1);
-        vadr[dt][uu][0] = vbase + swz<HD>(r0, gran) + (vc4 & 1) * 8;
-        vadr[dt][uu][1] = vbase + swz<HD>(r0 + 16, gran) + (vc4 & 1) * 8;
-      }
+      vadr[dt] = vbase + swz<HD>(32 * ((ks * NSUB) / 2) + vr, 2 * dt + (vc4 >> 1)) + (vc4 & 1) * 8;
   }
 
   // ---- online-softmax state of this wave's share of the keys
-  float mrun = -INFINITY, lpart = 0.0f;
+  float mrun = -INFINITY, lpart = 0.0f;  // running max in log2 units, partial sum
+  const float scale = pl.scale_log2;
   f32x4 acc[DTILES];
 #pragma unroll
   for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // S^T of this wave's keys of the tile in stage ST.
-  auto scores = [&](auto st_c, f32x4 (&sacc)[NSUB]) {
+  auto scores = [&](auto st_c, f32x4 (&sacc)[NSUB]) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
       bf16x8 kop[KSTEPS];
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk)
-        kop[kk] = *reinterpret_cast<const bf16x8*>(smem + ST * L::TILEB + kofs[i][kk]);
+        kop[kk] = *reinterpret_cast<const bf16x8*>(smem + ST * L::TILEB + i * 16 * L::ROWB + kofs[kk]);
       f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) sa = mfma(kop[kk], qop[kk], sa);
@@ -413,40 +485,72 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     }
   };
 
-  // V^T reads of the tile in stage ST (they complete during the softmax).
-  auto vread = [&](auto st_c, bf16x4 (&vlo)[DTILES][NU], bf16x4 (&vhi)[DTILES][NU]) {
+  // V^T operands of the tile in stage ST (the reads complete during the softmax).
+  auto vread = [&](auto st_c, bf16x8 (&vop)[DTILES][NU]) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt)
 #pragma unroll
-      for (int uu = 0; uu < NU; ++uu) tr_read_pair<ST * L::TILEB>(vadr[dt][uu][0], vadr[dt][uu][1], vlo[dt][uu], vhi[dt][uu]);
+      for (int uu = 0; uu < NU; ++uu) {
+        constexpr int O = ST * L::TILEB;
+        bf16x4 lo, hi;
+        if (uu == 0) {
+          lo = tr_read<O>(vadr[dt]);
+          hi = tr_read<O + 16 * L::ROWB>(vadr[dt]);
+        } else {
+          lo = tr_read<O + 32 * L::ROWB>(vadr[dt]);
+          hi = tr_read<O + 48 * L::ROWB>(vadr[dt]);
+        }
+        vop[dt][uu] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+  };
+
+  // Rotate block tile bt (its K rows in stage ST) in place.
+  auto rotate_block = [&](auto st_c, int bt) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_c)::value;
+    unsigned char* Kb = smem + KREG + ST * L::TILEB;
+    const int nvalid = min(KT, twoB - bt * KT);
+    for (int i = tid; i < nvalid * (L::GR / 2); i += NT) {
+      const int row = i / (L::GR / 2), j = i % (L::GR / 2);
+      uint4* px = reinterpret_cast<uint4*>(Kb + swz<HD>(row, j));
+      uint4* py = reinterpret_cast<uint4*>(Kb + swz<HD>(row, j + L::GR / 2));
+      const uint4 x4 = *px, y4 = *py;
+      const float4* csr = reinterpret_cast<const float4*>(cs_tab + ((bt * KT + row) % B) * HALF + 8 * j);
+      float4 c4[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) c4[q4] = csr[q4];
+      const uint32_t wx[4] = {x4.x, x4.y, x4.z, x4.w};
+      const uint32_t wy[4] = {y4.x, y4.y, y4.z, y4.w};
+      uint32_t ox[4], oy[4];
+      rotate8(wx, wy, c4, ox, oy);
+      *px = make_uint4(ox[0], ox[1], ox[2], ox[3]);
+      *py = make_uint4(oy[0], oy[1], oy[2], oy[3]);
+    }
+    lds_barrier<63>();
   };
 
   // Softmax of the scores and O^T += V^T P^T.  MODE 0: every key visible;
-  // 1: keys kbase+k < klimit; 2: block column kbase+k per the tau bits.
-  auto finish = [&](auto mode_c, const f32x4 (&sacc)[NSUB], bf16x4 (&vlo)[DTILES][NU],
-                    bf16x4 (&vhi)[DTILES][NU], int kbase, int klimit) {
+  // MODE 1: key k of the tile visible when bit k of cmask is set.
+  auto finish = [&](auto mode_c, const f32x4 (&sacc)[NSUB], const bf16x8 (&vop)[DTILES][NU], uint64_t cmask)
+                    __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_c)::value;
     float sv[NSUB][4];
     float tmax = -INFINITY;
+    // this lane's keys are 16*(ks*NSUB + i) + 4g + j: one variable shift, then constant bit tests
+    const uint64_t cm = MODE == 0 ? 0ull : cmask >> (16 * ks * NSUB + 4 * g);
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int k = 16 * (ks * NSUB + i) + 4 * g + j;
-        bool vis = true;
-        if (MODE == 1) vis = kbase + k < klimit;
-        if (MODE == 2) {
-          const int c = kbase + k;
-          vis = c < 64 ? ((vis_lo >> c) & 1ull) : ((vis_hi >> (c - 64)) & 1ull);
-        }
-        const float x = vis ? sacc[i][j] * pl.scale_log2 : -INFINITY;
+        const bool vis = MODE == 0 || ((cm >> (16 * i + j)) & 1ull);
+        const float x = vis ? sacc[i][j] : -INFINITY;  // raw score; the scale is applied below
         sv[i][j] = x;
         tmax = fmaxf(tmax, x);
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax *= scale;  // log2 units (scale > 0)
     if (__any(tmax > mrun + kRescale)) {
       const float mnew = fmaxf(mrun, tmax);
       const float alpha = (mnew == mrun) ? 1.0f : __builtin_amdgcn_exp2f(mrun - mnew);
@@ -462,7 +566,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     for (int i = 0; i < NSUB; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        pv[i][j] = __builtin_amdgcn_exp2f(sv[i][j] - muse);
+        pv[i][j] = __builtin_amdgcn_exp2f(fmaf(sv[i][j], scale, -muse));
         lsum += pv[i][j];
       }
     lpart += lsum;
@@ -483,114 +587,62 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       pop[uu] = bf16x8{pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
     }
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) {
-      if (NU == 2)
-        lds_read_wait(vlo[dt][0], vhi[dt][0], vlo[dt][NU - 1], vhi[dt][NU - 1]);
-      else
-        lds_read_wait(vlo[dt][0], vhi[dt][0]);
-    }
+    for (int dt = 0; dt < DTILES; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) {
-#pragma unroll
-      for (int uu = 0; uu < NU; ++uu) {
-        const bf16x4 lo = vlo[dt][uu], hi = vhi[dt][uu];
-        const bf16x8 vop = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[dt] = mfma(vop, pop[uu], acc[dt]);
-      }
-    }
+      for (int uu = 0; uu < NU; ++uu) acc[dt] = mfma(vop[dt][uu], pop[uu], acc[dt]);
   };
 
-  // ---- block keys (split 0): rotated K and V of this KV head in the last
-  //      stage, one 64-row tile at a time (a second tile only when B > 32)
-  auto block_tile = [&](int bt) {
-    unsigned char* Kb = smem + KREG + (NSTAGE - 1) * L::TILEB;
-    unsigned char* Vb = smem + VREG + (NSTAGE - 1) * L::TILEB;
-#pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      const int i = tid + it * NT;
-      if (i >= KT * (L::GR / 2)) continue;
-      const int row = i / (L::GR / 2), j = i % (L::GR / 2), c = bt * KT + row;
-      const uint32_t wx[4] = {bkx[it].x, bkx[it].y, bkx[it].z, bkx[it].w};
-      const uint32_t wy[4] = {bky[it].x, bky[it].y, bky[it].z, bky[it].w};
-      uint16_t lo8[8], hi8[8];
-      const float4* csr = reinterpret_cast<const float4*>(cs_tab + (c % B) * HALF + 8 * j);
-      float4 c4[4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) c4[q4] = csr[q4];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 cs = (e & 1) ? make_float2(c4[e >> 1].z, c4[e >> 1].w) : make_float2(c4[e >> 1].x, c4[e >> 1].y);
-        float xo, yo;
-        rope_apply(bf16_bits_to_f32(static_cast<uint16_t>(wx[e >> 1] >> (16 * (e & 1)))),
-                   bf16_bits_to_f32(static_cast<uint16_t>(wy[e >> 1] >> (16 * (e & 1)))), cs, xo, yo);
-        lo8[e] = f32_to_bf16_bits(xo);
-        hi8[e] = f32_to_bf16_bits(yo);
-      }
-      *reinterpret_cast<u16x8*>(Kb + swz<HD>(row, j)) = u16x8{lo8[0], lo8[1], lo8[2], lo8[3], lo8[4], lo8[5], lo8[6], lo8[7]};
-      *reinterpret_cast<u16x8*>(Kb + swz<HD>(row, j + L::GR / 2)) =
-          u16x8{hi8[0], hi8[1], hi8[2], hi8[3], hi8[4], hi8[5], hi8[6], hi8[7]};
-    }
-#pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
-      const int i = tid + it * NT;
-      if (i >= KT * L::GR) continue;
-      const int row = i / L::GR, j = i % L::GR;
-      *reinterpret_cast<uint4*>(Vb + swz<HD>(row, j)) = bvv[it];
-    }
-    lds_barrier<63>();
-    f32x4 sb[NSUB];
-    bf16x4 vlo[DTILES][NU], vhi[DTILES][NU];
-    vread(IC<NSTAGE - 1>{}, vlo, vhi);
-    scores(IC<NSTAGE - 1>{}, sb);
-    finish(IC<2>{}, sb, vlo, vhi, bt * KT, 0);
-    lds_barrier<63>();
-  };
-  if (has_block) {
-    block_tile(0);
-    if (twoB > KT) {  // B > 32: the loads of the second tile wait for the ring loads too (rare shape)
-      load_block(1, bkx, bky, bvv);
-      block_tile(1);
-    }
-  }
-
-  // ---- prompt keys [c0, c1): software-pipelined over the ring
-  f32x4 scur[NSUB];
-  if (ntiles > 0) {
-    // tile 0 landed; the loads of tiles 1..NSTAGE-2 may still be in flight
-    if (ntiles - 1 >= NSTAGE - 2)
-      lds_barrier<(NSTAGE - 2) * LPW>();
-    else
-      lds_barrier<0>();
-    scores(IC<0>{}, scur);
-  }
-  auto step = [&](auto k_c, int t) {
+  // ---- the T = ntiles + nbt tiles, software-pipelined over the ring.
+  //      Before step t: tiles 0 .. min(t + NSTAGE - 2, T - 1) are issued
+  //      (0 .. min(NSTAGE, T) - 1 for t = 0), in tile order.
+  f32x4 sb[2][NSUB];  // scores of tiles t (sb[t % 2]) and t+1
+  if (T >= NSTAGE)
+    lds_barrier<(NSTAGE - 1) * LPW>();  // tile 0 landed
+  else
+    lds_barrier<0>();
+  if (ntiles == 0) rotate_block(IC<0>{}, 0);
+  scores(IC<0>{}, sb[0]);
+  auto step = [&](auto k_c, auto p_c, int t) __attribute__((always_inline)) {
     constexpr int K = decltype(k_c)::value;  // stage of tile t (t % NSTAGE)
-    if (t + 1 < ntiles) {
-      // tile t+1 must have landed: only the loads of tiles t+2..t+NSTAGE-2 may
-      // still be in flight; the barrier also frees the stage of tile t-1
-      if (t + NSTAGE - 2 < ntiles)
-        lds_barrier<(NSTAGE - 3) * LPW>();
-      else
-        lds_barrier<0>();
-      if (t + NSTAGE - 1 < ntiles) issue(IC<(K + NSTAGE - 1) % NSTAGE>{}, t + NSTAGE - 1, c1);
+    constexpr int P = decltype(p_c)::value;  // t % 2
+    if (t + 1 < T) {
+      // tile t+1 must have landed: only the loads of later tiles may still be
+      // in flight; for t >= 1 the barrier also frees the stage of tile t-1
+      if (t == 0) {
+        if (T >= NSTAGE)
+          lds_barrier<(NSTAGE - 2) * LPW>();
+        else
+          lds_barrier<0>();
+      } else {
+        if (t + NSTAGE - 2 < T)
+          lds_barrier<(NSTAGE - 3) * LPW>();
+        else
+          lds_barrier<0>();
+        if (t + NSTAGE - 1 < T) issue(IC<(K + NSTAGE - 1) % NSTAGE>{}, t + NSTAGE - 1, ntiles, c1);
+      }
+      if (t + 1 >= ntiles) rotate_block(IC<(K + 1) % NSTAGE>{}, t + 1 - ntiles);
     }
-    bf16x4 vlo[DTILES][NU], vhi[DTILES][NU];
-    vread(IC<K>{}, vlo, vhi);
-    f32x4 snext[NSUB];
-    if (t + 1 < ntiles) scores(IC<(K + 1) % NSTAGE>{}, snext);
-    const int kbase = c0 + t * KT;
-    if (kbase + KT <= c1)
-      finish(IC<0>{}, scur, vlo, vhi, kbase, c1);
-    else
-      finish(IC<1>{}, scur, vlo, vhi, kbase, c1);
-#pragma unroll
-    for (int i = 0; i < NSUB; ++i) scur[i] = snext[i];
+    bf16x8 vop[DTILES][NU];
+    vread(IC<K>{}, vop);
+    if (t + 1 < T) scores(IC<(K + 1) % NSTAGE>{}, sb[1 - P]);
+    if (t < ntiles) {
+      const int kbase = c0 + t * KT;
+      if (kbase + KT <= c1)
+        finish(IC<0>{}, sb[P], vop, 0ull);
+      else
+        finish(IC<1>{}, sb[P], vop, (1ull << (c1 - kbase)) - 1ull);
+    } else {
+      finish(IC<1>{}, sb[P], vop, t == ntiles ? vis_lo : vis_hi);
+    }
   };
-  for (int t0 = 0; t0 < ntiles; t0 += NSTAGE) {
-    step(IC<0>{}, t0);
-    if (t0 + 1 < ntiles) step(IC<1>{}, t0 + 1);
-    if (t0 + 2 < ntiles) step(IC<2>{}, t0 + 2);
-    if (NSTAGE > 3 && t0 + 3 < ntiles) step(IC<(NSTAGE > 3 ? 3 : 0)>{}, t0 + 3);
+  // unrolled over a multiple of NSTAGE and 2 so stage and buffer are constants
+  for (int t0 = 0; t0 < T; t0 += (NSTAGE == 3 ? 6 : 4)) {
+    step(IC<0>{}, IC<0>{}, t0);
+    if (t0 + 1 < T) step(IC<1>{}, IC<1>{}, t0 + 1);
+    if (t0 + 2 < T) step(IC<2 % NSTAGE>{}, IC<0>{}, t0 + 2);
+    if (t0 + 3 < T) step(IC<3 % NSTAGE>{}, IC<1>{}, t0 + 3);
+    if (NSTAGE == 3 && t0 + 4 < T) step(IC<4 % NSTAGE>{}, IC<0>{}, t0 + 4);
+    if (NSTAGE == 3 && t0 + 5 < T) step(IC<5 % NSTAGE>{}, IC<1>{}, t0 + 5);
   }
 
   // ---- combine the key splits of each row (through the drained ring)
@@ -639,9 +691,8 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
       const f32x4 v = acc[dt];
-      const uint32_t w0 = f32_to_bf16_bits(v[0] * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1] * inv)) << 16);
-      const uint32_t w1 = f32_to_bf16_bits(v[2] * inv) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(op + 16 * dt + 4 * g) = make_uint2(w0, w1);
+      *reinterpret_cast<uint2*>(op + 16 * dt + 4 * g) =
+          make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
     }
     if (a.lse && g == 0) a.lse[rout] = (mrun + log2f(l)) * kLn2;
   } else {
@@ -659,10 +710,10 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   }
 }
 
-template <int HD, int RW, int KSPLIT, int NSTAGE>
+template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP>
 hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
-  auto kern = verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE>;
-  const size_t lds = mfma_lds_bytes(HD, NSTAGE, pl.B);
+  auto kern = verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP>;
+  const size_t lds = mfma_lds_bytes(HD, NSTAGE, pl.B, RW * 16, QSEP);
   static int attr_set = 0;  // largest dynamic LDS size already allowed for this instantiation
   if (static_cast<int>(lds) > attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -675,27 +726,30 @@ hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int HD, int NSTAGE>
+template <int HD, int NSTAGE, bool QSEP>
 hipError_t launch_stages(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
   switch (pl.rows_wg / 16) {
-    case 1: return launch_cfg<HD, 1, 4, NSTAGE>(pl, a, s);
-    case 2: return launch_cfg<HD, 2, 4, NSTAGE>(pl, a, s);
-    case 4: return launch_cfg<HD, 4, 2, NSTAGE>(pl, a, s);
-    default: return launch_cfg<HD, 8, 1, NSTAGE>(pl, a, s);
+    case 1: return launch_cfg<HD, 1, 4, NSTAGE, QSEP>(pl, a, s);
+    case 2: return launch_cfg<HD, 2, 4, NSTAGE, QSEP>(pl, a, s);
+    case 4: return launch_cfg<HD, 4, 2, NSTAGE, QSEP>(pl, a, s);
+    default: return launch_cfg<HD, 8, 1, NSTAGE, QSEP>(pl, a, s);
   }
 }
 
 }  // namespace
 
-// Dynamic LDS of one workgroup: the tile ring plus the RoPE table.
-size_t mfma_lds_bytes(int hd, int nstage, int B) {
+// Dynamic LDS of one workgroup: the tile ring, stage labels and positions,
+// the staged query rows when they have their own region, the RoPE table.
+size_t mfma_lds_bytes(int hd, int nstage, int B, int rows_wg, bool qsep) {
   const size_t ring = static_cast<size_t>(nstage) * 2 * KT * hd * 2;
-  return ring + static_cast<size_t>(B) * (hd / 2) * sizeof(float2);
+  return ring + 512 + (qsep ? static_cast<size_t>(rows_wg) * hd * 2 : 0) +
+         static_cast<size_t>(B) * (hd / 2) * sizeof(float2);
 }
 
 hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
-  if (pl.d == 64) return launch_stages<64, 4>(pl, a, s);
-  return pl.nstage == 4 ? launch_stages<128, 4>(pl, a, s) : launch_stages<128, 3>(pl, a, s);
+  if (pl.d == 64) return launch_stages<64, 4, true>(pl, a, s);
+  if (pl.qsep) return launch_stages<128, 4, true>(pl, a, s);
+  return pl.nstage == 4 ? launch_stages<128, 4, false>(pl, a, s) : launch_stages<128, 3, false>(pl, a, s);
 }
 
 }  // namespace simsd

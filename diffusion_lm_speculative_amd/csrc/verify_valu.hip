@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void verify_valu_kernel(Plan pl, VerifyArgs a)
 #pragma unroll
     for (int e = 0; e < NE / 2; ++e) {
       const int f = l16 + 16 * e;
-      rope_apply(Elem<T>::load(qp, f), Elem<T>::load(qp, f + HALF), rope_cos_sin(pos, pl.inv_freq[f]),
+      rope_apply(Elem<T>::load(qp, f), Elem<T>::load(qp, f + HALF), rope_cos_sin(pos, rope_inv_freq(f, HD, pl.log2_base)),
                  q[e], q[e + NE / 2]);
     }
     mask_row_bits(tau_b, B, r, pl.mask_mode, dbits, mbits);
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void verify_valu_kernel(Plan pl, VerifyArgs a)
           const T* kp = static_cast<const T*>(a.k_blk) +
                         ((static_cast<size_t>(b) * twoB + c) * pl.Hkv + kvh) * HD;
           rope_apply(Elem<T>::load(kp, f), Elem<T>::load(kp, f + HALF),
-                     rope_cos_sin(block_pos(pos_b, plen, c % B), pl.inv_freq[f]), xo, yo);
+                     rope_cos_sin(block_pos(pos_b, plen, c % B), rope_inv_freq(f, HD, pl.log2_base)), xo, yo);
         }
         Ks[key][f] = xo;
         Ks[key][f + HALF] = yo;

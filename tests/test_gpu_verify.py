@@ -124,6 +124,22 @@ def test_faulted_sequences(impl):
     assert st.cpu().tolist() == [0, sd.ST_TAU_RANGE, sd.ST_PROMPT_LEN, sd.ST_POS_NEG]
 
 
+@pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
+def test_cache_rows_past_prompt_len_are_never_read(impl):
+    # Cache rows at positions >= P_b are not part of the input: fill them with
+    # NaN and Inf.  Prompt lengths end inside the first tiles of a split (the
+    # rows a kernel may fetch before it knows P_b), on tile edges and at 0.
+    w = _w(NB=6, Hq=8, Hkv=2, P=700, B=4)
+    t = gpu_inputs(w, 91)
+    t["prompt_len"][:] = torch.tensor([0, 1, 63, 64, 130, 700], dtype=torch.int32)
+    for b, plen in enumerate(t["prompt_len"].tolist()):
+        t["k_cache"][b, :, plen:] = float("nan")
+        t["v_cache"][b, :, plen:] = float("inf")
+    for kv_chunk in (0, 64, 128):
+        out, _, _ = _check(t, w, f"nan tail chunk={kv_chunk}", impl=impl, kv_chunk=kv_chunk)
+        assert torch.isfinite(out).all()
+
+
 def test_mask_mistake_is_visible_in_block_dominated_case():
     # With no prompt the block mask decides the result: the kernel must sit far
     # closer to the temporal-mask oracle than to the all-visible one.
