@@ -199,10 +199,12 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   static_assert(QSEP || RW * 16 <= 2 * KT, "query rows must fit the last stage");
   static_assert((KSPLIT - 1) * RW * 16 * XSTR * 4 <= 2 * NSTAGE * L::TILEB, "exchange buffer fits the ring");
   static_assert(NT % HALF == 0, "each lane keeps one RoPE frequency");
-  // The running max moves only when a score exceeds it by more than this
-  // (log2 units): probabilities stay below 2^8 and the rescale of the
-  // accumulators is skipped for most tiles.
-  constexpr float kRescale = 8.0f;
+  // Probabilities are taken relative to a per-row reference fixed at the
+  // row's first tile with a visible key (no rescaling of the accumulators
+  // inside the loop).  A row whose probabilities could reach past this bound
+  // (log2 units) makes the workgroup run its keys a second time with the
+  // exact row maximum as the reference.
+  constexpr float kRefSlack = 64.0f;
 
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -463,7 +465,8 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   }
 
   // ---- online-softmax state of this wave's share of the keys
-  float mrun = -INFINITY, lpart = 0.0f;  // running max in log2 units, partial sum
+  float mref = -INFINITY, lpart = 0.0f;  // reference (log2 units, -inf until set), partial sum
+  float lmax = -INFINITY;                 // this lane's largest raw score so far
   const float scale = pl.scale_log2;
   f32x4 acc[DTILES];
 #pragma unroll
@@ -548,18 +551,13 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
         tmax = fmaxf(tmax, x);
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    tmax *= scale;  // log2 units (scale > 0)
-    if (__any(tmax > mrun + kRescale)) {
-      const float mnew = fmaxf(mrun, tmax);
-      const float alpha = (mnew == mrun) ? 1.0f : __builtin_amdgcn_exp2f(mrun - mnew);
-      mrun = mnew;
-      lpart *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt) acc[dt] *= alpha;
+    lmax = fmaxf(lmax, tmax);
+    if (__any(mref == -INFINITY)) {  // first tile with a visible key for some row of this wave
+      float rmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+      if (mref == -INFINITY) mref = rmax * scale;  // stays -inf while the row sees nothing
     }
-    const float muse = (mrun == -INFINITY) ? 0.0f : mrun;
+    const float muse = (mref == -INFINITY) ? 0.0f : mref;
     float pv[NSUB][4];
     float lsum = 0.0f;
 #pragma unroll
@@ -596,6 +594,8 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   //      Before step t: tiles 0 .. min(t + NSTAGE - 2, T - 1) are issued
   //      (0 .. min(NSTAGE, T) - 1 for t = 0), in tile order.
   f32x4 sb[2][NSUB];  // scores of tiles t (sb[t % 2]) and t+1
+  int* pass_flag = reinterpret_cast<int*>(smem + S::TPREG + 512 - 4);  // after the positions
+  for (int pass = 0;; ++pass) {
   if (T >= NSTAGE)
     lds_barrier<(NSTAGE - 1) * LPW>();  // tile 0 landed
   else
@@ -645,6 +645,31 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     if (NSTAGE == 3 && t0 + 5 < T) step(IC<5 % NSTAGE>{}, IC<1>{}, t0 + 5);
   }
 
+  // ---- a second pass when some row's probabilities may have grown past
+  //      2^kRefSlack (or the sums are not finite): the exact row maximum
+  //      over this wave's keys becomes the reference
+  float rowmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+  rowmax = fmaxf(rowmax, __shfl_xor(rowmax, 32));
+  bool bad = !(lpart <= 0x1p60f);  // a lane's share; also catches NaN
+#pragma unroll
+  for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bad |= !__builtin_isfinite(acc[dt][j]);
+  bad |= mref != -INFINITY && rowmax * scale > mref + kRefSlack;
+  if (pass > 0) break;
+  wait_counts<0, 15>();
+  if (tid == 0) *pass_flag = 0;
+  lds_barrier<0>();
+  if (__any(bad) && lane == 0) *pass_flag = 1;
+  lds_barrier<0>();
+  if (*pass_flag == 0) break;
+  mref = rowmax == -INFINITY ? -INFINITY : rowmax * scale;
+  lpart = 0.0f;
+#pragma unroll
+  for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  issue_range(0, min(NSTAGE, T), ntiles, c1);
+  }
+
   // ---- combine the key splits of each row (through the drained ring)
   wait_counts<0, 15>();  // no ring load may land after the workgroup ends
   if (status_writer) a.status[b] = 0;
@@ -660,7 +685,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       for (int dt = 0; dt < DTILES; ++dt)
         *reinterpret_cast<float4*>(xr + 16 * dt + 4 * g) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
       if (g == 0) {
-        xr[HD] = mrun;
+        xr[HD] = mref;
         xr[HD + 1] = l;
       }
     }
@@ -670,8 +695,8 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     for (int k2 = 1; k2 < KSPLIT; ++k2) {
       const float* xr = xb + (((k2 - 1) * RW + rw) * 16 + n) * XSTR;
       const float m2 = xr[HD], l2 = xr[HD + 1];
-      const float mnew = fmaxf(mrun, m2);
-      const float a1 = (mrun == mnew) ? 1.0f : exp2f(mrun - mnew);
+      const float mnew = fmaxf(mref, m2);
+      const float a1 = (mref == mnew) ? 1.0f : exp2f(mref - mnew);
       const float a2 = (m2 == mnew) ? 1.0f : exp2f(m2 - mnew);
       l = l * a1 + l2 * a2;
 #pragma unroll
@@ -679,7 +704,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
         const float4 o2 = *reinterpret_cast<const float4*>(xr + 16 * dt + 4 * g);
         acc[dt] = acc[dt] * a1 + f32x4{o2.x, o2.y, o2.z, o2.w} * a2;
       }
-      mrun = mnew;
+      mref = mnew;
     }
   }
 
@@ -694,7 +719,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       *reinterpret_cast<uint2*>(op + 16 * dt + 4 * g) =
           make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
     }
-    if (a.lse && g == 0) a.lse[rout] = (mrun + log2f(l)) * kLn2;
+    if (a.lse && g == 0) a.lse[rout] = (mref + log2f(l)) * kLn2;
   } else {
     const size_t slot = (static_cast<size_t>(b) * pl.Hkv + kvh) * pl.nsplit + s;
     float* po = a.part_o + (slot * pl.M + m) * HD;
@@ -704,7 +729,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
     }
     if (g == 0) {
-      a.part_ml[(slot * pl.M + m) * 2 + 0] = mrun;
+      a.part_ml[(slot * pl.M + m) * 2 + 0] = mref;
       a.part_ml[(slot * pl.M + m) * 2 + 1] = l;
     }
   }

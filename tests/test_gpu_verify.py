@@ -140,6 +140,26 @@ def test_cache_rows_past_prompt_len_are_never_read(impl):
         assert torch.isfinite(out).all()
 
 
+@pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
+@pytest.mark.parametrize("big", [12.0, 200.0])
+def test_late_keys_far_above_the_first_tiles(impl, big):
+    # A few late prompt keys score far above everything before them (by
+    # hundreds of log2 units for big=200): probabilities taken relative to an
+    # early reference would overflow, so the result must still match.  The
+    # block rows sit at RoPE position 0, where the rotation is exact, so the
+    # bf16 query operand carries no rounding that keys this long would
+    # magnify beyond the bf16 tolerance.
+    w = _w(NB=2, Hq=8, Hkv=2, P=600, B=4)
+    t = gpu_inputs(w, 101)
+    t["k_cache"][:, :, 590:593] = big
+    t["k_cache"][1, :, 300] = -big
+    pos_d = torch.zeros((2, 4), dtype=torch.int32, device=dev())
+    for kv_chunk in (0, 128, 640):
+        out, lse, _ = _check(t, w, f"late big keys {big} chunk={kv_chunk}", impl=impl, kv_chunk=kv_chunk,
+                             pos_d=pos_d)
+        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+
+
 def test_mask_mistake_is_visible_in_block_dominated_case():
     # With no prompt the block mask decides the result: the kernel must sit far
     # closer to the temporal-mask oracle than to the all-visible one.
