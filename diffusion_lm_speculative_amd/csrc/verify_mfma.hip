@@ -284,8 +284,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const size_t blk_row = static_cast<size_t>(pl.Hkv) * HD;  // elements between block rows
   const uint16_t* kblk_b = kblk + (static_cast<size_t>(b) * twoB * pl.Hkv + kvh) * HD;
   const uint16_t* vblk_b = vblk + (static_cast<size_t>(b) * twoB * pl.Hkv + kvh) * HD;
-  auto issue = [&](auto st_c, int t, int ntl, int lim) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_c)::value;
+  auto issue = [&](int ST, int t, int ntl, int lim) __attribute__((always_inline)) {
     if (t < ntl) {
       const int kb = c0 + t * KT;
       const bool full = kb + KT <= lim;
@@ -318,10 +317,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   };
   // tiles [from, to) of the ring, to <= NSTAGE
   auto issue_range = [&](int from, int to, int ntl, int lim) __attribute__((always_inline)) {
-    if (from <= 0 && 0 < to) issue(IC<0>{}, 0, ntl, lim);
-    if (from <= 1 && 1 < to) issue(IC<1>{}, 1, ntl, lim);
-    if (from <= 2 && 2 < to) issue(IC<2>{}, 2, ntl, lim);
-    if (NSTAGE > 3 && from <= 3 && 3 < to) issue(IC<(NSTAGE > 3 ? 3 : 0)>{}, 3, ntl, lim);
+    for (int t = from; t < to; ++t) issue(t, t, ntl, lim);
   };
 
   // The first prompt tiles go in flight before prompt_len is known, assuming
@@ -440,7 +436,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   }
   if (!QSEP) {
     lds_barrier<63>();  // every wave holds its query rows: the last stage is free
-    if (NSTAGE - 1 < T) issue(IC<NSTAGE - 1>{}, NSTAGE - 1, ntiles, c1);
+    if (NSTAGE - 1 < T) issue(NSTAGE - 1, NSTAGE - 1, ntiles, c1);
   }
 
   // ---- loop-invariant LDS offsets of this lane's operand reads
@@ -473,14 +469,14 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // S^T of this wave's keys of the tile in stage ST.
-  auto scores = [&](auto st_c, f32x4 (&sacc)[NSUB]) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_c)::value;
+  auto scores = [&](int st, f32x4 (&sacc)[NSUB]) __attribute__((always_inline)) {
+    const int sto = st * L::TILEB;
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
       bf16x8 kop[KSTEPS];
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk)
-        kop[kk] = *reinterpret_cast<const bf16x8*>(smem + ST * L::TILEB + i * 16 * L::ROWB + kofs[kk]);
+        kop[kk] = *reinterpret_cast<const bf16x8*>(smem + (kofs[kk] + sto) + i * 16 * L::ROWB);
       f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) sa = mfma(kop[kk], qop[kk], sa);
@@ -489,29 +485,28 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   };
 
   // V^T operands of the tile in stage ST (the reads complete during the softmax).
-  auto vread = [&](auto st_c, bf16x8 (&vop)[DTILES][NU]) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_c)::value;
+  auto vread = [&](int st, bf16x8 (&vop)[DTILES][NU]) __attribute__((always_inline)) {
+    const uint32_t sto = st * L::TILEB;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt)
 #pragma unroll
       for (int uu = 0; uu < NU; ++uu) {
-        constexpr int O = ST * L::TILEB;
+        const uint32_t va = vadr[dt] + sto;
         bf16x4 lo, hi;
         if (uu == 0) {
-          lo = tr_read<O>(vadr[dt]);
-          hi = tr_read<O + 16 * L::ROWB>(vadr[dt]);
+          lo = tr_read<0>(va);
+          hi = tr_read<16 * L::ROWB>(va);
         } else {
-          lo = tr_read<O + 32 * L::ROWB>(vadr[dt]);
-          hi = tr_read<O + 48 * L::ROWB>(vadr[dt]);
+          lo = tr_read<32 * L::ROWB>(va);
+          hi = tr_read<48 * L::ROWB>(va);
         }
         vop[dt][uu] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
   };
 
   // Rotate block tile bt (its K rows in stage ST) in place.
-  auto rotate_block = [&](auto st_c, int bt) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_c)::value;
-    unsigned char* Kb = smem + KREG + ST * L::TILEB;
+  auto rotate_block = [&](int st, int bt) __attribute__((always_inline)) {
+    unsigned char* Kb = smem + KREG + st * L::TILEB;
     const int nvalid = min(KT, twoB - bt * KT);
     for (int i = tid; i < nvalid * (L::GR / 2); i += NT) {
       const int row = i / (L::GR / 2), j = i % (L::GR / 2);
@@ -600,11 +595,15 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     lds_barrier<(NSTAGE - 1) * LPW>();  // tile 0 landed
   else
     lds_barrier<0>();
-  if (ntiles == 0) rotate_block(IC<0>{}, 0);
-  scores(IC<0>{}, sb[0]);
-  auto step = [&](auto k_c, auto p_c, int t) __attribute__((always_inline)) {
-    constexpr int K = decltype(k_c)::value;  // stage of tile t (t % NSTAGE)
+  if (ntiles == 0) rotate_block(0, 0);
+  scores(0, sb[0]);
+  // Tiles [0, nfull) are whole prompt tiles (every key visible); the rest
+  // (a ragged prompt tail, then the block tiles) go through the masked path.
+  const int nfull = (c1 - c0) / KT;
+  auto step = [&](auto p_c, auto mode_c, int t) __attribute__((always_inline)) {
     constexpr int P = decltype(p_c)::value;  // t % 2
+    const int K = t % NSTAGE;                // stage of tile t
+    const int K1 = K + 1 == NSTAGE ? 0 : K + 1;
     if (t + 1 < T) {
       // tile t+1 must have landed: only the loads of later tiles may still be
       // in flight; for t >= 1 the barrier also frees the stage of tile t-1
@@ -618,31 +617,31 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
           lds_barrier<(NSTAGE - 3) * LPW>();
         else
           lds_barrier<0>();
-        if (t + NSTAGE - 1 < T) issue(IC<(K + NSTAGE - 1) % NSTAGE>{}, t + NSTAGE - 1, ntiles, c1);
+        if (t + NSTAGE - 1 < T) issue(K == 0 ? NSTAGE - 1 : K - 1, t + NSTAGE - 1, ntiles, c1);
       }
-      if (t + 1 >= ntiles) rotate_block(IC<(K + 1) % NSTAGE>{}, t + 1 - ntiles);
+      if (t + 1 >= ntiles) rotate_block(K1, t + 1 - ntiles);
     }
     bf16x8 vop[DTILES][NU];
-    vread(IC<K>{}, vop);
-    if (t + 1 < T) scores(IC<(K + 1) % NSTAGE>{}, sb[1 - P]);
-    if (t < ntiles) {
-      const int kbase = c0 + t * KT;
-      if (kbase + KT <= c1)
-        finish(IC<0>{}, sb[P], vop, 0ull);
-      else
-        finish(IC<1>{}, sb[P], vop, (1ull << (c1 - kbase)) - 1ull);
+    vread(K, vop);
+    if (t + 1 < T) scores(K1, sb[1 - P]);
+    if (decltype(mode_c)::value == 0) {
+      finish(IC<0>{}, sb[P], vop, 0ull);
     } else {
-      finish(IC<1>{}, sb[P], vop, t == ntiles ? vis_lo : vis_hi);
+      const int nk = c1 - (c0 + t * KT);  // keys of a prompt tile below c1
+      const uint64_t cm = t >= ntiles ? (t == ntiles ? vis_lo : vis_hi)
+                                      : (nk >= KT ? ~0ull : (1ull << nk) - 1ull);
+      finish(IC<1>{}, sb[P], vop, cm);
     }
   };
-  // unrolled over a multiple of NSTAGE and 2 so stage and buffer are constants
-  for (int t0 = 0; t0 < T; t0 += (NSTAGE == 3 ? 6 : 4)) {
+  // unrolled by two so the score buffers are constants
+  int t0 = 0;
+  for (; t0 + 2 <= nfull; t0 += 2) {
     step(IC<0>{}, IC<0>{}, t0);
+    step(IC<1>{}, IC<0>{}, t0 + 1);
+  }
+  for (; t0 < T; t0 += 2) {
+    step(IC<0>{}, IC<1>{}, t0);
     if (t0 + 1 < T) step(IC<1>{}, IC<1>{}, t0 + 1);
-    if (t0 + 2 < T) step(IC<2 % NSTAGE>{}, IC<0>{}, t0 + 2);
-    if (t0 + 3 < T) step(IC<3 % NSTAGE>{}, IC<1>{}, t0 + 3);
-    if (NSTAGE == 3 && t0 + 4 < T) step(IC<4 % NSTAGE>{}, IC<0>{}, t0 + 4);
-    if (NSTAGE == 3 && t0 + 5 < T) step(IC<5 % NSTAGE>{}, IC<1>{}, t0 + 5);
   }
 
   // ---- a second pass when some row's probabilities may have grown past
