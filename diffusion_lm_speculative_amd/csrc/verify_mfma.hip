@@ -129,6 +129,17 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t
                : "memory");
 }
 
+// Two wave-uniform 4-byte loads through the scalar cache, waited for here.
+// (The compiler cannot prove such loads scalar once the direct-to-LDS loads,
+// which it sees as arbitrary memory writes, have been issued; a vector load
+// would make it wait for every load in flight.)
+__device__ __forceinline__ void sload2(const int32_t* p0, const int32_t* p1, int& v0, int& v1) {
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(v0), "=&s"(v1)
+               : "s"(p0), "s"(p1)
+               : "memory");
+}
+
 // One direct-to-LDS load of 4 bytes per lane into LDS at m0 + 4*lane.
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
@@ -262,11 +273,11 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
 
   // ---- ring loads.  Lane `lane` of load instruction `ins` fills LDS
   //      granule position lane%GR of tile row ins*RPI + lane/GR, i.e. global
-  //      granule (pos ^ row) of that row.  Prompt tile t covers keys
-  //      c0 + 64t ..; in a tile that ends past `lim` the rows beyond it
-  //      re-read key lim-1 (finite values; their scores are masked).  Tile
-  //      ntl + bt is block tile bt: block rows 64bt.. of this KV head's K and
-  //      V (rows past 2B re-read row 2B-1), rotated in LDS once landed.
+  //      granule (pos ^ row) of that row.  Tile t < nbt is block tile t:
+  //      block rows 64t.. of this KV head's K and V (rows past 2B re-read
+  //      row 2B-1), rotated in LDS once landed.  Tile nbt + u is prompt tile
+  //      u, keys c0 + 64u ..; in a tile that ends past `lim` the rows beyond
+  //      it re-read key lim-1 (finite values; their scores are masked).
   const size_t cache_base = (static_cast<size_t>(b) * pl.Hkv + kvh) * static_cast<size_t>(pl.p_max) * HD;
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + cache_base;
   const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + cache_base;
@@ -284,9 +295,9 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const size_t blk_row = static_cast<size_t>(pl.Hkv) * HD;  // elements between block rows
   const uint16_t* kblk_b = kblk + (static_cast<size_t>(b) * twoB * pl.Hkv + kvh) * HD;
   const uint16_t* vblk_b = vblk + (static_cast<size_t>(b) * twoB * pl.Hkv + kvh) * HD;
-  auto issue = [&](int ST, int t, int ntl, int lim) __attribute__((always_inline)) {
-    if (t < ntl) {
-      const int kb = c0 + t * KT;
+  auto issue = [&](int ST, int t, int lim) __attribute__((always_inline)) {
+    if (t >= nbt) {
+      const int kb = c0 + (t - nbt) * KT;
       const bool full = kb + KT <= lim;
       const uint16_t* ktile = kc + static_cast<size_t>(kb) * HD;
       const uint16_t* vtile = vc + static_cast<size_t>(kb) * HD;
@@ -303,42 +314,56 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
         dma16s(isv ? vtile : ktile, off, sbase + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024);
       }
     } else {
-      const int bt = t - ntl;
 #pragma unroll
       for (int mm = 0; mm < LPW; ++mm) {
         const int ins = wave * LPW + mm;
         const bool isv = ins >= L::IPT;
         const int ii = isv ? ins - L::IPT : ins;
-        const int c = min(bt * KT + static_cast<int>(goff[mm] / L::ROWB), twoB - 1);
+        const int c = min(t * KT + static_cast<int>(goff[mm] / L::ROWB), twoB - 1);
         const uint32_t off = static_cast<uint32_t>(c * blk_row * 2) + goff[mm] % L::ROWB;
         dma16s(isv ? vblk_b : kblk_b, off, sbase + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024);
       }
     }
   };
   // tiles [from, to) of the ring, to <= NSTAGE
-  auto issue_range = [&](int from, int to, int ntl, int lim) __attribute__((always_inline)) {
-    for (int t = from; t < to; ++t) issue(t, t, ntl, lim);
+  auto issue_range = [&](int from, int to, int lim) __attribute__((always_inline)) {
+    for (int t = from; t < to; ++t) issue(t, t, lim);
   };
 
-  // The first prompt tiles go in flight before prompt_len is known, assuming
-  // the whole cache capacity (always in bounds).
+  // Tile order: the block tiles (split 0 only), then the prompt tiles.  The
+  // first tiles go in flight before prompt_len is known, the prompt ones
+  // assuming the whole cache capacity (always in bounds).
   const int c1s = min(c0 + pl.chunk, pl.p_max);
   const int nts = c1s > c0 ? (c1s - c0 + KT - 1) / KT : 0;
-  const int nspec = min(NPRO, nts);
-  issue_range(0, nspec, nts, c1s);
-  const double lane_inv_freq = rope_inv_freq(tid % HALF, HD, pl.log2_base);
+  const int nspec = min(NPRO, nbt + nts);
+  issue_range(0, nspec, c1s);
 
-  // ---- wait for the prologue loads only, then share them
+  // ---- RoPE table of the B block positions, while the loads are in flight:
+  //      positions come by scalar loads (a wave's 64 entries need at most two)
+  float2* cs_tab = reinterpret_cast<float2*>(smem + TABREG);
+  {
+    const double lane_inv_freq = rope_inv_freq(tid % HALF, HD, pl.log2_base);
+    for (int i0 = 0; i0 < B * HALF; i0 += NT) {
+      const int kw = __builtin_amdgcn_readfirstlane((i0 + wave * 64) / HALF);
+      const int k0 = min(kw, B - 1), k1 = min(kw + 1, B - 1);
+      int p0 = plen + k0, p1 = plen + k1;
+      if (pos_b) sload2(pos_b + k0, pos_b + k1, p0, p1);
+      const int i = i0 + tid;
+      if (i < B * HALF) cs_tab[i] = rope_cos_sin(i / HALF == kw ? p0 : p1, lane_inv_freq);
+    }
+  }
+
+  // ---- wait for the prologue loads only (all but the ring's), then share them
   if (NSTAGE > 3 && nspec >= 4)
-    wait_counts<(NSTAGE > 3 ? 4 : 0) * LPW, 15>();
+    wait_counts<(NSTAGE > 3 ? 4 : 0) * LPW, 0>();
   else if (nspec >= 3)
-    wait_counts<3 * LPW, 15>();
+    wait_counts<3 * LPW, 0>();
   else if (nspec == 2)
-    wait_counts<2 * LPW, 15>();
+    wait_counts<2 * LPW, 0>();
   else if (nspec == 1)
-    wait_counts<LPW, 15>();
+    wait_counts<LPW, 0>();
   else
-    wait_counts<0, 15>();
+    wait_counts<0, 0>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
@@ -355,7 +380,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const bool status_writer = a.status && kvh == 0 && s == 0 && rg == 0 && tid == 0;
   const int c1 = min(c0 + pl.chunk, plen);
   const int ntiles = c1 > c0 ? (c1 - c0 + KT - 1) / KT : 0;
-  const int T = ntiles + nbt;
+  const int T = nbt + ntiles;
   if (st || T == 0) {
     wait_counts<0, 15>();  // drain the ring loads before the workgroup's LDS is released
     if (status_writer) a.status[b] = st;
@@ -367,58 +392,50 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     }
     return;
   }
-  // A speculative tile that reaches past the prompt may hold cache rows
-  // beyond P_b (any bits, NaN included, which a zero probability would not
-  // cancel in P V), and its stage may be needed for the block: drop them all
-  // and issue again.  Then fill the remaining prologue stages.
+  // A speculative prompt tile that reaches past the prompt may hold cache
+  // rows beyond P_b (any bits, NaN included, which a zero probability would
+  // not cancel in P V): drop them and issue again.  Then fill the remaining
+  // prologue stages.
   int issued = nspec;
-  if (nspec > 0 && c0 + nspec * KT > c1) {
+  if (nspec > nbt && c0 + (nspec - nbt) * KT > c1) {
     wait_counts<0, 15>();
-    issued = 0;
+    issued = nbt;
   }
-  issue_range(issued, min(NPRO, T), ntiles, c1);
+  issue_range(issued, min(NPRO, T), c1);
 
-  // ---- RoPE table of the B block positions
-  float2* cs_tab = reinterpret_cast<float2*>(smem + TABREG);
-  for (int i = tid; i < B * HALF; i += NT) {
-    const int k = i / HALF;
-    cs_tab[i] = rope_cos_sin(pos_b ? tp[64 + k] : plen + k, lane_inv_freq);
+  // ---- rotate the staged query rows in place (one granule pair per item)
+  for (int it = tid; it < RW * 16 * (L::GR / 2); it += NT) {
+    const int lr = it / (L::GR / 2), j = it % (L::GR / 2);
+    const int mq = rg * pl.rows_wg + lr;
+    if (mq >= pl.M) continue;
+    unsigned char* qrow = smem + S::qrow(lr);
+    uint4* px = reinterpret_cast<uint4*>(qrow + ((j ^ (lr & (L::GR - 1))) << 4));
+    uint4* py = reinterpret_cast<uint4*>(qrow + (((j + L::GR / 2) ^ (lr & (L::GR - 1))) << 4));
+    const uint4 x4 = *px, y4 = *py;
+    const float4* csr = reinterpret_cast<const float4*>(cs_tab + ((mq % twoB) % B) * HALF + 8 * j);
+    float4 c4[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) c4[q4] = csr[q4];
+    const uint32_t wx[4] = {x4.x, x4.y, x4.z, x4.w};
+    const uint32_t wy[4] = {y4.x, y4.y, y4.z, y4.w};
+    uint32_t ox[4], oy[4];
+    rotate8(wx, wy, c4, ox, oy);
+    *px = make_uint4(ox[0], ox[1], ox[2], ox[3]);
+    *py = make_uint4(oy[0], oy[1], oy[2], oy[3]);
   }
   lds_barrier<63>();
 
-  // ---- rotated Q operand and block visibility of this lane's row
+  // ---- Q operand and block visibility of this lane's row
   bf16x8 qop[KSTEPS];
   uint64_t vis_lo = 0, vis_hi = 0;
   const int tau_row = __shfl(tau_v, r % B);  // stage of this lane's response position
   {
     const int lr = rw * 16 + n;
     const unsigned char* qrow = smem + S::qrow(lr);
-    uint32_t qw[KSTEPS][4];
 #pragma unroll
     for (int i = 0; i < KSTEPS; ++i) {
-      const uint4 w = *reinterpret_cast<const uint4*>(qrow + (((4 * i + g) ^ (lr & (L::GR - 1))) << 4));
-      qw[i][0] = w.x;
-      qw[i][1] = w.y;
-      qw[i][2] = w.z;
-      qw[i][3] = w.w;
-    }
-    const float4* csr = reinterpret_cast<const float4*>(cs_tab + (r % B) * HALF);
-#pragma unroll
-    for (int i = 0; i < KSTEPS / 2; ++i) {
-      float4 c4[4];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) c4[q4] = csr[(32 * i + 8 * g) / 2 + q4];
-      uint32_t ox[4], oy[4];
-      rotate8(qw[i], qw[i + KSTEPS / 2], c4, ox, oy);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qw[i][e] = rok ? ox[e] : 0u;
-        qw[i + KSTEPS / 2][e] = rok ? oy[e] : 0u;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) {
-      const uint4 w = make_uint4(qw[i][0], qw[i][1], qw[i][2], qw[i][3]);
+      const uint4 w = rok ? *reinterpret_cast<const uint4*>(qrow + (((4 * i + g) ^ (lr & (L::GR - 1))) << 4))
+                          : make_uint4(0u, 0u, 0u, 0u);
       qop[i] = __builtin_bit_cast(bf16x8, w);
     }
     if (rok) {
@@ -436,7 +453,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   }
   if (!QSEP) {
     lds_barrier<63>();  // every wave holds its query rows: the last stage is free
-    if (NSTAGE - 1 < T) issue(NSTAGE - 1, NSTAGE - 1, ntiles, c1);
+    if (NSTAGE - 1 < T) issue(NSTAGE - 1, NSTAGE - 1, c1);
   }
 
   // ---- loop-invariant LDS offsets of this lane's operand reads
@@ -504,7 +521,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       }
   };
 
-  // Rotate block tile bt (its K rows in stage ST) in place.
+  // Rotate block tile bt (its K rows in stage st) in place.
   auto rotate_block = [&](int st, int bt) __attribute__((always_inline)) {
     unsigned char* Kb = smem + KREG + st * L::TILEB;
     const int nvalid = min(KT, twoB - bt * KT);
@@ -588,20 +605,22 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   // ---- the T = ntiles + nbt tiles, software-pipelined over the ring.
   //      Before step t: tiles 0 .. min(t + NSTAGE - 2, T - 1) are issued
   //      (0 .. min(NSTAGE, T) - 1 for t = 0), in tile order.
-  f32x4 sb[2][NSUB];  // scores of tiles t (sb[t % 2]) and t+1
+  // Score buffer of tile t: sb[(t - nbt) % 2].
+  f32x4 sb[2][NSUB];
   int* pass_flag = reinterpret_cast<int*>(smem + S::TPREG + 512 - 4);  // after the positions
+  const int nfull = (c1 - c0) / KT;  // whole prompt tiles: nbt .. nbt + nfull - 1
   for (int pass = 0;; ++pass) {
   if (T >= NSTAGE)
     lds_barrier<(NSTAGE - 1) * LPW>();  // tile 0 landed
   else
     lds_barrier<0>();
-  if (ntiles == 0) rotate_block(0, 0);
-  scores(0, sb[0]);
-  // Tiles [0, nfull) are whole prompt tiles (every key visible); the rest
-  // (a ragged prompt tail, then the block tiles) go through the masked path.
-  const int nfull = (c1 - c0) / KT;
+  if (nbt > 0) rotate_block(0, 0);
+  if (nbt & 1)
+    scores(0, sb[1]);
+  else
+    scores(0, sb[0]);
   auto step = [&](auto p_c, auto mode_c, int t) __attribute__((always_inline)) {
-    constexpr int P = decltype(p_c)::value;  // t % 2
+    constexpr int P = decltype(p_c)::value;  // (t - nbt) % 2
     const int K = t % NSTAGE;                // stage of tile t
     const int K1 = K + 1 == NSTAGE ? 0 : K + 1;
     if (t + 1 < T) {
@@ -617,9 +636,9 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
           lds_barrier<(NSTAGE - 3) * LPW>();
         else
           lds_barrier<0>();
-        if (t + NSTAGE - 1 < T) issue(K == 0 ? NSTAGE - 1 : K - 1, t + NSTAGE - 1, ntiles, c1);
+        if (t + NSTAGE - 1 < T) issue(K == 0 ? NSTAGE - 1 : K - 1, t + NSTAGE - 1, c1);
       }
-      if (t + 1 >= ntiles) rotate_block(K1, t + 1 - ntiles);
+      if (t + 1 < nbt) rotate_block(K1, t + 1);
     }
     bf16x8 vop[DTILES][NU];
     vread(K, vop);
@@ -627,15 +646,21 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     if (decltype(mode_c)::value == 0) {
       finish(IC<0>{}, sb[P], vop, 0ull);
     } else {
-      const int nk = c1 - (c0 + t * KT);  // keys of a prompt tile below c1
-      const uint64_t cm = t >= ntiles ? (t == ntiles ? vis_lo : vis_hi)
-                                      : (nk >= KT ? ~0ull : (1ull << nk) - 1ull);
+      const int nk = c1 - (c0 + (t - nbt) * KT);  // keys of a prompt tile below c1
+      const uint64_t cm = t < nbt ? (t == 0 ? vis_lo : vis_hi) : (nk >= KT ? ~0ull : (1ull << nk) - 1ull);
       finish(IC<1>{}, sb[P], vop, cm);
     }
   };
-  // unrolled by two so the score buffers are constants
-  int t0 = 0;
-  for (; t0 + 2 <= nfull; t0 += 2) {
+  // block tiles, then whole prompt tiles two at a time (the score buffers are
+  // constants), then the rest through the masked path
+  if (nbt == 1) {
+    step(IC<1>{}, IC<1>{}, 0);
+  } else if (nbt == 2) {
+    step(IC<0>{}, IC<1>{}, 0);
+    step(IC<1>{}, IC<1>{}, 1);
+  }
+  int t0 = nbt;
+  for (; t0 + 2 <= nbt + nfull; t0 += 2) {
     step(IC<0>{}, IC<0>{}, t0);
     step(IC<1>{}, IC<0>{}, t0 + 1);
   }
@@ -666,7 +691,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   lpart = 0.0f;
 #pragma unroll
   for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  issue_range(0, min(NSTAGE, T), ntiles, c1);
+  issue_range(0, min(NSTAGE, T), c1);
   }
 
   // ---- combine the key splits of each row (through the drained ring)
