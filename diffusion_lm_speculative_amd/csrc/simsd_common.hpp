@@ -52,21 +52,15 @@ __device__ __forceinline__ void mask_row_bits_at(TauAt tau_at, int B, int r, int
     return;
   }
   const bool slot_row = r >= B;
-  const int i = slot_row ? r - B : r;
-  const int ti = tau_at(i);
-  uint64_t d = 0, m = 0;
-  for (int j = 0; j < B; ++j) {
-    const int tj = tau_at(j);
-    const uint64_t bit = 1ull << j;
-    if (slot_row) {
-      if (tj < ti) d |= bit;
-      if (tj >= ti) m |= bit;
-    } else if (tj <= ti) {
-      d |= bit;
-    }
-  }
-  dbits = d;
-  mbits = m;
+  const int ti = tau_at(slot_row ? r - B : r);
+  // D_j is visible when tau_j <= lim (a slot row needs tau_j < tau_i); a slot
+  // row sees exactly the slots D~_j whose data token it does not see.
+  const int lim = slot_row ? ti - 1 : ti;
+  uint32_t lo = 0, hi = 0;
+  for (int j = 0; j < B && j < 32; ++j) lo |= static_cast<uint32_t>(tau_at(j) <= lim) << j;
+  for (int j = 32; j < B; ++j) hi |= static_cast<uint32_t>(tau_at(j) <= lim) << (j - 32);
+  dbits = (static_cast<uint64_t>(hi) << 32) | lo;
+  mbits = slot_row ? (all & ~dbits) : 0ull;
 }
 
 __device__ __forceinline__ void mask_row_bits(const int32_t* tau, int B, int r, int mode, uint64_t& dbits,

@@ -428,7 +428,6 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   // ---- Q operand and block visibility of this lane's row
   bf16x8 qop[KSTEPS];
   uint64_t vis_lo = 0, vis_hi = 0;
-  const int tau_row = __shfl(tau_v, r % B);  // stage of this lane's response position
   {
     const int lr = rw * 16 + n;
     const unsigned char* qrow = smem + S::qrow(lr);
@@ -440,8 +439,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     }
     if (rok) {
       uint64_t dbits, mbits;
-      mask_row_bits_at([&](int j) { return j == r % B ? tau_row : __builtin_amdgcn_readlane(tau_v, j); }, B, r,
-                       pl.mask_mode, dbits, mbits);
+      mask_row_bits_at([&](int j) { return tp[j]; }, B, r, pl.mask_mode, dbits, mbits);
       if (B >= 64) {
         vis_lo = dbits;
         vis_hi = mbits;
