@@ -155,9 +155,11 @@ def main():
         ast = torch.empty((w.NB,), dtype=torch.int32, device=dev)
         aws = torch.empty(max(sd.accept_workspace_bytes(w.NB, w.B, VOCAB), 256), dtype=torch.uint8, device=dev)
 
-        def accept(a=a, n_acc=n_acc, nxt=nxt, ast=ast, aws=aws, i=i):
-            sd.accept_prefix(a["p"], a["q"], a["draft_tok"], a["tau"], gamma, 1234, i, n_accepted=n_acc,
-                             next_token=nxt, status=ast, workspace=aws, stream=stream)
+        bound = sd.bind_accept(a["p"], a["q"], a["draft_tok"], a["tau"], gamma, n_accepted=n_acc, next_token=nxt,
+                               status=ast, workspace=aws, stream=stream)
+
+        def accept(bound=bound, i=i):
+            bound(1234, i)
 
         sets.append(dict(t=t, a=a, call=call, accept=accept, out=out, lse=lse, st=st, ws=ws, n_acc=n_acc,
                          nxt=nxt, ast=ast, aws=aws))

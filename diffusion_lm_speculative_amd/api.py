@@ -189,6 +189,44 @@ def accept_prefix(p_target, q_draft, draft_tok, tau, gamma, seed, offset=0, *, n
     return n_accepted, next_token, status
 
 
+@dataclass
+class AcceptCall:
+    """An accept_prefix call with every pointer bound once (for timing loops);
+    call it with (seed, offset).  `keep` holds the bound tensors."""
+    args_head: tuple
+    args_tail: tuple
+    keep: tuple = ()
+
+    def __call__(self, seed, offset=0):
+        rc = L.load().simsd_accept_prefix(*self.args_head, ctypes.c_uint64(int(seed)), ctypes.c_uint64(int(offset)),
+                                          *self.args_tail)
+        if rc:
+            L.check(rc, "simsd_accept_prefix")
+
+
+def bind_accept(p_target, q_draft, draft_tok, tau, gamma, *, n_accepted, next_token=None, status=None,
+                workspace=None, stream=None) -> AcceptCall:
+    NB, B, V = p_target.shape
+    dev = p_target.device
+    _need(p_target, "p_target", torch.float32)
+    _need(q_draft, "q_draft", torch.float32, (NB, B, V), dev)
+    _need(draft_tok, "draft_tok", torch.int32, (NB, B), dev)
+    _need(tau, "tau", torch.int32, (NB, B), dev)
+    _need(n_accepted, "n_accepted", torch.int32, (NB,), dev)
+    if next_token is not None:
+        _need(next_token, "next_token", torch.int32, (NB,), dev)
+        ws_bytes = accept_workspace_bytes(NB, B, V)
+        if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+            raise ValueError(f"workspace of {ws_bytes} bytes required")
+    if status is not None:
+        _need(status, "status", torch.int32, (NB,), dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    head = (_ptr(p_target), _ptr(q_draft), _ptr(draft_tok), _ptr(tau), NB, B, int(gamma), V)
+    tail = (_ptr(n_accepted), _ptr(next_token), _ptr(status), _ptr(workspace), ctypes.c_size_t(ws_len),
+            _stream_handle(stream))
+    return AcceptCall(head, tail, (p_target, q_draft, draft_tok, tau, n_accepted, next_token, status, workspace))
+
+
 def debug_mask(tau, mask_mode=L.MASK_TEMPORAL, stream=None):
     """Block visibility words [NB][2B][2] (int64 view of the uint64 bits)."""
     lib = L.load()

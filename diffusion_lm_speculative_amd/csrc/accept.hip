@@ -7,17 +7,21 @@
 // kept with probability min(1, p(x)/q(x)); at the first rejection a
 // replacement is drawn from max(0, p - q) normalised.
 //
-// Two launches.  Both recompute the walk of their sequence (tau inverse,
-// validation, one stage decision per thread; gamma <= 64 Philox draws and
-// 2*gamma gathered floats), which is cheaper than passing it between them.
-//   1. segment sums: the rejected position's row is split into NSEG segments
-//      spread over NB*NSEG workgroups; each sums max(0, p - q) and p over
-//      its segment in fp64 with coalesced loads (the rows dominate the bytes
-//      of this step: 2 * V * 4 bytes per rejecting sequence).
-//   2. select: one workgroup per sequence writes n and the status, walks the
-//      segment sums in order to the segment that holds u' * S, and scans that
-//      segment tile by tile (block-wide fp64 prefix sums) for the first index
-//      whose prefix sum exceeds it.
+// Two launches, both starting with the walk of their sequence in wave 0 (tau
+// inverse and validation, one stage per lane: gamma <= 64 Philox draws and
+// 2*gamma gathered floats).
+//   1. chunk sums, grid (row groups, NB): when a stage rejects, the rejected
+//      position's row is cut into chunks of kChunk elements and each wave
+//      sums max(0, p - q) and p over its chunks in fp64 with coalesced loads
+//      (the rows are the bytes of this step: 2 * V * 4 per rejecting
+//      sequence).
+//      Its first group also stores the walk's outcome (n, status, rejected
+//      position and the replacement draw's Philox word) for launch 2.
+//   2. select, one wave per sequence: writes n and the status; from the
+//      stored walk and the chunk sums (loaded together) it finds the chunk
+//      holding u' * S and scans that chunk for the first index whose prefix
+//      sum exceeds it.  Without a replacement draw this launch alone decides
+//      the walk.
 // The acceptance compare u * q(x) < p(x) is exact in fp64 (24-bit u times a
 // float needs <= 48 bits).  Prefix sums are fp64 in a blocked order, so an
 // index may differ from a strictly sequential sum only where the threshold
@@ -32,8 +36,9 @@
 namespace simsd {
 namespace {
 
-constexpr int kAccThreads = 256;
-constexpr int kScanEpt = 8;  // elements per thread per tile of the in-segment scan
+constexpr int kAccThreads = 512;
+constexpr int kAccWaves = kAccThreads / 64;
+constexpr int kChunk = 1024;                  // elements per chunk: one wave pass, 16 per lane
 
 // Philox-4x64 with 10 rounds: each round multiplies counter words 0 and 2 by
 // the 4x64 multipliers, keeps both 64-bit halves of the products and mixes
@@ -63,50 +68,68 @@ __device__ __forceinline__ uint64_t philox_word0(uint64_t c0, uint64_t c1, uint6
   return c0;
 }
 
-struct Walk {
-  int kinv[65];  // kinv[t] = position of stage t
-  int st;        // status flags
-  int nrej;      // first rejected stage (gamma + 1 when none)
+// The walk's outcome for a sequence, stored by the chunk-sum launch for the
+// select launch.
+struct WalkRecord {
+  int32_t n, st, krow, pad;
+  unsigned long long draw;  // word 0 of the replacement draw (stage n + 1)
+  unsigned long long pad2;
 };
 
-// Validate tau and the walked tokens, then decide every stage in parallel.
-// Block-wide; on return w.st and w.nrej are valid for every thread.
+static_assert(sizeof(WalkRecord) == 32, "walk record layout");
+
+struct Walk {
+  int kinv[65];  // kinv[t] = position of stage t (-1: no position has stage t)
+  int tok[64];   // draft token of each position
+  unsigned long long draw[64];  // word 0 of the replacement draw's counter (b, t, 1, offset), stage t = index + 1
+  int st;        // status flags
+  int n;         // accepted prefix length (gamma when no stage rejects)
+};
+
+// Validate tau and the walked tokens, then decide every stage in parallel
+// (wave 0, one stage per lane).  On return w.st and w.n are valid for every
+// thread.
 __device__ void tau_walk(Walk& w, const float* p, const float* q, const int32_t* tau_b, const int32_t* draft_b,
-                         int b, int B, int gamma, int64_t V, uint64_t seed, uint64_t offset) {
+                         int b, int B, int gamma, int64_t V, uint64_t seed, uint64_t offset, bool draws) {
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    int st = 0;
-    uint64_t seen = 0;
-    for (int k = 0; k < B; ++k) {
-      const int t = tau_b[k];
-      if (t < 1 || t > B) {
-        st = SIMSD_ST_TAU_RANGE;
-      } else {
-        if (((seen >> (t - 1)) & 1ull) && !st) st = SIMSD_ST_TAU_NOT_PERM;
-        seen |= 1ull << (t - 1);
-        w.kinv[t] = k;
-      }
-    }
-    if (st == 0) {
-      for (int t = 1; t <= gamma; ++t) {
-        const int x = draft_b[w.kinv[t]];
-        if (x < 0 || static_cast<int64_t>(x) >= V) st |= SIMSD_ST_TOKEN_RANGE;
-      }
-    }
-    w.st = st;
-    w.nrej = gamma + 1;
+  for (int i = tid; i <= 64; i += blockDim.x) w.kinv[i] = -1;
+  __syncthreads();
+  bool range_bad = false;
+  if (tid < B) {  // stage label and draft token of position tid, loaded together
+    const int t = tau_b[tid];
+    w.tok[tid] = draft_b[tid];
+    range_bad = t < 1 || t > B;
+    if (!range_bad) w.kinv[t] = tid;
   }
   __syncthreads();
-  if (w.st == 0 && tid < gamma) {
-    const int t = tid + 1;
-    const int k = w.kinv[t];
-    const int x = draft_b[k];
-    const uint64_t r = philox_word0(static_cast<uint64_t>(b), static_cast<uint64_t>(t), 0ull, offset, seed, 0ull);
-    const double u = static_cast<double>(r >> 40) * 0x1p-24;
-    const size_t row = (static_cast<size_t>(b) * B + k) * static_cast<size_t>(V);
-    const double pv = static_cast<double>(p[row + x]);
-    const double qv = static_cast<double>(q[row + x]);
-    if (!(u * qv < pv)) atomicMin(&w.nrej, t);
+  if (tid < 64) {  // wave 0
+    // a permutation leaves no stage 1..B without a position
+    const bool missing = tid < B && w.kinv[tid + 1] < 0;
+    int st = __any(range_bad) ? SIMSD_ST_TAU_RANGE : (__any(missing) ? SIMSD_ST_TAU_NOT_PERM : 0);
+    int k = 0, x = 0;
+    if (st == 0 && tid < gamma) {
+      k = w.kinv[tid + 1];
+      x = w.tok[k];
+    }
+    const bool tok_bad = st == 0 && tid < gamma && (x < 0 || static_cast<int64_t>(x) >= V);
+    if (__any(tok_bad)) st = SIMSD_ST_TOKEN_RANGE;
+    bool reject = false;
+    if (st == 0 && tid < gamma) {
+      const int t = tid + 1;
+      const uint64_t r = philox_word0(static_cast<uint64_t>(b), static_cast<uint64_t>(t), 0ull, offset, seed, 0ull);
+      const double u = static_cast<double>(r >> 40) * 0x1p-24;
+      const size_t row = (static_cast<size_t>(b) * B + k) * static_cast<size_t>(V);
+      const double pv = static_cast<double>(p[row + x]);
+      const double qv = static_cast<double>(q[row + x]);
+      reject = !(u * qv < pv);
+    }
+    if (draws && tid < gamma)  // the replacement draw of every stage that could be the first rejected one
+      w.draw[tid] = philox_word0(static_cast<uint64_t>(b), static_cast<uint64_t>(tid + 1), 1ull, offset, seed, 0ull);
+    const uint64_t rej = __ballot(reject);
+    if (tid == 0) {
+      w.st = st;
+      w.n = rej ? __builtin_ctzll(rej) : gamma;
+    }
   }
   __syncthreads();
 }
@@ -116,242 +139,264 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// Segment sums of the residual max(0, p - q) and of p for the rejected
-// position of sequence blockIdx.y; segment blockIdx.x.
-__global__ __launch_bounds__(kAccThreads) void accept_segsum_kernel(const float* __restrict__ p,
-                                                                    const float* __restrict__ q,
-                                                                    const int32_t* __restrict__ draft,
-                                                                    const int32_t* __restrict__ tau, int B,
-                                                                    int gamma, int64_t V, uint64_t seed,
-                                                                    uint64_t offset, int nseg, int64_t segsz,
-                                                                    double* __restrict__ seg_sums) {
+__global__ __launch_bounds__(kAccThreads) void accept_chunks_kernel(
+    const float* __restrict__ p, const float* __restrict__ q, const int32_t* __restrict__ draft,
+    const int32_t* __restrict__ tau, int B, int gamma, int64_t V, uint64_t seed, uint64_t offset, int cpw, int nch,
+    double* __restrict__ chunk_sums, WalkRecord* __restrict__ records) {
   __shared__ Walk w;
-  __shared__ double red[2][kAccThreads / 64];
   const int b = blockIdx.y;
-  const int seg = blockIdx.x;
+  const int grp = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   tau_walk(w, p, q, tau + static_cast<size_t>(b) * B, draft + static_cast<size_t>(b) * B, b, B, gamma, V, seed,
-           offset);
-  const int n = w.nrej - 1;
+           offset, grp == 0);
+  const int n = w.n;
+  if (grp == 0 && tid == 0) {
+    WalkRecord r{};
+    r.n = n;
+    r.st = w.st;
+    r.krow = (w.st == 0 && n < gamma) ? w.kinv[n + 1] : 0;
+    r.draw = (w.st == 0 && n < gamma) ? w.draw[n] : 0ull;
+    records[b] = r;
+  }
   if (w.st || n >= gamma) return;
   const size_t row = (static_cast<size_t>(b) * B + w.kinv[n + 1]) * static_cast<size_t>(V);
   const float* pr = p + row;
   const float* qr = q + row;
-  const int64_t v0 = seg * segsz;
-  const int64_t v1 = min(V, v0 + segsz);
-  double sr = 0.0, sp = 0.0;
-  int64_t v = v0 + threadIdx.x;
-  for (; v + 3 * kAccThreads < v1; v += 4 * kAccThreads) {
-    float pv[4], qv[4];
+  double* cs = chunk_sums + static_cast<size_t>(b) * nch * 2;
+  const int c_end = min(nch, (grp + 1) * cpw);
+  const bool vec = (reinterpret_cast<uintptr_t>(pr) % 16 == 0) && (reinterpret_cast<uintptr_t>(qr) % 16 == 0);
+  for (int c = grp * cpw + wave; c < c_end; c += kAccWaves) {
+    float pv[16], qv[16];
+    if (vec && static_cast<int64_t>(c + 1) * kChunk <= V) {  // whole chunk, 16-byte loads
+      const float4* p4 = reinterpret_cast<const float4*>(pr + static_cast<int64_t>(c) * kChunk) + lane;
+      const float4* q4 = reinterpret_cast<const float4*>(qr + static_cast<int64_t>(c) * kChunk) + lane;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      pv[u] = pr[v + u * kAccThreads];
-      qv[u] = qr[v + u * kAccThreads];
+      for (int i = 0; i < 4; ++i) {
+        const float4 a = p4[64 * i], bq = q4[64 * i];
+        pv[4 * i + 0] = a.x; pv[4 * i + 1] = a.y; pv[4 * i + 2] = a.z; pv[4 * i + 3] = a.w;
+        qv[4 * i + 0] = bq.x; qv[4 * i + 1] = bq.y; qv[4 * i + 2] = bq.z; qv[4 * i + 3] = bq.w;
+      }
+    } else {
+      const int64_t v0 = static_cast<int64_t>(c) * kChunk + lane;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {  // unconditional loads (clamped index) so they all go out at once
+        const int64_t v = min(v0 + 64 * i, V - 1);
+        pv[i] = pr[v];
+        qv[i] = qr[v];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (v0 + 64 * i >= V) pv[i] = qv[i] = 0.0f;
     }
+    double sr = 0.0, sp = 0.0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const double d = static_cast<double>(pv[u]) - static_cast<double>(qv[u]);
+    for (int i = 0; i < 16; ++i) {
+      const double d = static_cast<double>(pv[i]) - static_cast<double>(qv[i]);
       sr += d > 0.0 ? d : 0.0;
-      sp += static_cast<double>(pv[u]);
+      sp += static_cast<double>(pv[i]);
     }
-  }
-  for (; v < v1; v += kAccThreads) {
-    const double d = static_cast<double>(pr[v]) - static_cast<double>(qr[v]);
-    sr += d > 0.0 ? d : 0.0;
-    sp += static_cast<double>(pr[v]);
-  }
-  sr = wave_sum(sr);
-  sp = wave_sum(sp);
-  const int wv = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    red[0][wv] = sr;
-    red[1][wv] = sp;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double a = 0.0, c = 0.0;
-    for (int i = 0; i < kAccThreads / 64; ++i) {
-      a += red[0][i];
-      c += red[1][i];
+    sr = wave_sum(sr);
+    sp = wave_sum(sp);
+    if (lane == 0) {
+      cs[2 * c + 0] = sr;
+      cs[2 * c + 1] = sp;
     }
-    seg_sums[(static_cast<size_t>(b) * nseg + seg) * 2 + 0] = a;
-    seg_sums[(static_cast<size_t>(b) * nseg + seg) * 2 + 1] = c;
   }
 }
 
-__device__ __forceinline__ double weight(const float* p, const float* q, int64_t v, bool residual) {
-  const double pv = static_cast<double>(p[v]);
-  if (!residual) return pv;
-  const double r = pv - static_cast<double>(q[v]);
-  return r > 0.0 ? r : 0.0;
-}
+__device__ __forceinline__ double chunk_sum_global(const double* cs, int c, int col) { return cs[2 * c + col]; }
 
-struct Select {
-  double wtot[kAccThreads / 64];
-  double base, thr, total;
-  unsigned long long pick;  // candidate index (min over threads)
-  unsigned long long last;  // 1 + last index with positive weight (max over threads)
-  int sel;
-  int residual;
-};
-
-// Exclusive prefix over the block in thread order; the block total is left in
-// sh.total.  Wave-level shuffle scan, then the wave totals.
-__device__ __forceinline__ double block_excl_scan(double v, Select& sh) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+__device__ __forceinline__ double wave_excl_scan(double v) {
+  const int lane = threadIdx.x & 63;
   double inc = v;
   for (int d = 1; d < 64; d <<= 1) {
     const double y = __shfl_up(inc, d);
     if (lane >= d) inc += y;
   }
-  __syncthreads();
-  if (lane == 63) sh.wtot[wv] = inc;
-  __syncthreads();
-  double before = 0.0, total = 0.0;
-  for (int i = 0; i < kAccThreads / 64; ++i) {
-    if (i < wv) before += sh.wtot[i];
-    total += sh.wtot[i];
-  }
-  if (threadIdx.x == 0) sh.total = total;
-  return before + (inc - v);
+  return inc - v;
 }
 
-__global__ __launch_bounds__(kAccThreads) void accept_select_kernel(const float* __restrict__ p,
-                                                                    const float* __restrict__ q,
-                                                                    const int32_t* __restrict__ draft,
-                                                                    const int32_t* __restrict__ tau, int B,
-                                                                    int gamma, int64_t V, uint64_t seed,
-                                                                    uint64_t offset, int nseg, int64_t segsz,
-                                                                    const double* __restrict__ seg_sums,
-                                                                    int32_t* n_acc, int32_t* next_tok,
-                                                                    int32_t* status) {
+// One wave per sequence: writes n and the status; when a stage rejected,
+// walks the chunk sums (loaded while it decides the walk) to the chunk
+// holding u' * S and scans that chunk for the first index whose prefix sum
+// exceeds it.  Lane l takes chunks l*kPre.. and elements l*16.. of a chunk,
+// so a lane's sequential sum followed by a wave scan keeps index order.
+constexpr int kPre = 4;  // chunk sums per lane per pass
+
+__global__ __launch_bounds__(64) void accept_select_kernel(
+    const float* __restrict__ p, const float* __restrict__ q, const int32_t* __restrict__ draft,
+    const int32_t* __restrict__ tau, int B, int gamma, int64_t V, uint64_t seed, uint64_t offset, int nch,
+    const double* __restrict__ chunk_sums, const WalkRecord* __restrict__ records, int32_t* n_acc,
+    int32_t* next_tok, int32_t* status) {
   __shared__ Walk w;
-  __shared__ Select sh;
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  tau_walk(w, p, q, tau + static_cast<size_t>(b) * B, draft + static_cast<size_t>(b) * B, b, B, gamma, V, seed,
-           offset);
-  const int n = w.nrej - 1;
-  if (w.st) {
-    if (tid == 0) {
-      n_acc[b] = -1;
-      if (next_tok) next_tok[b] = -1;
+  const int lane = threadIdx.x;
+  if (!next_tok) {  // no replacement draw: only the walk
+    tau_walk(w, p, q, tau + static_cast<size_t>(b) * B, draft + static_cast<size_t>(b) * B, b, B, gamma, V, seed,
+             offset, false);
+    if (lane == 0) {
+      n_acc[b] = w.st ? -1 : w.n;
       if (status) status[b] = w.st;
     }
     return;
   }
-  if (tid == 0) {
-    n_acc[b] = n;
-    if (status) status[b] = 0;
+  // the walk's record and the first pass of chunk sums, loaded together
+  // (the sums are unused when no stage rejected)
+  const WalkRecord rec = records[b];
+  const double* cs = chunk_sums + static_cast<size_t>(b) * nch * 2;
+  double pre[kPre][2];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int c = lane * kPre + i;
+    const bool ok = c < nch;
+    pre[i][0] = ok ? cs[2 * c + 0] : 0.0;
+    pre[i][1] = ok ? cs[2 * c + 1] : 0.0;
   }
-  if (!next_tok) return;
-  if (n >= gamma) {
-    if (tid == 0) next_tok[b] = -1;
+  const int n = rec.n;
+  if (rec.st || n >= gamma) {
+    if (lane == 0) {
+      n_acc[b] = rec.st ? -1 : n;
+      next_tok[b] = -1;
+      if (status) status[b] = rec.st;
+    }
     return;
   }
-  const size_t row = (static_cast<size_t>(b) * B + w.kinv[n + 1]) * static_cast<size_t>(V);
+  const size_t row = (static_cast<size_t>(b) * B + rec.krow) * static_cast<size_t>(V);
   const float* pr = p + row;
   const float* qr = q + row;
-  if (tid == 0) {
-    const double* ss = seg_sums + static_cast<size_t>(b) * nseg * 2;
-    double tot_r = 0.0, tot_p = 0.0;
-    for (int s = 0; s < nseg; ++s) {
-      tot_r += ss[2 * s];
-      tot_p += ss[2 * s + 1];
+  constexpr int kPass = 64 * kPre;  // chunks per pass
+  auto chunk_sum = [&](int pass, int i, int col) {
+    const int c = pass * kPass + lane * kPre + i;
+    return pass == 0 ? pre[i][col] : (c < nch ? cs[2 * c + col] : 0.0);
+  };
+
+  // ---- totals; all-zero residual: draw from p itself
+  double tr = 0.0, tp = 0.0;
+  for (int pass = 0; pass * kPass < nch; ++pass)
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+      tr += chunk_sum(pass, i, 0);
+      tp += chunk_sum(pass, i, 1);
     }
-    const bool residual = tot_r > 0.0;
-    const double tot = residual ? tot_r : tot_p;
-    const int col = residual ? 0 : 1;
-    const uint64_t r2 = philox_word0(static_cast<uint64_t>(b), static_cast<uint64_t>(n + 1), 1ull, offset, seed,
-                                     0ull);
-    const double thr = static_cast<double>(r2 >> 11) * 0x1p-53 * tot;
-    int sel = -1;
-    double acc = 0.0;
-    if (tot > 0.0) {
-      sel = nseg - 1;
-      for (int s = 0; s < nseg; ++s) {
-        if (acc + ss[2 * s + col] > thr) {
-          sel = s;
-          break;
-        }
-        if (s + 1 < nseg) acc += ss[2 * s + col];
-      }
+  tr = wave_sum(tr);
+  tp = wave_sum(tp);
+  const bool residual = tr > 0.0;
+  const double tot = residual ? tr : tp;
+  const int col = residual ? 0 : 1;
+  const double thr = static_cast<double>(rec.draw >> 11) * 0x1p-53 * tot;
+  if (!(tot > 0.0)) {
+    if (lane == 0) {
+      n_acc[b] = n;
+      next_tok[b] = -1;
+      if (status) status[b] = 0;
     }
-    sh.sel = sel;
-    sh.base = acc;
-    sh.thr = thr;
-    sh.residual = residual;
-    sh.pick = ~0ull;
-    sh.last = 0ull;
-  }
-  __syncthreads();
-  if (sh.sel < 0) {
-    if (tid == 0) next_tok[b] = -1;
     return;
   }
-  const bool residual = sh.residual;
-  const double thr = sh.thr;
-  double base = sh.base;
-  const int64_t v_end = V;  // a crossing missed by rounding continues into later segments
-  const int64_t tsz = static_cast<int64_t>(kAccThreads) * kScanEpt;
-  unsigned long long last = 0ull;
-  for (int64_t t0 = sh.sel * segsz; t0 < v_end; t0 += tsz) {
-    const int64_t v0 = t0 + static_cast<int64_t>(tid) * kScanEpt;
-    double wv[kScanEpt];
-    double part = 0.0;
+
+  // ---- first chunk whose inclusive prefix exceeds thr (the last chunk when
+  //      rounding leaves none), and the prefix before it
+  int pick = nch - 1;
+  double base = -1.0;
+  double carry = 0.0;
+  for (int pass = 0; pass * kPass < nch && base < 0.0; ++pass) {
+    double v[kPre], sum = 0.0;
 #pragma unroll
-    for (int e = 0; e < kScanEpt; ++e) {
-      wv[e] = (v0 + e < v_end) ? weight(pr, qr, v0 + e, residual) : 0.0;
-      part += wv[e];
+    for (int i = 0; i < kPre; ++i) {
+      v[i] = chunk_sum(pass, i, col);
+      sum += v[i];
     }
-    double run = base + block_excl_scan(part, sh);
+    double run = carry + wave_excl_scan(sum);
+    int mine = -1;
+    double mybase = 0.0;
 #pragma unroll
-    for (int e = 0; e < kScanEpt; ++e) {
+    for (int i = 0; i < kPre; ++i) {
+      const int c = pass * kPass + lane * kPre + i;
+      if (mine < 0 && c < nch && run + v[i] > thr) {
+        mine = c;
+        mybase = run;
+      }
+      run += v[i];
+    }
+    const uint64_t hit = __ballot(mine >= 0);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      pick = __shfl(mine, src);
+      base = __shfl(mybase, src);
+    }
+    carry += wave_sum(sum);
+  }
+  if (base < 0.0) base = carry - (pick == nch - 1 ? chunk_sum_global(cs, pick, col) : 0.0);
+
+  // ---- scan from that chunk on (a crossing missed by rounding continues
+  //      into later chunks; failing that, the last index with positive weight)
+  int64_t found = -1, lastpos = -1;
+  for (int64_t t0 = static_cast<int64_t>(pick) * kChunk; t0 < V && found < 0; t0 += kChunk) {
+    const int64_t v0 = t0 + lane * 16;
+    double wv[16], sum = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t v = min(v0 + e, V - 1);
+      const double pv = static_cast<double>(pr[v]);
+      double x = pv;
+      if (residual) {
+        const double r = pv - static_cast<double>(qr[v]);
+        x = r > 0.0 ? r : 0.0;
+      }
+      wv[e] = v0 + e < V ? x : 0.0;
+      sum += wv[e];
+    }
+    double run = base + wave_excl_scan(sum);
+    int64_t mine = -1, mylast = -1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
       run += wv[e];
       if (wv[e] > 0.0) {
-        last = static_cast<unsigned long long>(v0 + e) + 1ull;
-        if (run > thr) {
-          atomicMin(&sh.pick, static_cast<unsigned long long>(v0 + e));
-          break;
-        }
+        mylast = v0 + e;
+        if (mine < 0 && run > thr) mine = v0 + e;
       }
     }
-    __syncthreads();
-    if (sh.pick != ~0ull) break;
-    base += sh.total;
+    const uint64_t hit = __ballot(mine >= 0);
+    if (hit) found = __shfl(mine, __builtin_ctzll(hit));
+    const uint64_t pos = __ballot(mylast >= 0);
+    if (pos) lastpos = __shfl(mylast, 63 - __builtin_clzll(pos));
+    base += wave_sum(sum);
   }
-  if (last) atomicMax(&sh.last, last);
-  __syncthreads();
-  if (tid == 0) next_tok[b] = sh.pick != ~0ull ? static_cast<int32_t>(sh.pick) : static_cast<int32_t>(sh.last) - 1;
+  if (lane == 0) {
+    n_acc[b] = n;
+    next_tok[b] = static_cast<int32_t>(found >= 0 ? found : lastpos);
+    if (status) status[b] = 0;
+  }
 }
 
 }  // namespace
 
-// Segments per row: enough workgroups to spread the row reads over the chip
-// (about 512 in total), each segment at least 4096 elements.
-void accept_plan(int NB, int64_t V, int& nseg, int64_t& segsz) {
-  int64_t ns = NB > 0 ? (512 + NB - 1) / NB : 1;
-  const int64_t cap = (V + 4095) / 4096;
-  if (ns > cap) ns = cap;
-  if (ns < 1) ns = 1;
-  if (ns > 256) ns = 256;
-  segsz = (V + ns - 1) / ns;
-  nseg = static_cast<int>((V + segsz - 1) / segsz);
+// Chunks per row and row groups: chunks of kChunk elements, spread over about
+// 512 workgroups in total, at least 4 chunks (one per wave) per group.
+void accept_plan(int NB, int64_t V, int& nch, int& cpw, int& ngrp) {
+  nch = static_cast<int>((V + kChunk - 1) / kChunk);
+  const int64_t want = NB > 0 ? (static_cast<int64_t>(nch) * NB + 511) / 512 : 1;
+  cpw = static_cast<int>(want < kAccWaves ? kAccWaves : want);
+  if (cpw > nch) cpw = nch;
+  ngrp = (nch + cpw - 1) / cpw;
 }
 
 hipError_t launch_accept(const float* p, const float* q, const int32_t* draft, const int32_t* tau,
                          int NB, int B, int gamma, int64_t V, uint64_t seed, uint64_t offset,
-                         int32_t* n_acc, int32_t* next_tok, int32_t* status, double* seg_sums, hipStream_t s) {
-  int nseg;
-  int64_t segsz;
-  accept_plan(NB, V, nseg, segsz);
+                         int32_t* n_acc, int32_t* next_tok, int32_t* status, void* workspace, hipStream_t s) {
+  int nch, cpw, ngrp;
+  accept_plan(NB, V, nch, cpw, ngrp);
+  double* chunk_sums = static_cast<double*>(workspace);
+  WalkRecord* records = nullptr;
   if (next_tok) {
-    hipLaunchKernelGGL(accept_segsum_kernel, dim3(nseg, NB), dim3(kAccThreads), 0, s, p, q, draft, tau, B, gamma,
-                       V, seed, offset, nseg, segsz, seg_sums);
+    const size_t off = (static_cast<size_t>(NB) * nch * 2 * sizeof(double) + 255) / 256 * 256;
+    records = reinterpret_cast<WalkRecord*>(static_cast<char*>(workspace) + off);
+    hipLaunchKernelGGL(accept_chunks_kernel, dim3(ngrp, NB), dim3(kAccThreads), 0, s, p, q, draft, tau, B, gamma, V,
+                       seed, offset, cpw, nch, chunk_sums, records);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(accept_select_kernel, dim3(NB), dim3(kAccThreads), 0, s, p, q, draft, tau, B, gamma, V, seed,
-                     offset, nseg, segsz, seg_sums, n_acc, next_tok, status);
+  hipLaunchKernelGGL(accept_select_kernel, dim3(NB), dim3(64), 0, s, p, q, draft, tau, B, gamma, V, seed,
+                     offset, nch, chunk_sums, records, n_acc, next_tok, status);
   return hipGetLastError();
 }
 

@@ -115,13 +115,14 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   return SIMSD_OK;
 }
 
-// Acceptance: fp64 (residual, target) sums per row segment.
+// Acceptance: fp64 (residual, target) sums per row chunk, then a 32-byte
+// walk record per sequence.
 size_t accept_workspace_bytes(int NB, int B, int64_t V) {
   if (NB == 0 || B == 0) return 0;
-  int nseg;
-  int64_t segsz;
-  accept_plan(NB, V, nseg, segsz);
-  return round_up(static_cast<size_t>(NB) * nseg * 2 * sizeof(double), 256);
+  int nch, cpw, ngrp;
+  accept_plan(NB, V, nch, cpw, ngrp);
+  return round_up(static_cast<size_t>(NB) * nch * 2 * sizeof(double), 256) +
+         round_up(static_cast<size_t>(NB) * 32, 256);
 }
 
 size_t workspace_bytes(const Plan& pl) {
@@ -237,7 +238,7 @@ int simsd_accept_prefix(const float* p_target, const float* q_draft, const int32
     if (!aligned(workspace, 256)) return SIMSD_ERR_ALIGN;
   }
   const hipError_t e = launch_accept(p_target, q_draft, draft_tok, tau, batch, B, gamma, vocab, seed, offset,
-                                     n_accepted, next_token, status, static_cast<double*>(workspace),
+                                     n_accepted, next_token, status, workspace,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
 }

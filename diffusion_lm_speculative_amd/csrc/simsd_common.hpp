@@ -171,10 +171,10 @@ hipError_t launch_verify_valu(const Plan& pl, const VerifyArgs& a, hipStream_t s
 hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 size_t mfma_lds_bytes(int hd, int nstage, int B, int rows_wg, bool qsep);
 hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s);
-void accept_plan(int NB, int64_t V, int& nseg, int64_t& segsz);
+void accept_plan(int NB, int64_t V, int& nch, int& cpw, int& ngrp);
 hipError_t launch_accept(const float* p, const float* q, const int32_t* draft, const int32_t* tau,
                          int NB, int B, int gamma, int64_t V, uint64_t seed, uint64_t offset,
-                         int32_t* n_acc, int32_t* next_tok, int32_t* status, double* seg_sums, hipStream_t s);
+                         int32_t* n_acc, int32_t* next_tok, int32_t* status, void* workspace, hipStream_t s);
 hipError_t launch_debug_mask(const int32_t* tau, int NB, int B, int mode, uint64_t* bits, hipStream_t s);
 hipError_t launch_debug_rope(const Plan& pl, const void* q_blk, const void* k_blk,
                              const int32_t* prompt_len, const int32_t* pos_d,

@@ -134,7 +134,9 @@ int simsd_verify_attn(const simsd_verify_desc* desc,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes that simsd_accept_prefix needs when next_token is not NULL
- * (host only, no HIP call): fp64 partial sums of the rejected rows. */
+ * (host only, no HIP call): fp64 partial sums of the rejected rows and a
+ * record of each sequence's walk.  The workspace needs no initialisation; two
+ * calls that overlap in time must not share one. */
 int simsd_accept_prefix_workspace(int32_t batch, int32_t B, int64_t vocab, size_t* bytes);
 
 /* Acceptance walk in tau order (section 4 above, read as textbook rejection

@@ -105,9 +105,10 @@ def test_workspace_query_sizes(lib):
     assert lib.simsd_verify_attn_workspace(None, ctypes.byref(ctypes.c_size_t())) == L.ERR_NULL
     assert lib.simsd_accept_prefix_workspace(4, 8, 151936, None) == L.ERR_NULL
     n = ctypes.c_size_t(7)
-    # fp64 (residual, target) sums per row segment: 512 / 4 = 128 segments per row (>= 4096 entries each)
+    # fp64 (residual, target) sums per 1024-entry chunk of a row (149 chunks for V = 151936), then a
+    # 32-byte walk record per sequence, each part 256-byte aligned
     assert lib.simsd_accept_prefix_workspace(4, 8, 151936, ctypes.byref(n)) == 0
-    assert n.value == (4 * 38 * 2 * 8 + 255) // 256 * 256
+    assert n.value == ru(4 * 149 * 2 * 8) + ru(4 * 32)
     assert lib.simsd_accept_prefix_workspace(4, 0, 151936, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.simsd_accept_prefix_workspace(4, 65, 151936, ctypes.byref(n)) == L.ERR_SHAPE
     assert lib.simsd_accept_prefix_workspace(4, 8, 0, ctypes.byref(n)) == L.ERR_SHAPE

@@ -34,11 +34,12 @@ def _residual_draw_ok(p, q, kinv, n, b, seed, offset, got):
     return lo <= thr + 1e-12 * s and c[got] > thr - 1e-12 * s
 
 
-def _check(inp, gamma, seed, offset):
+def _check(inp, gamma, seed, offset, workspace=None):
     p, q, x, tau = inp["p"], inp["q"], inp["draft_tok"], inp["tau"]
     NB, B, V = p.shape
     print(f"accept NB={NB} B={B} V={V} gamma={gamma} seed={seed} offset={offset}", flush=True)
-    n, nx, st = sd.accept_prefix(p.to(dev()), q.to(dev()), x.to(dev()), tau.to(dev()), gamma, seed, offset)
+    n, nx, st = sd.accept_prefix(p.to(dev()), q.to(dev()), x.to(dev()), tau.to(dev()), gamma, seed, offset,
+                                 workspace=workspace)
     torch.cuda.synchronize()
     pn, qn = p.cpu().numpy(), q.cpu().numpy()
     rn, rnx, rst = accept_ref(pn, qn, x.cpu().numpy(), tau.cpu().numpy(), gamma, seed, offset)
@@ -101,3 +102,38 @@ def test_status_flags():
     inp["draft_tok"][3, 2] = 20
     n, nx = _check(inp, 3, 1, 0)
     assert n.tolist()[1:] == [-1, -1, -1]
+
+
+def test_workspace_reused_across_calls_needs_no_clearing():
+    # One workspace, first filled with 0xff bytes, serves several calls in a
+    # row with different batches, vocabularies and outcomes.
+    ws = torch.full((sd.accept_workspace_bytes(64, 16, 151936),), 0xFF, dtype=torch.uint8, device=dev())
+    for i, (NB, B, V, gamma) in enumerate([(64, 16, 151936, 16), (7, 8, 5000, 8), (64, 16, 151936, 16),
+                                           (30, 4, 20000, 2)]):
+        inp = synth.make_accept_inputs(NB, B, V, seed=700 + i, device=dev())
+        _check(inp, gamma, seed=31 + i, offset=i, workspace=ws)
+
+
+def test_empty_residual_draws_from_target():
+    # p = q / 2 (not normalised): a stage rejects when u >= 1/2, and the
+    # residual max(0, p - q) is then zero everywhere, so the draw uses p.
+    NB, B, V = 24, 6, 3000
+    inp = synth.make_accept_inputs(NB, B, V, seed=77)
+    inp["p"] = inp["q"] * 0.5
+    n, nx = _check(inp, B, 12, 1)
+    assert (n < B).any()
+
+
+def test_bound_call_matches_accept_prefix():
+    NB, B, V = 32, 8, 151936
+    inp = synth.make_accept_inputs(NB, B, V, seed=2002, device=dev())
+    ws = torch.empty(sd.accept_workspace_bytes(NB, B, V), dtype=torch.uint8, device=dev())
+    outs = [torch.full((NB,), -7, dtype=torch.int32, device=dev()) for _ in range(3)]
+    call = sd.bind_accept(inp["p"], inp["q"], inp["draft_tok"], inp["tau"], B, n_accepted=outs[0],
+                          next_token=outs[1], status=outs[2], workspace=ws)
+    for offset in (0, 5):
+        call(1234, offset)
+        n, nx, st = sd.accept_prefix(inp["p"], inp["q"], inp["draft_tok"], inp["tau"], B, 1234, offset)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], n) and torch.equal(outs[1], nx) and torch.equal(outs[2], st)
+    _check(inp, B, 1234, 5)
