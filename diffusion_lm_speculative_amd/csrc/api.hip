@@ -51,9 +51,9 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
 
   if (pl.impl == SIMSD_IMPL_MFMA) {
     // Row waves of 16 rows each, up to 8 (128 rows; more rows take more row
-    // groups, which read the same K/V split at about the same time).  With
-    // fewer than 8 row waves each tile's keys are split over 2 or 4 waves so
-    // that every workgroup runs 4 to 8 waves.
+    // groups, which read the same K/V split on one XCD at about the same
+    // time).  With fewer than 8 row waves each tile's keys are split over 2
+    // or 4 waves so that every workgroup runs 4 to 8 waves.
     const int tiles = (pl.M + 15) / 16;
     int rw = 1;
     while (rw < tiles && rw < 8) rw *= 2;
@@ -107,6 +107,7 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   pl.chunk = static_cast<int>(chunk);
   pl.nsplit = static_cast<int>(nsplit);
   const int64_t grid = nsplit * pl.nrg * static_cast<int64_t>(pl.NB) * pl.Hkv;
+  pl.rg_xcd = pl.impl == SIMSD_IMPL_MFMA && pl.nrg > 1 && (grid / pl.nrg) % 8 == 0;
   if (grid > 0x7fffffffLL) return SIMSD_ERR_SHAPE;
   if (pl.nsplit > 1) {
     pl.part_o_floats = static_cast<size_t>(pl.NB) * pl.Hkv * pl.nsplit * pl.M * pl.d;

@@ -227,11 +227,21 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const int rw = wave % RW;  // row wave: rows rw*16 .. +15 of the row group
   const int ks = wave / RW;  // key split: keys [ks*64/KSPLIT, (ks+1)*64/KSPLIT) of every tile
 
-  int idx = blockIdx.x;
+  // Workgroup -> (split, row group, KV head, sequence).  Consecutive
+  // workgroups go to different XCDs (blockIdx mod 8); with several row groups
+  // the row groups of one K/V stream share an XCD and run back to back, so
+  // the later ones find its tiles in that XCD's L2.
+  int idx = blockIdx.x, rg = 0;
+  if (pl.nrg > 1 && pl.rg_xcd) {
+    const int y = idx / 8;
+    rg = y % pl.nrg;
+    idx = (y / pl.nrg) * 8 + idx % 8;
+  } else if (pl.nrg > 1) {
+    rg = (idx / pl.nsplit) % pl.nrg;
+    idx = (idx / (pl.nsplit * pl.nrg)) * pl.nsplit + idx % pl.nsplit;
+  }
   const int s = idx % pl.nsplit;
   idx /= pl.nsplit;
-  const int rg = idx % pl.nrg;
-  idx /= pl.nrg;
   const int kvh = idx % pl.Hkv;
   const int b = idx / pl.Hkv;
 
