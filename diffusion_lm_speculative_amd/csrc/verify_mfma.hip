@@ -118,14 +118,23 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // the compiler's view: otherwise it makes every later LDS access of the wave
 // wait for all such loads in flight.  Completion is tracked by hand with
 // s_waitcnt vmcnt, and every path drains the loads before the workgroup ends.
+//
+// The compiler does not know that the asm is a vector memory instruction, so
+// it inserts none of the wait states the CDNA3/CDNA4 ISA requires before one:
+// one after an SALU write of M0 (read by a load with the LDS bit), five after
+// a VALU write of an SGPR the load reads (its address base, which a
+// v_readlane may have just restored from a spill).  The leading s_nop 4
+// gives both.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
 }
 
 // The same load from the wave-uniform base `base` (kept in SGPRs) plus the
 // per-lane byte offset `voff`.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
 
@@ -142,7 +151,8 @@ __device__ __forceinline__ void sload2(const int32_t* p0, const int32_t* p1, int
 
 // One direct-to-LDS load of 4 bytes per lane into LDS at m0 + 4*lane.
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -89,6 +89,27 @@ def test_bf16_small(label, ov, impl):
     _check(gpu_inputs(w, 7 + len(label)), w, f"{label} impl={impl}", impl=impl)
 
 
+LONG = [
+    # (label, overrides): one long split per sequence, so the ring runs its
+    # steady state (refills of every stage) and its ragged end
+    ("rows16", dict(Hq=8, Hkv=8, B=8)),
+    ("rows32", dict(Hq=8, Hkv=2, B=4)),
+    ("rows64", dict(Hq=8, Hkv=2, B=8)),
+    ("rows128", dict(Hq=8, Hkv=2, B=16)),
+    ("rows256", dict(Hq=8, Hkv=2, B=32)),
+    ("rows512", dict(Hq=4, Hkv=1, B=64)),
+    ("d64", dict(Hq=8, Hkv=2, d=64, B=8)),
+]
+
+
+@pytest.mark.parametrize("label,ov", LONG, ids=[s[0] for s in LONG])
+def test_bf16_long_splits(label, ov):
+    w = _w(NB=2, P=1000, p_lo=300, **ov)
+    t = gpu_inputs(w, 41 + len(label))
+    for kv_chunk in (1024, 320):
+        _check(t, w, f"long {label} chunk={kv_chunk}", impl=sd.IMPL_MFMA, kv_chunk=kv_chunk)
+
+
 @pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
 @pytest.mark.parametrize("kv_chunk", [64, 128, 192])
 def test_bf16_forced_splits(kv_chunk, impl):
