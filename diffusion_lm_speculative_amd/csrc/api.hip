@@ -107,8 +107,10 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   pl.chunk = static_cast<int>(chunk);
   pl.nsplit = static_cast<int>(nsplit);
   const int64_t grid = nsplit * pl.nrg * static_cast<int64_t>(pl.NB) * pl.Hkv;
-  pl.rg_xcd = pl.impl == SIMSD_IMPL_MFMA && pl.nrg > 1 && (grid / pl.nrg) % 8 == 0;
   if (grid > 0x7fffffffLL) return SIMSD_ERR_SHAPE;
+  // the MFMA kernel's grid is (nsplit, Hkv, NB * nrg): y and z stay below 2^16
+  if (pl.impl == SIMSD_IMPL_MFMA && (pl.Hkv > 65535 || static_cast<int64_t>(pl.NB) * pl.nrg > 65535))
+    return SIMSD_ERR_SHAPE;
   if (pl.nsplit > 1) {
     pl.part_o_floats = static_cast<size_t>(pl.NB) * pl.Hkv * pl.nsplit * pl.M * pl.d;
     pl.part_ml_floats = static_cast<size_t>(pl.NB) * pl.Hkv * pl.nsplit * pl.M * 2;

@@ -138,7 +138,6 @@ struct Plan {
   double rope_base;
   double log2_base;                   // log2(rope_base)
   int qsep;                           // MFMA: query rows staged in their own LDS region
-  int rg_xcd;                         // MFMA: row groups of a K/V stream placed on one XCD
   float scale_log2;                   // softmax scale * log2(e)
   size_t part_o_floats, part_ml_floats;
 };

@@ -237,23 +237,18 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const int rw = wave % RW;  // row wave: rows rw*16 .. +15 of the row group
   const int ks = wave / RW;  // key split: keys [ks*64/KSPLIT, (ks+1)*64/KSPLIT) of every tile
 
-  // Workgroup -> (split, row group, KV head, sequence).  Consecutive
-  // workgroups go to different XCDs (blockIdx mod 8); with several row groups
-  // the row groups of one K/V stream share an XCD and run back to back, so
-  // the later ones find its tiles in that XCD's L2.
-  int idx = blockIdx.x, rg = 0;
-  if (pl.nrg > 1 && pl.rg_xcd) {
-    const int y = idx / 8;
-    rg = y % pl.nrg;
-    idx = (y / pl.nrg) * 8 + idx % 8;
-  } else if (pl.nrg > 1) {
-    rg = (idx / pl.nsplit) % pl.nrg;
-    idx = (idx / (pl.nsplit * pl.nrg)) * pl.nsplit + idx % pl.nsplit;
+  // Workgroup -> (split, KV head, sequence and row group) straight from the
+  // 3-D grid (no integer division on the way to the first loads).  The
+  // hardware hands consecutive workgroups (x fastest) to consecutive XCDs, so
+  // with nsplit*Hkv a multiple of 8 the row groups of one K/V stream share an
+  // XCD and the later ones find its tiles in that XCD's L2.
+  const int s = blockIdx.x;
+  const int kvh = blockIdx.y;
+  int b = blockIdx.z, rg = 0;
+  if (pl.nrg > 1) {
+    rg = b % pl.nrg;
+    b /= pl.nrg;
   }
-  const int s = idx % pl.nsplit;
-  idx /= pl.nsplit;
-  const int kvh = idx % pl.Hkv;
-  const int b = idx / pl.Hkv;
 
   const int B = pl.B, twoB = pl.twoB;
   const int32_t* tau_b = a.tau + static_cast<size_t>(b) * B;
@@ -788,8 +783,9 @@ hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = static_cast<int>(lds);
   }
-  const unsigned grid = static_cast<unsigned>(pl.nsplit) * pl.nrg * pl.NB * pl.Hkv;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(RW * KSPLIT * 64), lds, s, pl, a);
+  const dim3 grid(static_cast<unsigned>(pl.nsplit), static_cast<unsigned>(pl.Hkv),
+                  static_cast<unsigned>(pl.NB) * static_cast<unsigned>(pl.nrg));
+  hipLaunchKernelGGL(kern, grid, dim3(RW * KSPLIT * 64), lds, s, pl, a);
   return hipGetLastError();
 }
 
