@@ -350,7 +350,13 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   // assuming the whole cache capacity (always in bounds).
   const int c1s = min(c0 + pl.chunk, pl.p_max);
   const int nts = c1s > c0 ? (c1s - c0 + KT - 1) / KT : 0;
-  const int nspec = min(NPRO, nbt + nts);
+  // Only the first two go out before the query rows and stage labels have
+  // landed: behind a whole ring of tile loads from every workgroup those small
+  // scattered loads land about with its last tile, and the work that needs
+  // them would then leave the memory idle once the rings are full.  The rest
+  // of the ring is issued once they are in.
+  constexpr int kSpecTiles = NPRO < 2 ? NPRO : 2;
+  const int nspec = min(kSpecTiles, nbt + nts);
   issue_range(0, nspec, c1s);
 
   // ---- RoPE table of the B block positions, while the loads are in flight:
@@ -452,9 +458,27 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
                           : make_uint4(0u, 0u, 0u, 0u);
       qop[i] = __builtin_bit_cast(bf16x8, w);
     }
-    if (rok) {
-      uint64_t dbits, mbits;
-      mask_row_bits_at([&](int j) { return tp[j]; }, B, r, pl.mask_mode, dbits, mbits);
+    // Block visibility of the row from the stage labels held in lanes
+    // 0..B-1 (tau_v): the D_j a row sees are those with a stage of at most
+    // lim (its own stage for a data row, one less for a mask slot), i.e. the
+    // ballot of tau_j <= lim; a slot row sees the slots D~_j whose D_j it
+    // does not see.
+    {
+      const uint64_t all = (B >= 64) ? ~0ull : ((1ull << B) - 1ull);
+      const int ti = __shfl(tau_v, r % B);
+      const bool slot_row = r >= B;
+      const int lim = slot_row ? ti - 1 : ti;
+      uint64_t dbits = 0;
+      for (int k = 1; k <= B; ++k) {
+        const uint64_t pk = __ballot(lane < B && tau_v <= k);
+        dbits = (lim == k) ? pk : dbits;
+      }
+      uint64_t mbits = slot_row ? (all & ~dbits) : 0ull;
+      if (pl.mask_mode == SIMSD_MASK_FULL) {
+        dbits = all;
+        mbits = all;
+      }
+      if (!rok) dbits = mbits = 0;
       if (B >= 64) {
         vis_lo = dbits;
         vis_hi = mbits;
