@@ -523,19 +523,29 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // S^T of this wave's keys of the tile in stage ST.
-  auto scores = [&](int st, f32x4 (&sacc)[NSUB]) __attribute__((always_inline)) {
+  // K operands of this wave's keys of the tile in stage ST, all read at once
+  // (their latency is then paid once, behind the softmax of the previous tile).
+  auto kread = [&](int st, bf16x8 (&kop)[NSUB][KSTEPS]) __attribute__((always_inline)) {
     const int sto = st * L::TILEB;
 #pragma unroll
-    for (int i = 0; i < NSUB; ++i) {
-      bf16x8 kop[KSTEPS];
+    for (int i = 0; i < NSUB; ++i)
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk)
-        kop[kk] = *reinterpret_cast<const bf16x8*>(smem + (kofs[kk] + sto) + i * 16 * L::ROWB);
+        kop[i][kk] = *reinterpret_cast<const bf16x8*>(smem + (kofs[kk] + sto) + i * 16 * L::ROWB);
+  };
+  auto kmma = [&](const bf16x8 (&kop)[NSUB][KSTEPS], f32x4 (&sacc)[NSUB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) {
       f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) sa = mfma(kop[kk], qop[kk], sa);
+      for (int kk = 0; kk < KSTEPS; ++kk) sa = mfma(kop[i][kk], qop[kk], sa);
       sacc[i] = sa;
     }
+  };
+  auto scores = [&](int st, f32x4 (&sacc)[NSUB]) __attribute__((always_inline)) {
+    bf16x8 kop[NSUB][KSTEPS];
+    kread(st, kop);
+    kmma(kop, sacc);
   };
 
   // V^T operands of the tile in stage ST (the reads complete during the softmax).
@@ -677,9 +687,10 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       }
       if (t + 1 < nbt) rotate_block(K1, t + 1);
     }
+    bf16x8 kop[NSUB][KSTEPS];
+    if (t + 1 < T) kread(K1, kop);
     bf16x8 vop[DTILES][NU];
     vread(K, vop);
-    if (t + 1 < T) scores(K1, sb[1 - P]);
     if (decltype(mode_c)::value == 0) {
       finish(IC<0>{}, sb[P], vop, 0ull);
     } else {
@@ -687,6 +698,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       const uint64_t cm = t < nbt ? (t == 0 ? vis_lo : vis_hi) : (nk >= KT ? ~0ull : (1ull << nk) - 1ull);
       finish(IC<1>{}, sb[P], vop, cm);
     }
+    if (t + 1 < T) kmma(kop, sb[1 - P]);
   };
   // block tiles, then whole prompt tiles two at a time (the score buffers are
   // constants), then the rest through the masked path
