@@ -1,18 +1,28 @@
 // Debug exports: the tau mask rows and the RoPE-copy rotation of the block
 // rows, produced by the same device functions the attention kernels use
-// (mask_row_bits, rope_cos_sin, rope_apply), so tests can compare them with
+// (mask_row_bits_wave / mask_row_bits, rope_cos_sin, rope_apply), so tests can compare them with
 // the oracle bit for bit.
 #include "simsd_common.hpp"
 
 namespace simsd {
 namespace {
 
+// One workgroup of 128 threads per sequence, thread r = block row r.  The
+// rows come from the wave-ballot form the MFMA kernel uses; the per-thread
+// form (the VALU kernel's) must agree, else the row reads all ones in both
+// words, which no valid mask has.
 __global__ void debug_mask_kernel(const int32_t* tau, int B, int mode, uint64_t* bits) {
   const int b = blockIdx.x;
   const int r = threadIdx.x;
+  const int lane = r & 63;
+  if (B < 1 || B > 64) return;  // uniform over the workgroup
+  const int32_t* tau_b = tau + static_cast<size_t>(b) * B;
+  const int tau_lane = lane < B ? tau_b[lane] : 0;
+  uint64_t d, m, d1, m1;
+  mask_row_bits_wave(tau_lane, lane, B, r % (2 * B), mode, d, m);
   if (r >= 2 * B) return;
-  uint64_t d, m;
-  mask_row_bits(tau + static_cast<size_t>(b) * B, B, r, mode, d, m);
+  mask_row_bits(tau_b, B, r, mode, d1, m1);
+  if (d != d1 || m != m1) d = m = ~0ull;
   uint64_t* o = bits + (static_cast<size_t>(b) * 2 * B + r) * 2;
   o[0] = d;
   o[1] = m;

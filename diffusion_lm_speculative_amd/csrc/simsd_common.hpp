@@ -63,6 +63,30 @@ __device__ __forceinline__ void mask_row_bits_at(TauAt tau_at, int B, int r, int
   mbits = slot_row ? (all & ~dbits) : 0ull;
 }
 
+// The same bits from a wave's view of the stage labels: lanes 0..B-1 hold
+// tau_j in `tau_lane` (1 <= B <= 64), and every lane of the wave calls this
+// (wave ballots).  The D_j row r sees are those with a stage of at most lim,
+// the ballot of tau_j <= lim for the lim of the row; a slot row sees the
+// slots D~_j whose D_j it does not see.
+__device__ __forceinline__ void mask_row_bits_wave(int tau_lane, int lane, int B, int r, int mode, uint64_t& dbits,
+                                                   uint64_t& mbits) {
+  const uint64_t all = (B >= 64) ? ~0ull : ((1ull << B) - 1ull);
+  const int ti = __shfl(tau_lane, r % B);
+  const bool slot_row = r >= B;
+  const int lim = slot_row ? ti - 1 : ti;
+  uint64_t d = 0;
+  for (int k = 1; k <= B; ++k) {
+    const uint64_t pk = __ballot(lane < B && tau_lane <= k);
+    d = (lim == k) ? pk : d;
+  }
+  dbits = d;
+  mbits = slot_row ? (all & ~d) : 0ull;
+  if (mode == SIMSD_MASK_FULL) {
+    dbits = all;
+    mbits = all;
+  }
+}
+
 __device__ __forceinline__ void mask_row_bits(const int32_t* tau, int B, int r, int mode, uint64_t& dbits,
                                               uint64_t& mbits) {
   mask_row_bits_at([tau](int j) { return tau[j]; }, B, r, mode, dbits, mbits);

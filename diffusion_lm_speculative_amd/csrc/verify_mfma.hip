@@ -458,26 +458,10 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
                           : make_uint4(0u, 0u, 0u, 0u);
       qop[i] = __builtin_bit_cast(bf16x8, w);
     }
-    // Block visibility of the row from the stage labels held in lanes
-    // 0..B-1 (tau_v): the D_j a row sees are those with a stage of at most
-    // lim (its own stage for a data row, one less for a mask slot), i.e. the
-    // ballot of tau_j <= lim; a slot row sees the slots D~_j whose D_j it
-    // does not see.
+    // block visibility of the row from the stage labels held in lanes 0..B-1
     {
-      const uint64_t all = (B >= 64) ? ~0ull : ((1ull << B) - 1ull);
-      const int ti = __shfl(tau_v, r % B);
-      const bool slot_row = r >= B;
-      const int lim = slot_row ? ti - 1 : ti;
-      uint64_t dbits = 0;
-      for (int k = 1; k <= B; ++k) {
-        const uint64_t pk = __ballot(lane < B && tau_v <= k);
-        dbits = (lim == k) ? pk : dbits;
-      }
-      uint64_t mbits = slot_row ? (all & ~dbits) : 0ull;
-      if (pl.mask_mode == SIMSD_MASK_FULL) {
-        dbits = all;
-        mbits = all;
-      }
+      uint64_t dbits, mbits;
+      mask_row_bits_wave(tau_v, lane, B, r, pl.mask_mode, dbits, mbits);
       if (!rok) dbits = mbits = 0;
       if (B >= 64) {
         vis_lo = dbits;
