@@ -50,17 +50,18 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   pl.impl = d.impl == SIMSD_IMPL_AUTO ? (d.dtype == SIMSD_BF16 ? SIMSD_IMPL_MFMA : SIMSD_IMPL_VALU) : d.impl;
 
   if (pl.impl == SIMSD_IMPL_MFMA) {
-    // Row waves of 16 rows each, up to 8 (128 rows; more rows take more row
-    // groups, which read the same K/V split on one XCD at about the same
-    // time).  With fewer than 8 row waves each tile's keys are split over 2
-    // or 4 waves so that every workgroup runs 4 to 8 waves.
+    // 16-row tiles per workgroup: 1, 2 or 4 (one per row wave), or 8 (four
+    // row waves of two tiles each); each tile's keys are split over 4 or 2
+    // waves, so a workgroup runs 4 to 8 waves.  More rows take more row
+    // groups, which read the same K/V split on one XCD at about the same time.
     const int tiles = (pl.M + 15) / 16;
-    int rw = 1;
-    while (rw < tiles && rw < 8) rw *= 2;
-    pl.ksplit = rw >= 8 ? 1 : (rw == 4 ? 2 : 4);
-    pl.rowt = 1;
+    int nt16 = 1;
+    while (nt16 < tiles && nt16 < 8) nt16 *= 2;
+    const int rw = nt16 >= 8 ? 4 : nt16;
+    pl.rowt = nt16 >= 8 ? 2 : 1;
+    pl.ksplit = rw >= 4 ? 2 : 4;
     pl.threads = rw * pl.ksplit * 64;
-    pl.rows_wg = rw * 16;
+    pl.rows_wg = nt16 * 16;
     // Four ring stages with the query rows staged in their own LDS region
     // when that fits; else the query rows borrow the last stage during the
     // prologue; else three stages.

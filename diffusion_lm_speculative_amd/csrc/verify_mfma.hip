@@ -194,11 +194,12 @@ struct Smem {
   }
 };
 
-template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP>
+template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT>
 __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, VerifyArgs a) {
   using L = Layout<HD>;
   using S = Smem<HD, NSTAGE, QSEP>;
   constexpr int NW = RW * KSPLIT;                // waves: RW row waves x KSPLIT key splits
+  constexpr int ROWS = RW * ROWT * 16;           // rows of a workgroup: ROWT 16-row tiles per row wave
   constexpr int NT = NW * 64;
   constexpr int HALF = HD / 2;
   constexpr int KSTEPS = HD / 32;                // k-steps of S^T = K Q^T
@@ -208,17 +209,18 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   constexpr int LPW = 2 * L::IPT / NW;           // direct-to-LDS loads per wave per tile
   constexpr int KREG = S::KREG;
   constexpr int VREG = S::VREG;
-  constexpr int TABREG = S::tab(RW * 16);
+  constexpr int TABREG = S::tab(ROWS);
   constexpr int NPRO = QSEP ? NSTAGE : NSTAGE - 1;  // ring tiles issued before the query rows are read
-  constexpr int QI = RW * 16 / L::RPI;           // 1 KiB loads of the workgroup's query rows
+  constexpr int QI = ROWS / L::RPI;              // 1 KiB loads of the workgroup's query rows
   constexpr int XSTR = HD + 4;                   // floats per row of the key-split exchange buffer
   static_assert(KSPLIT == 1 || KSPLIT == 2 || KSPLIT == 4, "key split");
   static_assert(NSTAGE == 3 || NSTAGE == 4, "the pipeline keeps two tiles resident; at most 4 stages");
   static_assert(LPW * NW == 2 * L::IPT, "tile loads must split evenly over waves");
   static_assert(NSTAGE * LPW <= 63, "too many loads in flight for vmcnt");
   static_assert((NSTAGE - 1) * L::TILEB < 65536, "stage offsets must fit the LDS immediate");
-  static_assert(QSEP || RW * 16 <= 2 * KT, "query rows must fit the last stage");
-  static_assert((KSPLIT - 1) * RW * 16 * XSTR * 4 <= 2 * NSTAGE * L::TILEB, "exchange buffer fits the ring");
+  static_assert(QSEP || ROWS <= 2 * KT, "query rows must fit the last stage");
+  static_assert(ROWT == 1 || ROWT == 2, "row tiles per wave");
+  static_assert((KSPLIT - 1) * ROWS * XSTR * 4 <= 2 * NSTAGE * L::TILEB, "exchange buffer fits the ring");
   static_assert(NT % HALF == 0, "each lane keeps one RoPE frequency");
   // Probabilities are taken relative to a per-row reference fixed at the
   // row's first tile with a visible key (no rescaling of the accumulators
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int rw = wave % RW;  // row wave: rows rw*16 .. +15 of the row group
+  const int rw = wave % RW;  // row wave: rows (rw*ROWT + rt)*16 .. +15 of the row group, rt < ROWT
   const int ks = wave / RW;  // key split: keys [ks*64/KSPLIT, (ks+1)*64/KSPLIT) of every tile
 
   // Workgroup -> (split, KV head, sequence and row group) straight from the
@@ -254,10 +256,13 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const int32_t* tau_b = a.tau + static_cast<size_t>(b) * B;
   const int32_t* pos_b = a.pos_d ? a.pos_d + static_cast<size_t>(b) * B : nullptr;
 
-  const int m = rg * pl.rows_wg + rw * 16 + n;
-  const bool rok = m < pl.M;
-  const int hh = m / twoB, r = m % twoB;
-  const size_t rout = (static_cast<size_t>(b) * twoB + r) * pl.Hq + kvh * pl.G + hh;
+  // this lane's query row in row tile rt of the wave (m < M: a real row;
+  // r: its block row; its output row index), recomputed where needed rather
+  // than held in registers through the loop
+  auto row_m = [&](int rt) { return rg * pl.rows_wg + (rw * ROWT + rt) * 16 + n; };
+  auto row_out = [&](int mm) {
+    return (static_cast<size_t>(b) * twoB + mm % twoB) * pl.Hq + kvh * pl.G + mm / twoB;
+  };
   const int c0 = s * pl.chunk;
   const bool has_block = (s == 0);
   const int nbt = has_block ? (twoB + KT - 1) / KT : 0;  // block tiles, streamed after the prompt tiles
@@ -405,11 +410,16 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   if (st || T == 0) {
     wait_counts<0, 15>();  // drain the ring loads before the workgroup's LDS is released
     if (status_writer) a.status[b] = st;
-    if (st && pl.nsplit == 1 && rok && ks == 0) {
-      uint16_t* op = static_cast<uint16_t*>(a.out) + rout * HD;
+    if (st && pl.nsplit == 1 && ks == 0) {
 #pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt) *reinterpret_cast<uint2*>(op + 16 * dt + 4 * g) = make_uint2(0u, 0u);
-      if (a.lse && g == 0) a.lse[rout] = -INFINITY;
+      for (int rt = 0; rt < ROWT; ++rt) {
+        const int mm = row_m(rt);
+        if (mm >= pl.M) continue;
+        uint16_t* op = static_cast<uint16_t*>(a.out) + row_out(mm) * HD;
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) *reinterpret_cast<uint2*>(op + 16 * dt + 4 * g) = make_uint2(0u, 0u);
+        if (a.lse && g == 0) a.lse[row_out(mm)] = -INFINITY;
+      }
     }
     return;
   }
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   issue_range(issued, min(NPRO, T), c1);
 
   // ---- rotate the staged query rows in place (one granule pair per item)
-  for (int it = tid; it < RW * 16 * (L::GR / 2); it += NT) {
+  for (int it = tid; it < ROWS * (L::GR / 2); it += NT) {
     const int lr = it / (L::GR / 2), j = it % (L::GR / 2);
     const int mq = rg * pl.rows_wg + lr;
     if (mq >= pl.M) continue;
@@ -446,32 +456,30 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   }
   lds_barrier<63>();
 
-  // ---- Q operand and block visibility of this lane's row
-  bf16x8 qop[KSTEPS];
-  uint64_t vis_lo = 0, vis_hi = 0;
-  {
-    const int lr = rw * 16 + n;
+  // ---- Q operands of this lane's rows
+  bf16x8 qop[ROWT][KSTEPS];
+#pragma unroll
+  for (int rt = 0; rt < ROWT; ++rt) {
+    const int lr = (rw * ROWT + rt) * 16 + n;
+    const bool rok = row_m(rt) < pl.M;
     const unsigned char* qrow = smem + S::qrow(lr);
 #pragma unroll
     for (int i = 0; i < KSTEPS; ++i) {
       const uint4 w = rok ? *reinterpret_cast<const uint4*>(qrow + (((4 * i + g) ^ (lr & (L::GR - 1))) << 4))
                           : make_uint4(0u, 0u, 0u, 0u);
-      qop[i] = __builtin_bit_cast(bf16x8, w);
-    }
-    // block visibility of the row from the stage labels held in lanes 0..B-1
-    {
-      uint64_t dbits, mbits;
-      mask_row_bits_wave(tau_v, lane, B, r, pl.mask_mode, dbits, mbits);
-      if (!rok) dbits = mbits = 0;
-      if (B >= 64) {
-        vis_lo = dbits;
-        vis_hi = mbits;
-      } else {
-        vis_lo = dbits | (mbits << B);
-        vis_hi = mbits >> (64 - B);
-      }
+      qop[rt][i] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  // Block visibility of row tile rt's row in block tile bt (bit k: key k of
+  // the tile), from the stage labels held in lanes 0..B-1 (wave ballots).
+  auto block_vis = [&](int rt, int bt) -> uint64_t {
+    const int mm = row_m(rt);
+    uint64_t dbits, mbits;
+    mask_row_bits_wave(tau_v, lane, B, mm % twoB, pl.mask_mode, dbits, mbits);
+    if (mm >= pl.M) return 0ull;
+    if (B >= 64) return bt == 0 ? dbits : mbits;
+    return bt == 0 ? (dbits | (mbits << B)) : (mbits >> (64 - B));
+  };
   if (!QSEP) {
     lds_barrier<63>();  // every wave holds its query rows: the last stage is free
     if (NSTAGE - 1 < T) issue(NSTAGE - 1, NSTAGE - 1, c1);
@@ -498,15 +506,20 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       vadr[dt] = vbase + swz<HD>(32 * ((ks * NSUB) / 2) + vr, 2 * dt + (vc4 >> 1)) + (vc4 & 1) * 8;
   }
 
-  // ---- online-softmax state of this wave's share of the keys
-  float mref = -INFINITY, lpart = 0.0f;  // reference (log2 units, -inf until set), partial sum
-  float lmax = -INFINITY;                 // this lane's largest raw score so far
+  // ---- online-softmax state of this wave's share of the keys, per row tile
+  float mref[ROWT], lpart[ROWT];  // reference (log2 units, -inf until set), partial sum
+  float lmax[ROWT];               // this lane's largest raw score so far
   const float scale = pl.scale_log2;
-  f32x4 acc[DTILES];
+  f32x4 acc[ROWT][DTILES];
 #pragma unroll
-  for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int rt = 0; rt < ROWT; ++rt) {
+    mref[rt] = -INFINITY;
+    lpart[rt] = 0.0f;
+    lmax[rt] = -INFINITY;
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) acc[rt][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
-  // S^T of this wave's keys of the tile in stage ST.
   // K operands of this wave's keys of the tile in stage ST, all read at once
   // (their latency is then paid once, behind the softmax of the previous tile).
   auto kread = [&](int st, bf16x8 (&kop)[NSUB][KSTEPS]) __attribute__((always_inline)) {
@@ -517,16 +530,22 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       for (int kk = 0; kk < KSTEPS; ++kk)
         kop[i][kk] = *reinterpret_cast<const bf16x8*>(smem + (kofs[kk] + sto) + i * 16 * L::ROWB);
   };
-  auto kmma = [&](const bf16x8 (&kop)[NSUB][KSTEPS], f32x4 (&sacc)[NSUB]) __attribute__((always_inline)) {
+  // S^T of those keys for every row tile (each K operand feeds ROWT MFMAs).
+  auto kmma = [&](const bf16x8 (&kop)[NSUB][KSTEPS], f32x4 (&sacc)[ROWT][NSUB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
-      f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 sa[ROWT];
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) sa = mfma(kop[i][kk], qop[kk], sa);
-      sacc[i] = sa;
+      for (int rt = 0; rt < ROWT; ++rt) sa[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+        for (int rt = 0; rt < ROWT; ++rt) sa[rt] = mfma(kop[i][kk], qop[rt][kk], sa[rt]);
+#pragma unroll
+      for (int rt = 0; rt < ROWT; ++rt) sacc[rt][i] = sa[rt];
     }
   };
-  auto scores = [&](int st, f32x4 (&sacc)[NSUB]) __attribute__((always_inline)) {
+  auto scores = [&](int st, f32x4 (&sacc)[ROWT][NSUB]) __attribute__((always_inline)) {
     bf16x8 kop[NSUB][KSTEPS];
     kread(st, kop);
     kmma(kop, sacc);
@@ -575,69 +594,76 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     lds_barrier<63>();
   };
 
-  // Softmax of the scores and O^T += V^T P^T.  MODE 0: every key visible;
-  // MODE 1: key k of the tile visible when bit k of cmask is set.
-  auto finish = [&](auto mode_c, const f32x4 (&sacc)[NSUB], const bf16x8 (&vop)[DTILES][NU], uint64_t cmask)
-                    __attribute__((always_inline)) {
+  // Softmax of the scores and O^T += V^T P^T, for every row tile (each V^T
+  // operand feeds ROWT MFMAs).  MODE 0: every key visible; MODE 1: key k of
+  // the tile visible for row tile rt when bit k of cmask[rt] is set.
+  auto finish = [&](auto mode_c, const f32x4 (&sacc)[ROWT][NSUB], const bf16x8 (&vop)[DTILES][NU],
+                    const uint64_t (&cmask)[ROWT]) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_c)::value;
-    float sv[NSUB][4];
-    float tmax = -INFINITY;
-    // this lane's keys are 16*(ks*NSUB + i) + 4g + j: one variable shift, then constant bit tests
-    const uint64_t cm = MODE == 0 ? 0ull : cmask >> (16 * ks * NSUB + 4 * g);
+    bf16x8 pop[ROWT][NU];
 #pragma unroll
-    for (int i = 0; i < NSUB; ++i) {
+    for (int rt = 0; rt < ROWT; ++rt) {
+      float sv[NSUB][4];
+      float tmax = -INFINITY;
+      // this lane's keys are 16*(ks*NSUB + i) + 4g + j: one variable shift, then constant bit tests
+      const uint64_t cm = MODE == 0 ? 0ull : cmask[rt] >> (16 * ks * NSUB + 4 * g);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool vis = MODE == 0 || ((cm >> (16 * i + j)) & 1ull);
-        const float x = vis ? sacc[i][j] : -INFINITY;  // raw score; the scale is applied below
-        sv[i][j] = x;
-        tmax = fmaxf(tmax, x);
+      for (int i = 0; i < NSUB; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool vis = MODE == 0 || ((cm >> (16 * i + j)) & 1ull);
+          const float x = vis ? sacc[rt][i][j] : -INFINITY;  // raw score; the scale is applied below
+          sv[i][j] = x;
+          tmax = fmaxf(tmax, x);
+        }
       }
-    }
-    lmax = fmaxf(lmax, tmax);
-    if (__any(mref == -INFINITY)) {  // first tile with a visible key for some row of this wave
-      float rmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-      if (mref == -INFINITY) mref = rmax * scale;  // stays -inf while the row sees nothing
-    }
-    const float muse = (mref == -INFINITY) ? 0.0f : mref;
-    float pv[NSUB][4];
-    float lsum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NSUB; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pv[i][j] = __builtin_amdgcn_exp2f(fmaf(sv[i][j], scale, -muse));
-        lsum += pv[i][j];
+      lmax[rt] = fmaxf(lmax[rt], tmax);
+      if (__any(mref[rt] == -INFINITY)) {  // first tile with a visible key for some row of this wave
+        float rmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+        if (mref[rt] == -INFINITY) mref[rt] = rmax * scale;  // stays -inf while the row sees nothing
       }
-    lpart += lsum;
-    // P^T operand of k-step u: keys 4g..4g+3 of subtile 2u, then of 2u+1;
-    // subtiles of other waves contribute zeros.
-    bf16x8 pop[NU];
+      const float muse = (mref[rt] == -INFINITY) ? 0.0f : mref[rt];
+      float pv[NSUB][4];
+      float lsum = 0.0f;
 #pragma unroll
-    for (int uu = 0; uu < NU; ++uu) {
-      const int u = (ks * NSUB) / 2 + uu;
-      __bf16 pb[8];
+      for (int i = 0; i < NSUB; ++i)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int i = 2 * u + h2 - ks * NSUB;
-        const int ic = i < 0 ? 0 : (i >= NSUB ? NSUB - 1 : i);
+        for (int j = 0; j < 4; ++j) {
+          pv[i][j] = __builtin_amdgcn_exp2f(fmaf(sv[i][j], scale, -muse));
+          lsum += pv[i][j];
+        }
+      lpart[rt] += lsum;
+      // P^T operand of k-step u: keys 4g..4g+3 of subtile 2u, then of 2u+1;
+      // subtiles of other waves contribute zeros.
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pb[4 * h2 + j] = static_cast<__bf16>((i >= 0 && i < NSUB) ? pv[ic][j] : 0.0f);
+      for (int uu = 0; uu < NU; ++uu) {
+        const int u = (ks * NSUB) / 2 + uu;
+        __bf16 pb[8];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int i = 2 * u + h2 - ks * NSUB;
+          const int ic = i < 0 ? 0 : (i >= NSUB ? NSUB - 1 : i);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pb[4 * h2 + j] = static_cast<__bf16>((i >= 0 && i < NSUB) ? pv[ic][j] : 0.0f);
+        }
+        pop[rt][uu] = bf16x8{pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
       }
-      pop[uu] = bf16x8{pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
     }
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt)
 #pragma unroll
-      for (int uu = 0; uu < NU; ++uu) acc[dt] = mfma(vop[dt][uu], pop[uu], acc[dt]);
+      for (int uu = 0; uu < NU; ++uu)
+#pragma unroll
+        for (int rt = 0; rt < ROWT; ++rt) acc[rt][dt] = mfma(vop[dt][uu], pop[rt][uu], acc[rt][dt]);
   };
 
   // ---- the T = ntiles + nbt tiles, software-pipelined over the ring.
   //      Before step t: tiles 0 .. min(t + NSTAGE - 2, T - 1) are issued
   //      (0 .. min(NSTAGE, T) - 1 for t = 0), in tile order.
-  // Score buffer of tile t: sb[(t - nbt) % 2].
-  f32x4 sb[2][NSUB];
+  // Scores of the next tile: the softmax of tile t reads them before the
+  // score MFMAs of tile t+1 overwrite them, so one buffer serves.
+  f32x4 sb[ROWT][NSUB];
   int* pass_flag = reinterpret_cast<int*>(smem + S::TPREG + 512 - 4);  // after the positions
   const int nfull = (c1 - c0) / KT;  // whole prompt tiles: nbt .. nbt + nfull - 1
   for (int pass = 0;; ++pass) {
@@ -646,12 +672,8 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   else
     lds_barrier<0>();
   if (nbt > 0) rotate_block(0, 0);
-  if (nbt & 1)
-    scores(0, sb[1]);
-  else
-    scores(0, sb[0]);
-  auto step = [&](auto p_c, auto mode_c, int t) __attribute__((always_inline)) {
-    constexpr int P = decltype(p_c)::value;  // (t - nbt) % 2
+  scores(0, sb);
+  auto step = [&](auto mode_c, int t) __attribute__((always_inline)) {
     const int K = t % NSTAGE;                // stage of tile t
     const int K1 = K + 1 == NSTAGE ? 0 : K + 1;
     if (t + 1 < T) {
@@ -671,48 +693,55 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       }
       if (t + 1 < nbt) rotate_block(K1, t + 1);
     }
+    // One row tile: the K reads of tile t+1 go out first and land behind
+    // the softmax.  Two row tiles: the registers for both do not fit beside
+    // the softmax, so they go out after it and land behind the PV MFMAs.
     bf16x8 kop[NSUB][KSTEPS];
-    if (t + 1 < T) kread(K1, kop);
+    if (ROWT == 1 && t + 1 < T) kread(K1, kop);
     bf16x8 vop[DTILES][NU];
     vread(K, vop);
     if (decltype(mode_c)::value == 0) {
-      finish(IC<0>{}, sb[P], vop, 0ull);
+      const uint64_t cm[ROWT] = {};
+      finish(IC<0>{}, sb, vop, cm);
     } else {
       const int nk = c1 - (c0 + (t - nbt) * KT);  // keys of a prompt tile below c1
-      const uint64_t cm = t < nbt ? (t == 0 ? vis_lo : vis_hi) : (nk >= KT ? ~0ull : (1ull << nk) - 1ull);
-      finish(IC<1>{}, sb[P], vop, cm);
+      const uint64_t tail = nk >= KT ? ~0ull : (1ull << nk) - 1ull;
+      uint64_t cm[ROWT];
+#pragma unroll
+      for (int rt = 0; rt < ROWT; ++rt) cm[rt] = t < nbt ? block_vis(rt, t) : tail;
+      finish(IC<1>{}, sb, vop, cm);
     }
-    if (t + 1 < T) kmma(kop, sb[1 - P]);
+    if (ROWT > 1 && t + 1 < T) kread(K1, kop);
+    if (t + 1 < T) kmma(kop, sb);
   };
-  // block tiles, then whole prompt tiles two at a time (the score buffers are
-  // constants), then the rest through the masked path
+  // block tiles, then whole prompt tiles, then the rest through the masked
+  // path
   if (nbt == 1) {
-    step(IC<1>{}, IC<1>{}, 0);
+    step(IC<1>{}, 0);
   } else if (nbt == 2) {
-    step(IC<0>{}, IC<1>{}, 0);
-    step(IC<1>{}, IC<1>{}, 1);
+    step(IC<1>{}, 0);
+    step(IC<1>{}, 1);
   }
   int t0 = nbt;
-  for (; t0 + 2 <= nbt + nfull; t0 += 2) {
-    step(IC<0>{}, IC<0>{}, t0);
-    step(IC<1>{}, IC<0>{}, t0 + 1);
-  }
-  for (; t0 < T; t0 += 2) {
-    step(IC<0>{}, IC<1>{}, t0);
-    if (t0 + 1 < T) step(IC<1>{}, IC<1>{}, t0 + 1);
-  }
+  for (; t0 < nbt + nfull; ++t0) step(IC<0>{}, t0);
+  for (; t0 < T; ++t0) step(IC<1>{}, t0);
 
   // ---- a second pass when some row's probabilities may have grown past
   //      2^kRefSlack (or the sums are not finite): the exact row maximum
   //      over this wave's keys becomes the reference
-  float rowmax = fmaxf(lmax, __shfl_xor(lmax, 16));
-  rowmax = fmaxf(rowmax, __shfl_xor(rowmax, 32));
-  bool bad = !(lpart <= 0x1p60f);  // a lane's share; also catches NaN
+  float rowmax[ROWT];
+  bool bad = false;
 #pragma unroll
-  for (int dt = 0; dt < DTILES; ++dt)
+  for (int rt = 0; rt < ROWT; ++rt) {
+    rowmax[rt] = fmaxf(lmax[rt], __shfl_xor(lmax[rt], 16));
+    rowmax[rt] = fmaxf(rowmax[rt], __shfl_xor(rowmax[rt], 32));
+    bad |= !(lpart[rt] <= 0x1p60f);  // a lane's share; also catches NaN
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bad |= !__builtin_isfinite(acc[dt][j]);
-  bad |= mref != -INFINITY && rowmax * scale > mref + kRefSlack;
+    for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bad |= !__builtin_isfinite(acc[rt][dt][j]);
+    bad |= mref[rt] != -INFINITY && rowmax[rt] * scale > mref[rt] + kRefSlack;
+  }
   if (pass > 0) break;
   wait_counts<0, 15>();
   if (tid == 0) *pass_flag = 0;
@@ -720,82 +749,99 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   if (__any(bad) && lane == 0) *pass_flag = 1;
   lds_barrier<0>();
   if (*pass_flag == 0) break;
-  mref = rowmax == -INFINITY ? -INFINITY : rowmax * scale;
-  lpart = 0.0f;
 #pragma unroll
-  for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int rt = 0; rt < ROWT; ++rt) {
+    mref[rt] = rowmax[rt] == -INFINITY ? -INFINITY : rowmax[rt] * scale;
+    lpart[rt] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) acc[rt][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
   issue_range(0, min(NSTAGE, T), c1);
   }
 
   // ---- combine the key splits of each row (through the drained ring)
   wait_counts<0, 15>();  // no ring load may land after the workgroup ends
   if (status_writer) a.status[b] = 0;
-  float l = lpart;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (KSPLIT > 1) {
+  float l[ROWT];
+#pragma unroll
+  for (int rt = 0; rt < ROWT; ++rt) {
+    l[rt] = lpart[rt];
+    l[rt] += __shfl_xor(l[rt], 16);
+    l[rt] += __shfl_xor(l[rt], 32);
+  }
+  if constexpr (KSPLIT > 1) {
     float* xb = reinterpret_cast<float*>(smem);
     lds_barrier<0>();  // every wave is done reading the ring
     if (ks > 0) {
-      float* xr = xb + (((ks - 1) * RW + rw) * 16 + n) * XSTR;
 #pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt)
-        *reinterpret_cast<float4*>(xr + 16 * dt + 4 * g) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-      if (g == 0) {
-        xr[HD] = mref;
-        xr[HD + 1] = l;
+      for (int rt = 0; rt < ROWT; ++rt) {
+        float* xr = xb + ((((ks - 1) * RW + rw) * ROWT + rt) * 16 + n) * XSTR;
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt)
+          *reinterpret_cast<float4*>(xr + 16 * dt + 4 * g) =
+              make_float4(acc[rt][dt][0], acc[rt][dt][1], acc[rt][dt][2], acc[rt][dt][3]);
+        if (g == 0) {
+          xr[HD] = mref[rt];
+          xr[HD + 1] = l[rt];
+        }
       }
     }
     lds_barrier<0>();
     if (ks > 0) return;
 #pragma unroll
-    for (int k2 = 1; k2 < KSPLIT; ++k2) {
-      const float* xr = xb + (((k2 - 1) * RW + rw) * 16 + n) * XSTR;
-      const float m2 = xr[HD], l2 = xr[HD + 1];
-      const float mnew = fmaxf(mref, m2);
-      const float a1 = (mref == mnew) ? 1.0f : exp2f(mref - mnew);
-      const float a2 = (m2 == mnew) ? 1.0f : exp2f(m2 - mnew);
-      l = l * a1 + l2 * a2;
+    for (int k2 = 1; k2 < KSPLIT; ++k2)
 #pragma unroll
-      for (int dt = 0; dt < DTILES; ++dt) {
-        const float4 o2 = *reinterpret_cast<const float4*>(xr + 16 * dt + 4 * g);
-        acc[dt] = acc[dt] * a1 + f32x4{o2.x, o2.y, o2.z, o2.w} * a2;
+      for (int rt = 0; rt < ROWT; ++rt) {
+        const float* xr = xb + ((((k2 - 1) * RW + rw) * ROWT + rt) * 16 + n) * XSTR;
+        const float m2 = xr[HD], l2 = xr[HD + 1];
+        const float mnew = fmaxf(mref[rt], m2);
+        const float a1 = (mref[rt] == mnew) ? 1.0f : exp2f(mref[rt] - mnew);
+        const float a2 = (m2 == mnew) ? 1.0f : exp2f(m2 - mnew);
+        l[rt] = l[rt] * a1 + l2 * a2;
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) {
+          const float4 o2 = *reinterpret_cast<const float4*>(xr + 16 * dt + 4 * g);
+          acc[rt][dt] = acc[rt][dt] * a1 + f32x4{o2.x, o2.y, o2.z, o2.w} * a2;
+        }
+        mref[rt] = mnew;
       }
-      mref = mnew;
-    }
   }
 
   // ---- epilogue (key-split 0 waves)
-  if (!rok) return;
-  if (pl.nsplit == 1) {
-    const float inv = 1.0f / l;
-    uint16_t* op = static_cast<uint16_t*>(a.out) + rout * HD;
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) {
-      const f32x4 v = acc[dt];
-      *reinterpret_cast<uint2*>(op + 16 * dt + 4 * g) =
-          make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
-    }
-    if (a.lse && g == 0) a.lse[rout] = (mref + log2f(l)) * kLn2;
-  } else {
-    const size_t slot = (static_cast<size_t>(b) * pl.Hkv + kvh) * pl.nsplit + s;
-    float* po = a.part_o + (slot * pl.M + m) * HD;
+  for (int rt = 0; rt < ROWT; ++rt) {
+    const int mm = row_m(rt);
+    if (mm >= pl.M) continue;
+    if (pl.nsplit == 1) {
+      const float inv = 1.0f / l[rt];
+      uint16_t* op = static_cast<uint16_t*>(a.out) + row_out(mm) * HD;
 #pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) {
-      const f32x4 v = acc[dt];
-      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-    if (g == 0) {
-      a.part_ml[(slot * pl.M + m) * 2 + 0] = mref;
-      a.part_ml[(slot * pl.M + m) * 2 + 1] = l;
+      for (int dt = 0; dt < DTILES; ++dt) {
+        const f32x4 v = acc[rt][dt];
+        *reinterpret_cast<uint2*>(op + 16 * dt + 4 * g) =
+            make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
+      }
+      if (a.lse && g == 0) a.lse[row_out(mm)] = (mref[rt] + log2f(l[rt])) * kLn2;
+    } else {
+      const size_t slot = (static_cast<size_t>(b) * pl.Hkv + kvh) * pl.nsplit + s;
+      float* po = a.part_o + (slot * pl.M + mm) * HD;
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) {
+        const f32x4 v = acc[rt][dt];
+        *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (g == 0) {
+        a.part_ml[(slot * pl.M + mm) * 2 + 0] = mref[rt];
+        a.part_ml[(slot * pl.M + mm) * 2 + 1] = l[rt];
+      }
     }
   }
 }
 
-template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP>
+template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT>
 hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
-  auto kern = verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP>;
-  const size_t lds = mfma_lds_bytes(HD, NSTAGE, pl.B, RW * 16, QSEP);
+  auto kern = verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT>;
+  const size_t lds = mfma_lds_bytes(HD, NSTAGE, pl.B, RW * ROWT * 16, QSEP);
   static int attr_set = 0;  // largest dynamic LDS size already allowed for this instantiation
   if (static_cast<int>(lds) > attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -809,13 +855,18 @@ hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Rows per workgroup -> (row waves, key splits, row tiles per wave): up to 64
+// rows one 16-row tile per wave with the keys split over 4 or 2 waves; 128
+// rows four row waves of two row tiles each, keys split over 2 waves, so
+// every K and V operand read from LDS feeds two MFMAs.
 template <int HD, int NSTAGE, bool QSEP>
 hipError_t launch_stages(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
   switch (pl.rows_wg / 16) {
-    case 1: return launch_cfg<HD, 1, 4, NSTAGE, QSEP>(pl, a, s);
-    case 2: return launch_cfg<HD, 2, 4, NSTAGE, QSEP>(pl, a, s);
-    case 4: return launch_cfg<HD, 4, 2, NSTAGE, QSEP>(pl, a, s);
-    default: return launch_cfg<HD, 8, 1, NSTAGE, QSEP>(pl, a, s);
+    case 1: return launch_cfg<HD, 1, 4, NSTAGE, QSEP, 1>(pl, a, s);
+    case 2: return launch_cfg<HD, 2, 4, NSTAGE, QSEP, 1>(pl, a, s);
+    case 4: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 1>(pl, a, s);
+    case 8: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 2>(pl, a, s);
+    default: return hipErrorInvalidConfiguration;
   }
 }
 
