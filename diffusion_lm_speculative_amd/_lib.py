@@ -69,6 +69,9 @@ SIGNATURES = {
     "simsd_accept_prefix_workspace": (c_int32, [c_int32, c_int32, c_int64, ctypes.POINTER(c_size_t)]),
     "simsd_accept_prefix": (c_int32, [c_void_p] * 4 + [c_int32, c_int32, c_int32, c_int64, c_uint64, c_uint64]
                             + [c_void_p] * 4 + [c_size_t, c_void_p]),
+    "simsd_accept_coupled_workspace": (c_int32, [c_int32, c_int32, c_int64, ctypes.POINTER(c_size_t)]),
+    "simsd_accept_coupled": (c_int32, [c_void_p] * 4 + [c_int32, c_int32, c_int32, c_int64]
+                             + [c_void_p] * 4 + [c_size_t, c_void_p]),
     "simsd_debug_mask": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "simsd_debug_rope": (c_int32, [ctypes.POINTER(VerifyDesc)] + [c_void_p] * 7),
     "simsd_strerror": (ctypes.c_char_p, [c_int32]),

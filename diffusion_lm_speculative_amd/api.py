@@ -189,6 +189,44 @@ def accept_prefix(p_target, q_draft, draft_tok, tau, gamma, seed, offset=0, *, n
     return n_accepted, next_token, status
 
 
+def accept_coupled_workspace_bytes(batch, B, vocab) -> int:
+    n = ctypes.c_size_t(0)
+    L.check(L.load().simsd_accept_coupled_workspace(int(batch), int(B), int(vocab), ctypes.byref(n)),
+            "simsd_accept_coupled_workspace")
+    return int(n.value)
+
+
+def accept_coupled(p_target, noise_exp, draft_tok, tau, gamma, *, n_accepted=None, next_token=None, status=None,
+                   workspace=None, stream=None, with_next=True, with_status=True):
+    """Coupled-noise acceptance walked in tau order; returns (n_accepted, next_token, status)."""
+    lib = L.load()
+    NB, B, V = p_target.shape
+    dev = p_target.device
+    _need(p_target, "p_target", torch.float32)
+    _need(noise_exp, "noise_exp", torch.float32, (NB, B, V), dev)
+    _need(draft_tok, "draft_tok", torch.int32, (NB, B), dev)
+    _need(tau, "tau", torch.int32, (NB, B), dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((NB,), dtype=torch.int32, device=dev)
+    _need(n_accepted, "n_accepted", torch.int32, (NB,), dev)
+    if next_token is None and with_next:
+        next_token = torch.empty((NB,), dtype=torch.int32, device=dev)
+    if next_token is not None:
+        _need(next_token, "next_token", torch.int32, (NB,), dev)
+    if status is None and with_status:
+        status = torch.empty((NB,), dtype=torch.int32, device=dev)
+    if status is not None:
+        _need(status, "status", torch.int32, (NB,), dev)
+    if workspace is None:
+        workspace = torch.empty(max(accept_coupled_workspace_bytes(NB, B, V), 256), dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    rc = lib.simsd_accept_coupled(_ptr(p_target), _ptr(noise_exp), _ptr(draft_tok), _ptr(tau), NB, B, int(gamma), V,
+                                  _ptr(n_accepted), _ptr(next_token), _ptr(status), _ptr(workspace),
+                                  ctypes.c_size_t(ws_len), _stream_handle(stream))
+    L.check(rc, "simsd_accept_coupled")
+    return n_accepted, next_token, status
+
+
 @dataclass
 class AcceptCall:
     """An accept_prefix call with every pointer bound once (for timing loops);

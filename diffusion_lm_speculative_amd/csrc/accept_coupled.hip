@@ -1,0 +1,193 @@
+// Coupled-noise acceptance: the drafter and the target share one noise table
+// per output position, and a draft is kept exactly when it equals the
+// target's noised argmax at its position (SPOT page, "how to use it"
+// section, Proposition 2 there: given the noise the target's transition is a
+// deterministic argmax, marginalised it samples the target distribution).
+// The walk follows the drafted temporal order and commits the longest kept
+// prefix (SimSD page, section 4; tau is the stage map of its section 2).
+//
+// The noise comes in exponential form, E_v = exp(-g_v) for Gumbel g_v, so
+// the target token of a row is argmax_v p_v / E_v.  Two candidates a, b are
+// compared exactly: p_a * E_b against p_b * E_a, products of two fp32 values
+// and so exact in fp64; equal scores go to the smaller index; entries with
+// p_v <= 0 never win, and a row without one has no target token (-1).
+//
+// Two launches:
+//   1. row argmax, grid (NB * gamma rows, chunks of a row): the workgroup of
+//      stage t of sequence b finds the position k with tau[k] = t, streams
+//      its chunk of p[b][k] and E[b][k] (16-byte loads; the rows are this
+//      call's bytes: 2 * V * 4 per walked stage) and reduces its best
+//      (p, E, index) over lanes and waves with the exact comparison.
+//   2. walk, one wave per sequence: validation (labels 1..B, a permutation,
+//      drafted tokens in range), then stage by stage the reduction of the
+//      row's chunk winners and the compare with the draft.
+#include "simsd_common.hpp"
+
+namespace simsd {
+namespace {
+
+constexpr int kCoThreads = 512;
+constexpr int kCoWaves = kCoThreads / 64;
+constexpr int kCoPerLane = 16;                           // elements per lane per chunk
+constexpr int kCoChunk = kCoThreads * kCoPerLane;        // 8192 elements per workgroup
+
+struct Best {
+  float p, e;
+  int idx;  // -1: no candidate
+};
+
+// true when (p, e, i) beats the current best: larger p/E, else equal and a
+// smaller index
+__device__ __forceinline__ bool better(float p, float e, int i, const Best& b) {
+  if (!(p > 0.0f)) return false;
+  if (b.idx < 0) return true;
+  const double lhs = static_cast<double>(p) * static_cast<double>(b.e);
+  const double rhs = static_cast<double>(b.p) * static_cast<double>(e);
+  return lhs > rhs || (lhs == rhs && i < b.idx);
+}
+
+__device__ __forceinline__ void take(Best& b, float p, float e, int i) {
+  if (better(p, e, i, b)) b = Best{p, e, i};
+}
+
+__device__ __forceinline__ Best wave_best(Best b) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    Best o;
+    o.p = __shfl_xor(b.p, off);
+    o.e = __shfl_xor(b.e, off);
+    o.idx = __shfl_xor(b.idx, off);
+    if (o.idx >= 0) take(b, o.p, o.e, o.idx);
+  }
+  return b;
+}
+
+// Position k of stage t in a wave whose lanes 0..B-1 hold tau; -1 when no
+// label equals t (the walk launch reports the fault).
+__device__ __forceinline__ int stage_position(const int32_t* tau_b, int B, int t) {
+  const int lane = threadIdx.x & 63;
+  const int lab = lane < B ? tau_b[lane] : 0;
+  const uint64_t hit = __ballot(lane < B && lab == t);
+  return hit ? __builtin_ctzll(hit) : -1;
+}
+
+__global__ __launch_bounds__(kCoThreads) void coupled_argmax_kernel(const float* __restrict__ p,
+                                                                     const float* __restrict__ e,
+                                                                     const int32_t* __restrict__ tau, int B,
+                                                                     int gamma, int64_t V, int nch, float4* part) {
+  __shared__ Best sbest[kCoWaves];
+  const int row = blockIdx.x;
+  const int c = blockIdx.y;  // chunk of the row
+  const int b = row / gamma, t = row % gamma + 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = stage_position(tau + static_cast<size_t>(b) * B, B, t);
+  Best best{0.0f, 1.0f, -1};
+  if (k >= 0) {
+    const size_t base = (static_cast<size_t>(b) * B + k) * static_cast<size_t>(V);
+    const float* pr = p + base;
+    const float* er = e + base;
+    const int64_t v0 = static_cast<int64_t>(c) * kCoChunk;
+    const int64_t v1 = min(v0 + kCoChunk, V);
+    if ((V & 3) == 0) {  // rows start 16-byte aligned: 16-byte loads of 4 elements
+      for (int64_t v = v0 + 4 * tid; v < v1; v += 4 * kCoThreads) {
+        const float4 p4 = *reinterpret_cast<const float4*>(pr + v);
+        const float4 e4 = *reinterpret_cast<const float4*>(er + v);
+        const int i = static_cast<int>(v);
+        take(best, p4.x, e4.x, i);
+        take(best, p4.y, e4.y, i + 1);
+        take(best, p4.z, e4.z, i + 2);
+        take(best, p4.w, e4.w, i + 3);
+      }
+    } else {
+      for (int64_t v = v0 + tid; v < v1; v += kCoThreads) take(best, pr[v], er[v], static_cast<int>(v));
+    }
+  }
+  best = wave_best(best);
+  if (lane == 0) sbest[wave] = best;
+  __syncthreads();
+  if (wave == 0) {
+    Best w = lane < kCoWaves ? sbest[lane] : Best{0.0f, 1.0f, -1};
+    w = wave_best(w);
+    if (lane == 0)
+      part[static_cast<size_t>(row) * nch + c] = make_float4(w.p, w.e, __int_as_float(w.idx), 0.0f);
+  }
+}
+
+__global__ __launch_bounds__(64) void coupled_walk_kernel(const int32_t* __restrict__ draft,
+                                                           const int32_t* __restrict__ tau, int B, int gamma,
+                                                           int64_t V, int nch, const float4* __restrict__ part,
+                                                           int32_t* n_out, int32_t* next_out, int32_t* status) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int32_t* tau_b = tau + static_cast<size_t>(b) * B;
+  const int32_t* draft_b = draft + static_cast<size_t>(b) * B;
+  const int lab = lane < B ? tau_b[lane] : 0;
+  const int tok = lane < B ? draft_b[lane] : 0;
+  int st = 0;
+  if (__any(lane < B && (lab < 1 || lab > B))) {
+    st = SIMSD_ST_TAU_RANGE;
+  } else {
+    // a permutation leaves no stage 1..B without a position
+    bool missing = false;
+    for (int t = 1; t <= B; ++t) missing |= __ballot(lane < B && lab == t) == 0ull;
+    if (missing) {
+      st = SIMSD_ST_TAU_NOT_PERM;
+    } else if (__any(lane < B && lab <= gamma && (tok < 0 || static_cast<int64_t>(tok) >= V))) {
+      st = SIMSD_ST_TOKEN_RANGE;
+    }
+  }
+  int n = -1, nxt = -1;
+  if (st == 0) {
+    n = gamma;
+    for (int t = 1; t <= gamma; ++t) {
+      const int row = b * gamma + (t - 1);
+      Best w{0.0f, 1.0f, -1};
+      for (int c = lane; c < nch; c += 64) {
+        const float4 q = part[static_cast<size_t>(row) * nch + c];
+        const int i = __float_as_int(q.z);
+        if (i >= 0) take(w, q.x, q.y, i);
+      }
+      w = wave_best(w);
+      const uint64_t hit = __ballot(lane < B && lab == t);
+      const int k = __builtin_ctzll(hit);
+      const int x = __shfl(tok, k);
+      if (w.idx != x) {
+        n = t - 1;
+        nxt = w.idx;
+        break;
+      }
+    }
+  }
+  if (lane == 0) {
+    n_out[b] = n;
+    if (next_out) next_out[b] = nxt;
+    if (status) status[b] = st;
+  }
+}
+
+}  // namespace
+
+int coupled_chunks(int64_t V) { return static_cast<int>((V + kCoChunk - 1) / kCoChunk); }
+
+size_t coupled_workspace_bytes(int NB, int B, int64_t V) {
+  const size_t n = static_cast<size_t>(NB) * B * coupled_chunks(V) * sizeof(float4);
+  return (n + 255) & ~static_cast<size_t>(255);
+}
+
+hipError_t launch_accept_coupled(const float* p, const float* e, const int32_t* draft, const int32_t* tau, int NB,
+                                 int B, int gamma, int64_t V, int32_t* n_out, int32_t* next_out, int32_t* status,
+                                 void* workspace, hipStream_t s) {
+  const int nch = coupled_chunks(V);
+  float4* part = static_cast<float4*>(workspace);
+  if (gamma > 0) {
+    hipLaunchKernelGGL(coupled_argmax_kernel, dim3(NB * gamma, nch), dim3(kCoThreads), 0, s, p, e, tau, B, gamma,
+                       V, nch, part);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(coupled_walk_kernel, dim3(NB), dim3(64), 0, s, draft, tau, B, gamma, V, nch, part, n_out,
+                     next_out, status);
+  return hipGetLastError();
+}
+
+}  // namespace simsd

@@ -247,6 +247,34 @@ int simsd_accept_prefix(const float* p_target, const float* q_draft, const int32
   return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
 }
 
+int simsd_accept_coupled_workspace(int32_t batch, int32_t B, int64_t vocab, size_t* bytes) {
+  if (!bytes) return SIMSD_ERR_NULL;
+  if (batch < 0 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31)) return SIMSD_ERR_SHAPE;
+  *bytes = coupled_workspace_bytes(batch, B, vocab);
+  return SIMSD_OK;
+}
+
+int simsd_accept_coupled(const float* p_target, const float* noise_exp, const int32_t* draft_tok,
+                         const int32_t* tau, int32_t batch, int32_t B, int32_t gamma, int64_t vocab,
+                         int32_t* n_accepted, int32_t* next_token, int32_t* status, void* workspace,
+                         size_t workspace_bytes_in, void* stream) {
+  if (batch < 0 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31)) return SIMSD_ERR_SHAPE;
+  if (static_cast<int64_t>(batch) * gamma > 0x7fffffff || coupled_chunks(vocab) > 65535) return SIMSD_ERR_SHAPE;
+  if (gamma < 0 || gamma > B) return SIMSD_ERR_GAMMA;
+  if (batch == 0) return SIMSD_OK;
+  if (!n_accepted || (B > 0 && (!p_target || !noise_exp || !draft_tok || !tau))) return SIMSD_ERR_NULL;
+  if (!aligned(n_accepted, 4) || (next_token && !aligned(next_token, 4)) || (status && !aligned(status, 4)) ||
+      (p_target && !aligned(p_target, 16)) || (noise_exp && !aligned(noise_exp, 16)) ||
+      (draft_tok && !aligned(draft_tok, 4)) || (tau && !aligned(tau, 4)))
+    return SIMSD_ERR_ALIGN;
+  const size_t need = coupled_workspace_bytes(batch, B, vocab);
+  if (!workspace || workspace_bytes_in < need) return SIMSD_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return SIMSD_ERR_ALIGN;
+  const hipError_t e = launch_accept_coupled(p_target, noise_exp, draft_tok, tau, batch, B, gamma, vocab, n_accepted,
+                                             next_token, status, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
+}
+
 int simsd_debug_mask(const int32_t* tau, int32_t batch, int32_t B, int32_t mask_mode, uint64_t* bits,
                      void* stream) {
   if (batch < 0 || B < 0 || B > 64) return SIMSD_ERR_SHAPE;

@@ -196,6 +196,11 @@ hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s
 size_t mfma_lds_bytes(int hd, int nstage, int B, int rows_wg, bool qsep);
 hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 void accept_plan(int NB, int64_t V, int& nch, int& cpw, int& ngrp);
+int coupled_chunks(int64_t V);
+size_t coupled_workspace_bytes(int NB, int B, int64_t V);
+hipError_t launch_accept_coupled(const float* p, const float* e, const int32_t* draft, const int32_t* tau, int NB,
+                                 int B, int gamma, int64_t V, int32_t* n_out, int32_t* next_out, int32_t* status,
+                                 void* workspace, hipStream_t s);
 hipError_t launch_accept(const float* p, const float* q, const int32_t* draft, const int32_t* tau,
                          int NB, int B, int gamma, int64_t V, uint64_t seed, uint64_t offset,
                          int32_t* n_acc, int32_t* next_tok, int32_t* status, void* workspace, hipStream_t s);

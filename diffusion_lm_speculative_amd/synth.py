@@ -117,6 +117,16 @@ def make_accept_inputs(NB, B, V, seed, device="cpu", sigma=math.sqrt(2.0)):
     return dict(p=p.contiguous(), q=q.contiguous(), draft_tok=x.contiguous(), tau=tau.contiguous())
 
 
+def make_noise_exp(NB, B, V, seed, device="cpu"):
+    """Shared noise table in exponential form [NB][B][V] float32: Exp(1)
+    variates (E = exp(-g) for a Gumbel g), drawn from their own generator and
+    kept strictly positive (the smallest normal float32 replaces an
+    underflowed zero)."""
+    g = _gen(device, seed)
+    e = torch.empty((NB, B, V), device=device, dtype=torch.float32).exponential_(1.0, generator=g)
+    return e.clamp_min_(torch.finfo(torch.float32).tiny).contiguous()
+
+
 def to_numpy64(t):
     """Exact float64 copy of a float32 / bfloat16 tensor (for the oracle)."""
     return t.detach().to("cpu").to(torch.float32).double().numpy()

@@ -176,6 +176,50 @@ int simsd_accept_prefix(const float* p_target, const float* q_draft,
                         int32_t* n_accepted, int32_t* next_token, int32_t* status,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes that simsd_accept_coupled needs (host only, no HIP call):
+ * one (p, E, index) winner per 8192-element chunk of every walked row.  It
+ * needs no initialisation; two calls that overlap in time must not share one. */
+int simsd_accept_coupled_workspace(int32_t batch, int32_t B, int64_t vocab, size_t* bytes);
+
+/* Coupled-noise acceptance (SPOT page, "how to use it" section: the drafter
+ * and the target share one Gumbel noise table per output position; given the
+ * noise the target's next state is a deterministic argmax, and a draft is
+ * kept exactly when it equals that argmax), walked in tau order as above.
+ *
+ *  p_target  [NB][B][V] fp32  target probabilities for response position k.
+ *  noise_exp [NB][B][V] fp32  the shared noise in exponential form,
+ *                             E = exp(-g) for the Gumbel value g of (k, v):
+ *                             finite and > 0 (an Exp(1) draw).  The caller
+ *                             keys the table by output position; row k is
+ *                             the table of the position drafted into D_k.
+ *  draft_tok [NB][B] int32    token placed in D_k (the drafter's noised
+ *                             argmax over its own distribution).
+ *  tau       [NB][B] int32    permutation of 1..B.
+ *  gamma     0..B             stages walked; stage t is position k_t with
+ *                             tau[k_t] = t.
+ *  The target token of a row is argmax_v p_v / E_v (= argmax ln p_v + g_v),
+ *  decided exactly (p_a * E_b against p_b * E_a in fp64, exact for fp32
+ *  inputs; equal scores to the smaller index; p_v <= 0 never wins, a row
+ *  without a positive p_v has none: -1).
+ *  n_accepted [NB] int32      longest prefix of stages whose draft equals the
+ *                             target token, 0..gamma.
+ *  next_token [NB] int32      or NULL: the target token of stage n+1 (a draw
+ *                             from p once the noise is marginalised); -1 when
+ *                             n == gamma.
+ *  status    [NB] int32 or NULL: SIMSD_ST_TAU_RANGE, SIMSD_ST_TAU_NOT_PERM,
+ *                             SIMSD_ST_TOKEN_RANGE; a faulted sequence gets
+ *                             n_accepted = next_token = -1.
+ *  workspace / workspace_bytes: at least simsd_accept_coupled_workspace
+ *                             bytes, 256-byte aligned.
+ * p_target and noise_exp are 16-byte aligned.
+ *
+ * Errors: SIMSD_ERR_NULL, _SHAPE (negative sizes, B > 64, vocab < 1 or
+ * > 65535 * 8192, batch * gamma >= 2^31), _GAMMA, _WORKSPACE, _ALIGN, _HIP. */
+int simsd_accept_coupled(const float* p_target, const float* noise_exp, const int32_t* draft_tok,
+                         const int32_t* tau, int32_t batch, int32_t B, int32_t gamma, int64_t vocab,
+                         int32_t* n_accepted, int32_t* next_token, int32_t* status, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Export the block visibility that the attention kernels compute from tau,
  * through the same device function (section 2 rules plus the data-row
  * convention).  bits [NB][2B][2] uint64: word 0 bit j = row sees D_j, word 1

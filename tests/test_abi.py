@@ -37,7 +37,7 @@ def _declared():
 def test_header_declarations_match_binding():
     decl = _declared()
     assert decl == set(L.SIGNATURES), decl ^ set(L.SIGNATURES)
-    assert len(decl) == 8
+    assert len(decl) == 10
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -171,6 +171,38 @@ def test_accept_rejects_on_host(lib):
         assert call(**{k: A + 2}) == L.ERR_ALIGN, k
     # the residual draw (next_token != NULL) needs the workspace
     assert call(nx=A) == L.ERR_WORKSPACE
+
+
+@no_gpu_only
+def test_accept_coupled_rejects_on_host(lib):
+    WS = 1 << 20
+    def call(p=A, e=A, x=A, tau=A, NB=4, B=8, gamma=8, V=1000, n=A, nx=None, st=None, ws=A, wsb=WS):
+        return lib.simsd_accept_coupled(p, e, x, tau, NB, B, gamma, V, n, nx, st, ws, ctypes.c_size_t(wsb), None)
+    assert call(gamma=9) == L.ERR_GAMMA
+    assert call(gamma=-1) == L.ERR_GAMMA
+    assert call(B=65, gamma=1) == L.ERR_SHAPE
+    assert call(V=0) == L.ERR_SHAPE
+    assert call(V=65535 * 8192 + 1) == L.ERR_SHAPE
+    assert call(NB=-1) == L.ERR_SHAPE
+    assert call(NB=0, p=None, e=None, x=None, tau=None, n=None, ws=None) == 0
+    for k in ("p", "e", "x", "tau", "n"):
+        assert call(**{k: None}) == L.ERR_NULL, k
+    for k in ("x", "tau", "n", "nx", "st"):
+        assert call(**{k: A + 2}) == L.ERR_ALIGN, k
+    for k in ("p", "e"):  # rows are read in 16-byte pieces
+        assert call(**{k: A + 4}) == L.ERR_ALIGN, k
+    assert call(ws=None) == L.ERR_WORKSPACE
+    assert call(wsb=16) == L.ERR_WORKSPACE
+    assert call(ws=A + 64) == L.ERR_ALIGN
+
+
+def test_accept_coupled_workspace_size(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.simsd_accept_coupled_workspace(4, 16, 151936, ctypes.byref(n)) == 0
+    chunks = -(-151936 // 8192)
+    assert n.value == -(-(4 * 16 * chunks * 16) // 256) * 256
+    assert lib.simsd_accept_coupled_workspace(4, 65, 100, ctypes.byref(n)) == L.ERR_SHAPE
+    assert lib.simsd_accept_coupled_workspace(4, 8, 100, None) == L.ERR_NULL
 
 
 @no_gpu_only
