@@ -105,6 +105,59 @@ def copy_calibration(torch, dev, mib, steps, warmup):
                       "gbs_read_plus_write": 2 * n * 4 / (us * 1e-6) / 1e9}), flush=True)
 
 
+def coupled_measure(torch, sd, synth, dev, stream, steps, warmup):
+    """Coupled-noise acceptance over full vocabulary rows, timed on its own.
+
+    Workload: batch 64, B = gamma = 16, V = 151936, p = softmax of N(0, 2)
+    logits, Exp(1) noise.  Drafts hold the target token (argmax of p/E,
+    taken here with plain torch ops) for the first m stages of each sequence,
+    m uniform in 0..gamma, so the walk's lengths spread; the kernel reads
+    every walked row whatever the outcome.  Algorithmic bytes per call:
+    batch * gamma rows of p and E, V * 4 bytes each.
+    """
+    w = synth.WORKLOADS["sdar8b_var16k_b16_accept"]
+    NB, B, gamma, V = w.NB, w.B, w.gamma, w.vocab
+    sets = []
+    for i in range(2):  # two sets of 1.245 GB: larger than the last-level cache
+        a = synth.make_accept_inputs(NB, B, V, seed=3003 + 100 * i, device=dev)
+        del a["q"]
+        e = synth.make_noise_exp(NB, B, V, seed=3004 + 100 * i, device=dev)
+        target = torch.argmax(a["p"] / e, dim=-1).to(torch.int32)
+        g = torch.Generator(device=dev)
+        g.manual_seed(3005 + 100 * i)
+        m = torch.randint(0, gamma + 1, (NB, 1), generator=g, device=dev, dtype=torch.int32)
+        draft = torch.where(a["tau"] <= m, target, a["draft_tok"]).contiguous()
+        n = torch.empty((NB,), dtype=torch.int32, device=dev)
+        nx = torch.empty_like(n)
+        st = torch.empty_like(n)
+        ws = torch.empty(sd.accept_coupled_workspace_bytes(NB, B, V), dtype=torch.uint8, device=dev)
+        call = sd.bind_accept_coupled(a["p"], e, draft, a["tau"], gamma, n_accepted=n, next_token=nx, status=st,
+                                      workspace=ws, stream=stream)
+        sets.append(dict(call=call, n=n, st=st, m=m))
+    torch.cuda.synchronize()
+    for s in sets:
+        s["call"]()
+    torch.cuda.synchronize()
+    if any(int(s["st"].abs().sum()) for s in sets):
+        raise RuntimeError("coupled acceptance: device status flags set")
+    mean_n = sum(float(s["n"].float().mean()) for s in sets) / len(sets)
+    for i in range(warmup):
+        sets[i % 2]["call"]()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        sets[i % 2]["call"]()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    avg = sum(ms) / len(ms)
+    nbytes = NB * gamma * V * 4 * 2
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    return {"workload": "batch 64, B = gamma = 16, V = 151936, fp32 p and Exp(1) noise",
+            "us": {"mean": avg * 1e3, "median": ms[len(ms) // 2] * 1e3}, "mean_n_accepted": mean_n,
+            "algorithmic_bytes": nbytes, "achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +258,8 @@ def main():
     desc = sd.make_desc(sets[0]["t"]["q_blk"], sets[0]["t"]["k_blk"], sets[0]["t"]["k_cache"], rope_base=w.rope_base)
     traffic = measured_traffic()
 
+    coupled = coupled_measure(torch, sd, synth, dev, stream, args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         nb = w.NB
@@ -236,6 +291,7 @@ def main():
         "accept_us": {"mean": a_avg * 1e3, "median": accept_ms[len(accept_ms) // 2] * 1e3},
         "workspace_bytes": sd.verify_workspace_bytes(desc),
         "cpu_baseline": cpu,
+        "accept_coupled": coupled,
     }
     print(json.dumps(rec), flush=True)
 

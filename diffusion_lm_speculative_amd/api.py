@@ -265,6 +265,39 @@ def bind_accept(p_target, q_draft, draft_tok, tau, gamma, *, n_accepted, next_to
     return AcceptCall(head, tail, (p_target, q_draft, draft_tok, tau, n_accepted, next_token, status, workspace))
 
 
+@dataclass
+class CoupledCall:
+    """An accept_coupled call with every pointer bound once (for timing loops).
+    `keep` holds the bound tensors."""
+    args: tuple
+    keep: tuple = ()
+
+    def __call__(self):
+        rc = L.load().simsd_accept_coupled(*self.args)
+        if rc:
+            L.check(rc, "simsd_accept_coupled")
+
+
+def bind_accept_coupled(p_target, noise_exp, draft_tok, tau, gamma, *, n_accepted, next_token=None, status=None,
+                        workspace, stream=None) -> CoupledCall:
+    NB, B, V = p_target.shape
+    dev = p_target.device
+    _need(p_target, "p_target", torch.float32)
+    _need(noise_exp, "noise_exp", torch.float32, (NB, B, V), dev)
+    _need(draft_tok, "draft_tok", torch.int32, (NB, B), dev)
+    _need(tau, "tau", torch.int32, (NB, B), dev)
+    _need(n_accepted, "n_accepted", torch.int32, (NB,), dev)
+    for t, name in ((next_token, "next_token"), (status, "status")):
+        if t is not None:
+            _need(t, name, torch.int32, (NB,), dev)
+    ws_len = workspace.numel() * workspace.element_size()
+    if ws_len < accept_coupled_workspace_bytes(NB, B, V):
+        raise ValueError(f"workspace of {accept_coupled_workspace_bytes(NB, B, V)} bytes required")
+    args = (_ptr(p_target), _ptr(noise_exp), _ptr(draft_tok), _ptr(tau), NB, B, int(gamma), V, _ptr(n_accepted),
+            _ptr(next_token), _ptr(status), _ptr(workspace), ctypes.c_size_t(ws_len), _stream_handle(stream))
+    return CoupledCall(args, (p_target, noise_exp, draft_tok, tau, n_accepted, next_token, status, workspace))
+
+
 def debug_mask(tau, mask_mode=L.MASK_TEMPORAL, stream=None):
     """Block visibility words [NB][2B][2] (int64 view of the uint64 bits)."""
     lib = L.load()

@@ -18,9 +18,10 @@
 //      its chunk of p[b][k] and E[b][k] (16-byte loads; the rows are this
 //      call's bytes: 2 * V * 4 per walked stage) and reduces its best
 //      (p, E, index) over lanes and waves with the exact comparison.
-//   2. walk, one wave per sequence: validation (labels 1..B, a permutation,
-//      drafted tokens in range), then stage by stage the reduction of the
-//      row's chunk winners and the compare with the draft.
+//   2. walk, one workgroup per sequence: the reduction of every walked row's
+//      chunk winners (stages spread over the waves), then validation (labels
+//      1..B, a permutation, drafted tokens in range) and the compare of each
+//      draft with its stage's target token.
 #include "simsd_common.hpp"
 
 namespace simsd {
@@ -30,6 +31,7 @@ constexpr int kCoThreads = 512;
 constexpr int kCoWaves = kCoThreads / 64;
 constexpr int kCoPerLane = 16;                           // elements per lane per chunk
 constexpr int kCoChunk = kCoThreads * kCoPerLane;        // 8192 elements per workgroup
+constexpr int kMaxB = 64;                                // longest section (stages per sequence)
 
 struct Best {
   float p, e;
@@ -89,14 +91,30 @@ __global__ __launch_bounds__(kCoThreads) void coupled_argmax_kernel(const float*
     const int64_t v0 = static_cast<int64_t>(c) * kCoChunk;
     const int64_t v1 = min(v0 + kCoChunk, V);
     if ((V & 3) == 0) {  // rows start 16-byte aligned: 16-byte loads of 4 elements
-      for (int64_t v = v0 + 4 * tid; v < v1; v += 4 * kCoThreads) {
-        const float4 p4 = *reinterpret_cast<const float4*>(pr + v);
-        const float4 e4 = *reinterpret_cast<const float4*>(er + v);
-        const int i = static_cast<int>(v);
-        take(best, p4.x, e4.x, i);
-        take(best, p4.y, e4.y, i + 1);
-        take(best, p4.z, e4.z, i + 2);
-        take(best, p4.w, e4.w, i + 3);
+      // every load of the lane is issued before the first compare, so a wave
+      // keeps 8 x 1 KiB in flight.  Lanes past the row's end load the row's
+      // last four elements again (no branch around the loads) and drop them:
+      // p = 0 never wins
+      constexpr int kU = kCoPerLane / 4;
+      float4 p4[kU], e4[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t v = v0 + 4 * (tid + u * kCoThreads);
+        const int64_t vc = v < v1 ? v : v1 - 4;
+        p4[u] = *reinterpret_cast<const float4*>(pr + vc);
+        e4[u] = *reinterpret_cast<const float4*>(er + vc);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (v0 + 4 * (tid + u * kCoThreads) >= v1) p4[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = static_cast<int>(v0) + 4 * (tid + u * kCoThreads);
+        take(best, p4[u].x, e4[u].x, i);
+        take(best, p4[u].y, e4[u].y, i + 1);
+        take(best, p4[u].z, e4[u].z, i + 2);
+        take(best, p4[u].w, e4[u].w, i + 3);
       }
     } else {
       for (int64_t v = v0 + tid; v < v1; v += kCoThreads) take(best, pr[v], er[v], static_cast<int>(v));
@@ -113,16 +131,50 @@ __global__ __launch_bounds__(kCoThreads) void coupled_argmax_kernel(const float*
   }
 }
 
-__global__ __launch_bounds__(64) void coupled_walk_kernel(const int32_t* __restrict__ draft,
-                                                           const int32_t* __restrict__ tau, int B, int gamma,
-                                                           int64_t V, int nch, const float4* __restrict__ part,
-                                                           int32_t* n_out, int32_t* next_out, int32_t* status) {
+// Target tokens of the walked stages, then the walk.  Wave w reduces the
+// chunk winners of stages w, w + 16, w + 32, w + 48 (their loads issued
+// together), so the rows' reductions take one round of load latency rather
+// than one per stage; wave 0 then validates the sequence and walks.
+constexpr int kWalkWaves = 16;
+constexpr int kWalkRounds = (kMaxB + kWalkWaves - 1) / kWalkWaves;
+
+__global__ __launch_bounds__(kWalkWaves * 64) void coupled_walk_kernel(
+    const int32_t* __restrict__ draft, const int32_t* __restrict__ tau, int B, int gamma, int64_t V, int nch,
+    const float4* __restrict__ part, int32_t* n_out, int32_t* next_out, int32_t* status) {
+  __shared__ int s_target[kMaxB];
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int32_t* tau_b = tau + static_cast<size_t>(b) * B;
   const int32_t* draft_b = draft + static_cast<size_t>(b) * B;
-  const int lab = lane < B ? tau_b[lane] : 0;
-  const int tok = lane < B ? draft_b[lane] : 0;
+  const int lab = wave == 0 && lane < B ? tau_b[lane] : 0;
+  const int tok = wave == 0 && lane < B ? draft_b[lane] : 0;
+  const float4* part_b = part + static_cast<size_t>(b) * gamma * nch;
+
+  Best w[kWalkRounds];
+#pragma unroll
+  for (int u = 0; u < kWalkRounds; ++u) w[u] = Best{0.0f, 1.0f, -1};
+  for (int c = lane; c < nch; c += 64) {
+    float4 q[kWalkRounds];
+#pragma unroll
+    for (int u = 0; u < kWalkRounds; ++u) {
+      const int t = wave + kWalkWaves * u;  // 0-based stage
+      q[u] = t < gamma ? part_b[static_cast<size_t>(t) * nch + c] : make_float4(0.0f, 1.0f, __int_as_float(-1), 0.0f);
+    }
+#pragma unroll
+    for (int u = 0; u < kWalkRounds; ++u) {
+      const int i = __float_as_int(q[u].z);
+      if (i >= 0) take(w[u], q[u].x, q[u].y, i);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kWalkRounds; ++u) {
+    const int t = wave + kWalkWaves * u;
+    const Best r = wave_best(w[u]);
+    if (lane == 0 && t < gamma) s_target[t] = r.idx;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
   int st = 0;
   if (__any(lane < B && (lab < 1 || lab > B))) {
     st = SIMSD_ST_TAU_RANGE;
@@ -138,24 +190,16 @@ __global__ __launch_bounds__(64) void coupled_walk_kernel(const int32_t* __restr
   }
   int n = -1, nxt = -1;
   if (st == 0) {
+    // the lane of position k compares its draft with its stage's target
+    // token; the first mismatch in stage order ends the walk
+    const bool walked = lane < B && lab <= gamma;
+    const uint64_t miss = __ballot(walked && s_target[walked ? lab - 1 : 0] != tok);
     n = gamma;
-    for (int t = 1; t <= gamma; ++t) {
-      const int row = b * gamma + (t - 1);
-      Best w{0.0f, 1.0f, -1};
-      for (int c = lane; c < nch; c += 64) {
-        const float4 q = part[static_cast<size_t>(row) * nch + c];
-        const int i = __float_as_int(q.z);
-        if (i >= 0) take(w, q.x, q.y, i);
-      }
-      w = wave_best(w);
-      const uint64_t hit = __ballot(lane < B && lab == t);
-      const int k = __builtin_ctzll(hit);
-      const int x = __shfl(tok, k);
-      if (w.idx != x) {
-        n = t - 1;
-        nxt = w.idx;
-        break;
-      }
+    if (miss) {
+      int first = kMaxB + 1;  // smallest stage label among the mismatching lanes
+      for (uint64_t m = miss; m; m &= m - 1) first = min(first, __shfl(lab, __builtin_ctzll(m)));
+      n = first - 1;
+      nxt = s_target[first - 1];
     }
   }
   if (lane == 0) {
@@ -185,7 +229,7 @@ hipError_t launch_accept_coupled(const float* p, const float* e, const int32_t* 
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(coupled_walk_kernel, dim3(NB), dim3(64), 0, s, draft, tau, B, gamma, V, nch, part, n_out,
+  hipLaunchKernelGGL(coupled_walk_kernel, dim3(NB), dim3(kWalkWaves * 64), 0, s, draft, tau, B, gamma, V, nch, part, n_out,
                      next_out, status);
   return hipGetLastError();
 }
