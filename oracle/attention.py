@@ -13,6 +13,11 @@ Models" (gist.science summary of arXiv 2606.02544):
   later, still undecided stage).  Future data tokens stay hidden.
 * section 3 (position encoding alignment): D~_k reuses the RoPE index of
   D_k.
+* "Experimental results", ablations: dropping that RoPE copy ruins the
+  verification.  The page does not say which index the mask slots take
+  without the copy; the plainest reading, taken here as ``rope_mode =
+  ROPE_SEQUENTIAL``, is that the 2B block rows take consecutive indices in
+  layout order, so D~_k sits B past D_k (P_b + B + k by default).
 
 Readings taken where the page is silent (each is also listed in the design
 notes):
@@ -35,7 +40,10 @@ float64 scaled_dot_product_attention on the state each mask row is meant to
 reproduce, the all-visible mode against bidirectional attention, causal
 attention for tau = identity, joint permutation equivariance, a pure-Python
 brute-force enumeration on tiny inputs, RoPE against complex rotation and a
-hand-worked example, and hand-derived masks under tests/golden/.
+hand-worked example, and hand-derived masks under tests/golden/.  The
+ablation's positions are pinned by plain bidirectional attention over the
+block laid out at consecutive positions (RoPE by complex multiplication) and
+by the brute force with shifted mask-slot indices.
 """
 
 from __future__ import annotations
@@ -44,6 +52,11 @@ import numpy as np
 
 MASK_TEMPORAL = 0
 MASK_FULL = 1
+
+# RoPE index of the mask slots: the method's copy, or the ablation's
+# consecutive indices.
+ROPE_COPY = 0
+ROPE_SEQUENTIAL = 1
 
 # Per-sequence fault flags (the same values the C-ABI documents).
 ST_TAU_RANGE = 1
@@ -115,7 +128,7 @@ def verify_status_ref(tau, prompt_len, pos_d, p_max):
 
 def verify_attn_ref(q_blk, k_blk, v_blk, k_cache, v_cache, prompt_len, tau,
                     pos_d=None, rope_base=10000.0, scale=None,
-                    mask_mode=MASK_TEMPORAL):
+                    mask_mode=MASK_TEMPORAL, rope_mode=ROPE_COPY):
     """Attention of the 2B block rows of every sequence, in float64.
 
     Shapes (contiguous, any float dtype; values are read exactly):
@@ -152,8 +165,9 @@ def verify_attn_ref(q_blk, k_blk, v_blk, k_cache, v_cache, prompt_len, tau,
             pos = P + np.arange(B, dtype=np.int64)
         else:
             pos = np.asarray(pos_d[b], dtype=np.int64)
-        # RoPE copy: D~_k takes the position of D_k.
-        row_pos = np.concatenate([pos, pos])
+        # RoPE copy: D~_k takes the position of D_k; without it (the
+        # ablation) D~_k follows the data section, B positions later.
+        row_pos = np.concatenate([pos, pos + B if rope_mode == ROPE_SEQUENTIAL else pos])
         q_hat = rope_rotate(q_blk[b], row_pos[:, None], rope_base)   # [2B][Hq][d]
         k_hat = rope_rotate(k_blk[b], row_pos[:, None], rope_base)   # [2B][Hkv][d]
         vis = np.concatenate(

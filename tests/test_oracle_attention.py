@@ -22,7 +22,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.attention import MASK_FULL, rope_rotate, verify_attn_ref
+from oracle.attention import MASK_FULL, ROPE_SEQUENTIAL, rope_rotate, verify_attn_ref
 
 
 def _inputs(seed, NB, Hq, Hkv, d, P, B, p_max=None, ties=False):
@@ -262,8 +262,9 @@ def test_faulted_sequences_are_zero():
 
 # ----------------------------------------------------------------------------- brute force
 
-def _brute_force(q, kb, vb, kc, vc, plen, tau, base):
-    """Pure-Python loops: enumerate each row's visible set, then softmax with math.exp."""
+def _brute_force(q, kb, vb, kc, vc, plen, tau, base, seq=False):
+    """Pure-Python loops: enumerate each row's visible set, then softmax with math.exp.
+    With ``seq`` the mask slots sit B positions after their data tokens."""
     NB, twoB, Hq, d = q.shape
     B = twoB // 2
     G = Hq // kb.shape[2]
@@ -271,11 +272,12 @@ def _brute_force(q, kb, vb, kc, vc, plen, tau, base):
     for b in range(NB):
         Pb = int(plen[b])
         pos = [Pb + k for k in range(B)]
+        mpos = [p + B for p in pos] if seq else pos
         for h in range(Hq):
             g = h // G
             for r in range(twoB):
                 i = r % B
-                qr = [float(v) for v in rope_rotate(q[b, r, h], pos[i], base)]
+                qr = [float(v) for v in rope_rotate(q[b, r, h], pos[i] if r < B else mpos[i], base)]
                 cols = []
                 for c in range(Pb):
                     cols.append((list(kc[b, g, c]), list(vc[b, g, c])))
@@ -287,7 +289,7 @@ def _brute_force(q, kb, vb, kc, vc, plen, tau, base):
                     if seen_d:
                         cols.append((list(rope_rotate(kb[b, j, g], pos[j], base)), list(vb[b, j, g])))
                     if seen_m:
-                        cols.append((list(rope_rotate(kb[b, B + j, g], pos[j], base)), list(vb[b, B + j, g])))
+                        cols.append((list(rope_rotate(kb[b, B + j, g], mpos[j], base)), list(vb[b, B + j, g])))
                 scores = [sum(a * c for a, c in zip(qr, k)) / math.sqrt(d) for k, _ in cols]
                 mx = max(scores)
                 w = [math.exp(s - mx) for s in scores]
@@ -309,3 +311,45 @@ def test_brute_force_with_ties():
     q, kb, vb, kc, vc, plen, tau = _inputs(104, 1, 2, 1, 8, 4, 5, ties=True)
     out, _, _ = verify_attn_ref(q, kb, vb, kc, vc, plen, tau, rope_base=1e4)
     np.testing.assert_allclose(out, _brute_force(q, kb, vb, kc, vc, plen, tau, 1e4), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed,P,B", [(105, 0, 3), (106, 5, 4)])
+def test_brute_force_without_rope_copy(seed, P, B):
+    q, kb, vb, kc, vc, plen, tau = _inputs(seed, 2, 4, 2, 8, P, B)
+    out, _, _ = verify_attn_ref(q, kb, vb, kc, vc, plen, tau, rope_base=1e4, rope_mode=ROPE_SEQUENTIAL)
+    want = _brute_force(q, kb, vb, kc, vc, plen, tau, 1e4, seq=True)
+    np.testing.assert_allclose(out, want, rtol=0, atol=1e-12)
+
+
+def _rope_complex(x, pos, base):
+    """RoPE as multiplication of (x_f + i x_{f+d/2}) by exp(i pos base^(-2f/d))."""
+    d = x.shape[-1]
+    z = x[..., : d // 2] + 1j * x[..., d // 2:]
+    zr = z * np.exp(1j * np.asarray(pos, dtype=np.float64)[..., None] * base ** (-np.arange(0, d, 2) / d))
+    return np.concatenate([zr.real, zr.imag], axis=-1)
+
+
+@pytest.mark.parametrize("P,with_pos", [(0, False), (11, False), (6, True)])
+def test_without_rope_copy_full_mode_is_attention_over_consecutive_positions(P, with_pos):
+    # All-visible mask: every block row attends to the prompt and all 2B block
+    # rows, which sit at consecutive positions P_b .. P_b + 2B - 1 (or at
+    # pos_d then pos_d + B): plain bidirectional attention over that layout.
+    NB, Hq, Hkv, d, B = 2, 4, 2, 16, 5
+    q, kb, vb, kc, vc, plen, tau = _inputs(33, NB, Hq, Hkv, d, P, B)
+    plen[:] = P
+    pos_d = np.array([[3, 40, 7, 9, 1], [100, 0, 2, 5, 6]]) if with_pos else None
+    out, _, _ = verify_attn_ref(q, kb, vb, kc, vc, plen, tau, pos_d=pos_d, mask_mode=MASK_FULL,
+                                rope_mode=ROPE_SEQUENTIAL)
+    for b in range(NB):
+        base_pos = np.asarray(pos_d[b]) if with_pos else P + np.arange(B)
+        rp = np.concatenate([base_pos, base_pos + B])
+        qh = _rope_complex(q[b], rp[:, None], 1e4)
+        kh = _rope_complex(kb[b], rp[:, None], 1e4)
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            keys = np.concatenate([kc[b, g, :P], kh[:, g]])
+            vals = np.concatenate([vc[b, g, :P], vb[b, :, g]])
+            np.testing.assert_allclose(out[b, :, h], _sdpa(qh[:, h], keys, vals), rtol=0, atol=1e-12)
+    # the two placements differ on the mask rows (the position shift is real)
+    copy, _, _ = verify_attn_ref(q, kb, vb, kc, vc, plen, tau, pos_d=pos_d, mask_mode=MASK_FULL)
+    assert np.abs(copy[:, B:] - out[:, B:]).max() > 1e-3
