@@ -9,7 +9,7 @@ kernels are HIP for gfx950 behind the C ABI of include/simsd.h
 (libsimsd.so); this package is its thin Python binding.
 """
 from ._lib import (  # noqa: F401
-    BF16, F32, IMPL_AUTO, IMPL_MFMA, IMPL_VALU, MASK_FULL, MASK_TEMPORAL, SimsdError,
+    BF16, F32, IMPL_AUTO, IMPL_MFMA, IMPL_VALU, MASK_FULL, MASK_TEMPORAL, ROPE_COPY, ROPE_SEQUENTIAL, SimsdError,
     ST_POS_NEG, ST_PROMPT_LEN, ST_TAU_NOT_PERM, ST_TAU_RANGE, ST_TOKEN_RANGE,
 )
 from .api import (  # noqa: F401

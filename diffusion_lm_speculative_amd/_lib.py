@@ -43,6 +43,8 @@ MASK_FULL = 1
 IMPL_AUTO = 0
 IMPL_VALU = 1
 IMPL_MFMA = 2
+ROPE_COPY = 0
+ROPE_SEQUENTIAL = 1
 
 
 class VerifyDesc(ctypes.Structure):
@@ -59,6 +61,7 @@ class VerifyDesc(ctypes.Structure):
         ("kv_chunk", c_int32),
         ("rope_base", c_double),
         ("softmax_scale", c_float),
+        ("rope_mode", c_int32),
     ]
 
 

@@ -45,7 +45,7 @@ _DT = {torch.float32: L.F32, torch.bfloat16: L.BF16}
 
 
 def make_desc(q_blk, k_blk, k_cache, *, rope_base, softmax_scale=0.0, mask_mode=L.MASK_TEMPORAL,
-              impl=L.IMPL_AUTO, kv_chunk=0, p_max=None):
+              impl=L.IMPL_AUTO, kv_chunk=0, p_max=None, rope_mode=L.ROPE_COPY):
     NB, twoB, Hq, d = q_blk.shape
     Hkv = k_blk.shape[2]
     if twoB % 2:
@@ -55,7 +55,7 @@ def make_desc(q_blk, k_blk, k_cache, *, rope_base, softmax_scale=0.0, mask_mode=
     if p_max is None:
         p_max = 0 if k_cache is None else k_cache.shape[2]
     return L.VerifyDesc(NB, Hq, Hkv, d, twoB // 2, p_max, _DT[q_blk.dtype], int(mask_mode), int(impl),
-                        int(kv_chunk), float(rope_base), float(softmax_scale))
+                        int(kv_chunk), float(rope_base), float(softmax_scale), int(rope_mode))
 
 
 def verify_workspace_bytes(desc) -> int:
@@ -67,8 +67,8 @@ def verify_workspace_bytes(desc) -> int:
 
 def verify_attn(q_blk, k_blk, v_blk, k_cache, v_cache, tau, prompt_len=None, pos_d=None, *,
                 rope_base=10000.0, softmax_scale=0.0, mask_mode=L.MASK_TEMPORAL, impl=L.IMPL_AUTO,
-                kv_chunk=0, out=None, lse=None, status=None, workspace=None, stream=None,
-                with_lse=True, with_status=True):
+                kv_chunk=0, rope_mode=L.ROPE_COPY, out=None, lse=None, status=None, workspace=None,
+                stream=None, with_lse=True, with_status=True):
     """SimSD verification attention; returns (out, lse, status).
 
     q_blk [NB][2B][Hq][d], k_blk/v_blk [NB][2B][Hkv][d], k_cache/v_cache
@@ -95,7 +95,7 @@ def verify_attn(q_blk, k_blk, v_blk, k_cache, v_cache, tau, prompt_len=None, pos
     if pos_d is not None:
         _need(pos_d, "pos_d", torch.int32, (NB, B), dev)
     desc = make_desc(q_blk, k_blk, k_cache, rope_base=rope_base, softmax_scale=softmax_scale,
-                     mask_mode=mask_mode, impl=impl, kv_chunk=kv_chunk)
+                     mask_mode=mask_mode, impl=impl, kv_chunk=kv_chunk, rope_mode=rope_mode)
     if out is None:
         out = torch.empty_like(q_blk)
     _need(out, "out", dt, tuple(q_blk.shape), dev)
@@ -309,12 +309,13 @@ def debug_mask(tau, mask_mode=L.MASK_TEMPORAL, stream=None):
     return bits
 
 
-def debug_rope(q_blk, k_blk, prompt_len=None, pos_d=None, *, rope_base, p_max=0, stream=None):
+def debug_rope(q_blk, k_blk, prompt_len=None, pos_d=None, *, rope_base, p_max=0, rope_mode=L.ROPE_COPY,
+               stream=None):
     """Rotated block rows (q_rot, k_rot) as the attention kernels use them."""
     lib = L.load()
     _need(q_blk, "q_blk", q_blk.dtype)
     _need(k_blk, "k_blk", q_blk.dtype)
-    desc = make_desc(q_blk, k_blk, None, rope_base=rope_base, p_max=p_max)
+    desc = make_desc(q_blk, k_blk, None, rope_base=rope_base, p_max=p_max, rope_mode=rope_mode)
     q_rot = torch.empty_like(q_blk)
     k_rot = torch.empty_like(k_blk)
     L.check(lib.simsd_debug_rope(ctypes.byref(desc), _ptr(q_blk), _ptr(k_blk), _ptr(prompt_len), _ptr(pos_d),

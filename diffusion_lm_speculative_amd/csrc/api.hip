@@ -26,7 +26,8 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
     return SIMSD_ERR_SHAPE;
   if ((d.dtype != SIMSD_F32 && d.dtype != SIMSD_BF16) ||
       (d.mask_mode != SIMSD_MASK_TEMPORAL && d.mask_mode != SIMSD_MASK_FULL) ||
-      (d.impl != SIMSD_IMPL_AUTO && d.impl != SIMSD_IMPL_VALU && d.impl != SIMSD_IMPL_MFMA))
+      (d.impl != SIMSD_IMPL_AUTO && d.impl != SIMSD_IMPL_VALU && d.impl != SIMSD_IMPL_MFMA) ||
+      (d.rope_mode != SIMSD_ROPE_COPY && d.rope_mode != SIMSD_ROPE_SEQUENTIAL))
     return SIMSD_ERR_DTYPE;
   if (d.impl == SIMSD_IMPL_MFMA && d.dtype != SIMSD_BF16) return SIMSD_ERR_DTYPE;
   if (d.kv_chunk < 0 || d.kv_chunk % kKeyTile != 0) return SIMSD_ERR_KV_CHUNK;
@@ -48,6 +49,14 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   const float scale = d.softmax_scale > 0.0f ? d.softmax_scale : 1.0f / std::sqrt(static_cast<float>(d.head_dim));
   pl.scale_log2 = scale * kLog2e;
   pl.impl = d.impl == SIMSD_IMPL_AUTO ? (d.dtype == SIMSD_BF16 ? SIMSD_IMPL_MFMA : SIMSD_IMPL_VALU) : d.impl;
+  pl.rope_seq = d.rope_mode == SIMSD_ROPE_SEQUENTIAL;
+  pl.tab_rows = pl.rope_seq ? 2 * d.B : d.B;  // distinct block positions
+  if (pl.impl == SIMSD_IMPL_MFMA && d.head_dim == 128 &&
+      mfma_lds_bytes(128, 3, pl.tab_rows, 128, false) + 1024 > kLdsPerCu) {
+    // the RoPE table does not fit beside a 3-stage ring
+    if (d.impl == SIMSD_IMPL_MFMA) return SIMSD_ERR_SHAPE;
+    pl.impl = SIMSD_IMPL_VALU;
+  }
 
   if (pl.impl == SIMSD_IMPL_MFMA) {
     // 16-row tiles per workgroup: 1, 2 or 4 (one per row wave), or 8 (four
@@ -65,11 +74,11 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
     // Four ring stages with the query rows staged in their own LDS region
     // when that fits; else the query rows borrow the last stage during the
     // prologue; else three stages.
-    if (mfma_lds_bytes(pl.d, 4, pl.B, pl.rows_wg, true) + 1024 <= kLdsPerCu) {
+    if (mfma_lds_bytes(pl.d, 4, pl.tab_rows, pl.rows_wg, true) + 1024 <= kLdsPerCu) {
       pl.nstage = 4;
       pl.qsep = 1;
     } else {
-      pl.nstage = mfma_lds_bytes(pl.d, 4, pl.B, pl.rows_wg, false) + 1024 <= kLdsPerCu ? 4 : 3;
+      pl.nstage = mfma_lds_bytes(pl.d, 4, pl.tab_rows, pl.rows_wg, false) + 1024 <= kLdsPerCu ? 4 : 3;
       pl.qsep = 0;
     }
   } else {
@@ -85,7 +94,7 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   // kMaxChunk keys so ragged prompt lengths still spread evenly.
   int64_t target = 2 * kNumCUs;
   if (pl.impl == SIMSD_IMPL_MFMA) {
-    const size_t per_wg = mfma_lds_bytes(pl.d, pl.nstage, pl.B, pl.rows_wg, pl.qsep != 0) + 1024;
+    const size_t per_wg = mfma_lds_bytes(pl.d, pl.nstage, pl.tab_rows, pl.rows_wg, pl.qsep != 0) + 1024;
     target = kNumCUs * static_cast<int64_t>(kLdsPerCu / per_wg);
   }
   const int64_t tiles_max = (static_cast<int64_t>(pl.p_max) + kKeyTile - 1) / kKeyTile;
@@ -141,7 +150,7 @@ using namespace simsd;
 
 extern "C" {
 
-int simsd_abi_version(void) { return 1; }
+int simsd_abi_version(void) { return 2; }
 
 const char* simsd_strerror(int code) {
   switch (code) {

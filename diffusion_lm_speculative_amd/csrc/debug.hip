@@ -39,7 +39,7 @@ __global__ void debug_rope_kernel(Plan pl, const T* q_blk, const T* k_blk, const
   const int half = pl.d / 2;
   const int plen = prompt_len ? prompt_len[b] : pl.p_max;
   const int32_t* pos_b = pos_d ? pos_d + static_cast<size_t>(b) * pl.B : nullptr;
-  const int pos = block_pos(pos_b, plen, c % pl.B);
+  const int64_t pos = block_row_pos(pos_b, plen, c, pl.B, pl.rope_seq != 0);
   const size_t qrow = (static_cast<size_t>(b) * pl.twoB + c) * pl.Hq;
   const size_t krow = (static_cast<size_t>(b) * pl.twoB + c) * pl.Hkv;
   for (int i = threadIdx.x; i < (pl.Hq + pl.Hkv) * half; i += blockDim.x) {

@@ -122,7 +122,7 @@ __device__ __forceinline__ double rope_inv_freq(int f, int d, double log2_base) 
   return exp2(-(2.0 * f / d) * log2_base);
 }
 
-__device__ __forceinline__ float2 rope_cos_sin(int pos, double inv_freq) {
+__device__ __forceinline__ float2 rope_cos_sin(int64_t pos, double inv_freq) {
   const double theta = static_cast<double>(pos) * inv_freq;
   const double k = rint(theta * kInvTwoPi);
   const double red = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, theta));
@@ -138,9 +138,13 @@ __device__ __forceinline__ void rope_apply(float x, float y, float2 cs, float& x
   yo = fmaf(y, cs.x, x * cs.y);
 }
 
-// Position of response position k of sequence b (D_k and D~_k share it).
-__device__ __forceinline__ int block_pos(const int32_t* pos_b, int plen, int k) {
-  return pos_b ? pos_b[k] : plen + k;
+// RoPE index of block row r (0..B-1: D_r, B..2B-1: D~_{r-B}) of a sequence:
+// D_k at pos_d[k] (default P_b + k); D~_k at the same index (the RoPE copy)
+// or B past it (the ablation without the copy, `seq`).
+__device__ __forceinline__ int64_t block_row_pos(const int32_t* pos_b, int plen, int r, int B, bool seq) {
+  const int k = r < B ? r : r - B;
+  const int64_t p = pos_b ? static_cast<int64_t>(pos_b[k]) : static_cast<int64_t>(plen) + k;
+  return seq && r >= B ? p + B : p;
 }
 
 // ---------------------------------------------------------------- split-KV plan
@@ -162,6 +166,8 @@ struct Plan {
   double rope_base;
   double log2_base;                   // log2(rope_base)
   int qsep;                           // MFMA: query rows staged in their own LDS region
+  int rope_seq;                       // D~_k at pos(D_k) + B instead of pos(D_k)
+  int tab_rows;                       // distinct block positions: B, or 2B with rope_seq
   float scale_log2;                   // softmax scale * log2(e)
   size_t part_o_floats, part_ml_floats;
 };
@@ -193,7 +199,7 @@ __device__ __forceinline__ int valid_splits(int plen, int chunk, int nsplit) {
 // Host-side launchers (one per translation unit).
 hipError_t launch_verify_valu(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s);
-size_t mfma_lds_bytes(int hd, int nstage, int B, int rows_wg, bool qsep);
+size_t mfma_lds_bytes(int hd, int nstage, int tab_rows, int rows_wg, bool qsep);
 hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 void accept_plan(int NB, int64_t V, int& nch, int& cpw, int& ngrp);
 int coupled_chunks(int64_t V);

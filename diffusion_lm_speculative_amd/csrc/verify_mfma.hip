@@ -364,18 +364,23 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const int nspec = min(kSpecTiles, nbt + nts);
   issue_range(0, nspec, c1s);
 
-  // ---- RoPE table of the B block positions, while the loads are in flight:
-  //      positions come by scalar loads (a wave's 64 entries need at most two)
+  // ---- RoPE table of the distinct block positions (B with the RoPE copy,
+  //      2B without it), while the loads are in flight: positions come by
+  //      scalar loads (a wave's 64 entries need at most two)
   float2* cs_tab = reinterpret_cast<float2*>(smem + TABREG);
+  const int nent = pl.tab_rows;  // block row r uses entry r % nent
   {
     const double lane_inv_freq = rope_inv_freq(tid % HALF, HD, pl.log2_base);
-    for (int i0 = 0; i0 < B * HALF; i0 += NT) {
+    for (int i0 = 0; i0 < nent * HALF; i0 += NT) {
       const int kw = __builtin_amdgcn_readfirstlane((i0 + wave * 64) / HALF);
-      const int k0 = min(kw, B - 1), k1 = min(kw + 1, B - 1);
+      const int r0 = min(kw, nent - 1), r1 = min(kw + 1, nent - 1);
+      const int k0 = r0 >= B ? r0 - B : r0, k1 = r1 >= B ? r1 - B : r1;  // r < 2B
       int p0 = plen + k0, p1 = plen + k1;
       if (pos_b) sload2(pos_b + k0, pos_b + k1, p0, p1);
+      const int64_t q0 = static_cast<int64_t>(p0) + (r0 >= B ? B : 0);
+      const int64_t q1 = static_cast<int64_t>(p1) + (r1 >= B ? B : 0);
       const int i = i0 + tid;
-      if (i < B * HALF) cs_tab[i] = rope_cos_sin(i / HALF == kw ? p0 : p1, lane_inv_freq);
+      if (i < nent * HALF) cs_tab[i] = rope_cos_sin(i / HALF == kw ? q0 : q1, lane_inv_freq);
     }
   }
 
@@ -443,7 +448,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     uint4* px = reinterpret_cast<uint4*>(qrow + ((j ^ (lr & (L::GR - 1))) << 4));
     uint4* py = reinterpret_cast<uint4*>(qrow + (((j + L::GR / 2) ^ (lr & (L::GR - 1))) << 4));
     const uint4 x4 = *px, y4 = *py;
-    const float4* csr = reinterpret_cast<const float4*>(cs_tab + ((mq % twoB) % B) * HALF + 8 * j);
+    const float4* csr = reinterpret_cast<const float4*>(cs_tab + ((mq % twoB) % nent) * HALF + 8 * j);
     float4 c4[4];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) c4[q4] = csr[q4];
@@ -580,7 +585,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       uint4* px = reinterpret_cast<uint4*>(Kb + swz<HD>(row, j));
       uint4* py = reinterpret_cast<uint4*>(Kb + swz<HD>(row, j + L::GR / 2));
       const uint4 x4 = *px, y4 = *py;
-      const float4* csr = reinterpret_cast<const float4*>(cs_tab + ((bt * KT + row) % B) * HALF + 8 * j);
+      const float4* csr = reinterpret_cast<const float4*>(cs_tab + ((bt * KT + row) % nent) * HALF + 8 * j);
       float4 c4[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) c4[q4] = csr[q4];
@@ -841,7 +846,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
 template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT>
 hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
   auto kern = verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT>;
-  const size_t lds = mfma_lds_bytes(HD, NSTAGE, pl.B, RW * ROWT * 16, QSEP);
+  const size_t lds = mfma_lds_bytes(HD, NSTAGE, pl.tab_rows, RW * ROWT * 16, QSEP);
   static int attr_set = 0;  // largest dynamic LDS size already allowed for this instantiation
   if (static_cast<int>(lds) > attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -874,10 +879,10 @@ hipError_t launch_stages(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
 
 // Dynamic LDS of one workgroup: the tile ring, stage labels and positions,
 // the staged query rows when they have their own region, the RoPE table.
-size_t mfma_lds_bytes(int hd, int nstage, int B, int rows_wg, bool qsep) {
+size_t mfma_lds_bytes(int hd, int nstage, int tab_rows, int rows_wg, bool qsep) {
   const size_t ring = static_cast<size_t>(nstage) * 2 * KT * hd * 2;
   return ring + 512 + (qsep ? static_cast<size_t>(rows_wg) * hd * 2 : 0) +
-         static_cast<size_t>(B) * (hd / 2) * sizeof(float2);
+         static_cast<size_t>(tab_rows) * (hd / 2) * sizeof(float2);
 }
 
 hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s) {

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void verify_valu_kernel(Plan pl, VerifyArgs a)
   uint64_t dbits = 0, mbits = 0;
   if (row_ok) {
     const T* qp = static_cast<const T*>(a.q_blk) + orow * HD;
-    const int pos = block_pos(pos_b, plen, r % B);
+    const int64_t pos = block_row_pos(pos_b, plen, r, B, pl.rope_seq != 0);
 #pragma unroll
     for (int e = 0; e < NE / 2; ++e) {
       const int f = l16 + 16 * e;
@@ -135,7 +135,9 @@ __global__ __launch_bounds__(256) void verify_valu_kernel(Plan pl, VerifyArgs a)
           const T* kp = static_cast<const T*>(a.k_blk) +
                         ((static_cast<size_t>(b) * twoB + c) * pl.Hkv + kvh) * HD;
           rope_apply(Elem<T>::load(kp, f), Elem<T>::load(kp, f + HALF),
-                     rope_cos_sin(block_pos(pos_b, plen, c % B), rope_inv_freq(f, HD, pl.log2_base)), xo, yo);
+                     rope_cos_sin(block_row_pos(pos_b, plen, c, B, pl.rope_seq != 0),
+                                  rope_inv_freq(f, HD, pl.log2_base)),
+                     xo, yo);
         }
         Ks[key][f] = xo;
         Ks[key][f + HALF] = yo;

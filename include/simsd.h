@@ -11,7 +11,8 @@
  *     response position a stage tau in 1..B; D~_i attends to D_j only when
  *     tau(j) < tau(i) and to D~_j when tau(j) >= tau(i);
  *   - section 3, position encoding alignment: D~_k reuses the RoPE index of
- *     D_k;
+ *     D_k (the "RoPE copy"; "Experimental results" reports the ablation that
+ *     drops it, available here as SIMSD_ROPE_SEQUENTIAL);
  *   - section 4, pipeline: one target forward computes the logits of all
  *     candidates under that mask; acceptance is standard rejection sampling
  *     walked in the drafted temporal order, committing the longest accepted
@@ -57,7 +58,7 @@ extern "C" {
 #define SIMSD_ERR_NULL        (-1) /* a required pointer is NULL */
 #define SIMSD_ERR_SHAPE       (-2) /* negative size, Hq % Hkv != 0, head_dim not 64/128, B > 64;
                                        bf16: Hkv or batch x ceil(Hq/Hkv*2B/128) above 65535 */
-#define SIMSD_ERR_DTYPE       (-3) /* unknown dtype, mask mode or implementation */
+#define SIMSD_ERR_DTYPE       (-3) /* unknown dtype, mask mode, RoPE mode or implementation */
 #define SIMSD_ERR_WORKSPACE   (-4) /* workspace NULL or smaller than the query says */
 #define SIMSD_ERR_GAMMA       (-5) /* gamma outside [0, B] */
 #define SIMSD_ERR_ALIGN       (-6) /* pointer not aligned as documented */
@@ -82,6 +83,17 @@ typedef enum { SIMSD_MASK_TEMPORAL = 0, SIMSD_MASK_FULL = 1 } simsd_mask_mode;
  * fp32.  VALU works for both dtypes (it is the fp32 path and a cross-check). */
 typedef enum { SIMSD_IMPL_AUTO = 0, SIMSD_IMPL_VALU = 1, SIMSD_IMPL_MFMA = 2 } simsd_impl;
 
+/* RoPE index of the mask slots.  COPY is the method (section 3): D~_k
+ * takes the index of D_k.  SEQUENTIAL is the ablation without the copy
+ * ("Experimental results"), read here as the 2B block rows taking
+ * consecutive indices in layout order: D~_k at pos(D_k) + B (by default
+ * D_k at P_b + k and D~_k at P_b + B + k).  The MFMA kernel keeps a RoPE
+ * table of one entry per distinct block position in LDS; at head_dim 128
+ * and B > 32 the SEQUENTIAL table does not fit beside a 3-stage ring, and
+ * AUTO then runs the VALU kernel (an explicit MFMA request is
+ * SIMSD_ERR_SHAPE). */
+typedef enum { SIMSD_ROPE_COPY = 0, SIMSD_ROPE_SEQUENTIAL = 1 } simsd_rope_mode;
+
 typedef struct {
   int32_t batch;        /* NB >= 0 */
   int32_t n_q_heads;    /* Hq >= 1 */
@@ -95,6 +107,7 @@ typedef struct {
   int32_t kv_chunk;     /* prompt keys per split, multiple of 64; 0 = library picks */
   double rope_base;     /* RoPE base, > 0 (1e4, 1e6, ...) */
   float softmax_scale;  /* 0 => 1/sqrt(d) */
+  int32_t rope_mode;    /* simsd_rope_mode */
 } simsd_verify_desc;
 
 /* Workspace bytes that simsd_verify_attn needs for `desc` (may be 0).
@@ -115,7 +128,8 @@ int simsd_verify_attn_workspace(const simsd_verify_desc* desc, size_t* bytes);
  *  tau     [NB][B] int32 stage labels 1..B (a permutation; ties are
  *                            tolerated: the mask rules stay well defined).
  *  pos_d   [NB][B] int32 RoPE position of D_k, or NULL meaning P_b + k;
- *                            D~_k always takes the same position.
+ *                            D~_k takes the same position (COPY) or that
+ *                            position + B (SEQUENTIAL).
  *  out     [NB][2B][Hq][d]   softmax-weighted values, in `dtype`.
  *  lse     [NB][2B][Hq] fp32 natural-log sum of exp of the scaled scores over
  *                            the visible set, or NULL.
@@ -238,7 +252,7 @@ int simsd_debug_rope(const simsd_verify_desc* desc, const void* q_blk, const voi
 /* Human-readable text for a return code (static storage). */
 const char* simsd_strerror(int code);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int simsd_abi_version(void);
 
 #ifdef __cplusplus

@@ -23,7 +23,7 @@ def gpu_inputs(w, seed, NB=None, P=None, on_device=False):
     return {k: v.to(dev()) for k, v in t.items()}
 
 
-def oracle_for(t, w, b_idx=None, pos_d=None, mask_mode=0, scale=None):
+def oracle_for(t, w, b_idx=None, pos_d=None, mask_mode=0, scale=None, rope_mode=0):
     """Oracle output for the sequences b_idx (all when None), from the same tensors."""
     sel = slice(None) if b_idx is None else list(b_idx)
     np64 = lambda x: synth.to_numpy64(x[sel])
@@ -31,7 +31,7 @@ def oracle_for(t, w, b_idx=None, pos_d=None, mask_mode=0, scale=None):
         np64(t["q_blk"]), np64(t["k_blk"]), np64(t["v_blk"]), np64(t["k_cache"]), np64(t["v_cache"]),
         t["prompt_len"][sel].cpu().numpy(), t["tau"][sel].cpu().numpy(),
         pos_d=None if pos_d is None else pos_d[sel].cpu().numpy(),
-        rope_base=w.rope_base, scale=scale, mask_mode=mask_mode)
+        rope_base=w.rope_base, scale=scale, mask_mode=mask_mode, rope_mode=rope_mode)
     return out, lse, st
 
 

@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.simsd_abi_version() == 1
+    assert lib.simsd_abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert lib.simsd_strerror(code)
     assert lib.simsd_strerror(-99) == b"unknown error code"
@@ -57,7 +57,8 @@ def test_abi_version_and_strerror(lib):
 
 def _desc(**kw):
     base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, B=4, p_max=256, dtype=L.BF16,
-                mask_mode=L.MASK_TEMPORAL, impl=L.IMPL_AUTO, kv_chunk=0, rope_base=1e6, softmax_scale=0.0)
+                mask_mode=L.MASK_TEMPORAL, impl=L.IMPL_AUTO, kv_chunk=0, rope_base=1e6, softmax_scale=0.0,
+                rope_mode=L.ROPE_COPY)
     base.update(kw)
     return L.VerifyDesc(*[base[f] for f, _ in L.VerifyDesc._fields_])
 
@@ -82,11 +83,31 @@ def _ws(lib, **kw):
     (dict(mask_mode=2), L.ERR_DTYPE),
     (dict(impl=3), L.ERR_DTYPE),
     (dict(impl=L.IMPL_MFMA, dtype=L.F32), L.ERR_DTYPE),
+    (dict(rope_mode=2), L.ERR_DTYPE),
+    (dict(rope_mode=-1), L.ERR_DTYPE),
+    # without the RoPE copy the MFMA kernel's table of 2B = 128 positions does
+    # not fit beside its ring at head dim 128
+    (dict(impl=L.IMPL_MFMA, rope_mode=L.ROPE_SEQUENTIAL, B=64), L.ERR_SHAPE),
     (dict(kv_chunk=100), L.ERR_KV_CHUNK),
     (dict(kv_chunk=-64), L.ERR_KV_CHUNK),
 ])
 def test_workspace_query_rejects(lib, kw, code):
     assert _ws(lib, **kw)[0] == code
+
+
+def test_descriptor_layout():
+    # int32 x 10, double, float, int32: the C struct is 56 bytes with the
+    # double at offset 40
+    assert ctypes.sizeof(L.VerifyDesc) == 56
+    assert L.VerifyDesc.rope_base.offset == 40
+    assert L.VerifyDesc.rope_mode.offset == 52
+
+
+def test_sequential_positions_plan(lib):
+    # AUTO still plans the cases the MFMA table cannot hold (on the VALU kernel)
+    assert _ws(lib, rope_mode=L.ROPE_SEQUENTIAL, B=64)[0] == 0
+    assert _ws(lib, rope_mode=L.ROPE_SEQUENTIAL, B=32, impl=L.IMPL_MFMA)[0] == 0
+    assert _ws(lib, rope_mode=L.ROPE_SEQUENTIAL, B=64, head_dim=64, impl=L.IMPL_MFMA)[0] == 0
 
 
 def test_workspace_query_sizes(lib):

@@ -47,16 +47,19 @@ def test_mask_bits_exact(B, ties):
 
 @pytest.mark.parametrize("dtype,d,base", [(torch.float32, 64, 1e4), (torch.float32, 128, 1e6),
                                           (torch.bfloat16, 128, 1e6), (torch.bfloat16, 64, 1e4)])
-def test_rope_copy_rows(dtype, d, base):
+@pytest.mark.parametrize("seq", [False, True])
+def test_rope_copy_rows(dtype, d, base, seq):
     g = torch.Generator().manual_seed(d)
     NB, B, Hq, Hkv = 3, 8, 8, 2
     q = (torch.randn(NB, 2 * B, Hq, d, generator=g) * 0.5).to(dtype)
     k = (torch.randn(NB, 2 * B, Hkv, d, generator=g) * 0.5).to(dtype)
     plen = torch.tensor([0, 4000, 16370], dtype=torch.int32)
     pos_d = None
-    qr, kr = sd.debug_rope(q.to(dev()), k.to(dev()), plen.to(dev()), pos_d, rope_base=base, p_max=16384)
+    qr, kr = sd.debug_rope(q.to(dev()), k.to(dev()), plen.to(dev()), pos_d, rope_base=base, p_max=16384,
+                           rope_mode=sd.ROPE_SEQUENTIAL if seq else sd.ROPE_COPY)
     pos = (plen[:, None].long() + torch.arange(B)).numpy()
-    rows = np.concatenate([pos, pos], axis=1)              # D~_k takes D_k's position
+    # D~_k takes D_k's position, or B past it without the RoPE copy
+    rows = np.concatenate([pos, pos + B if seq else pos], axis=1)
     q64 = rope_rotate(q.float().double().numpy(), rows[:, :, None], base)
     k64 = rope_rotate(k.float().double().numpy(), rows[:, :, None], base)
     for got, want in ((qr, q64), (kr, k64)):

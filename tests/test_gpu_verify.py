@@ -35,11 +35,11 @@ def _run(t, w, **kw):
     return out, lse, st
 
 
-def _check(t, w, label, impl=0, kv_chunk=0, pos_d=None, mask_mode=0, b_idx=None):
+def _check(t, w, label, impl=0, kv_chunk=0, pos_d=None, mask_mode=0, b_idx=None, rope_mode=0):
     print(f"case {label}: NB={t['q_blk'].shape[0]} Hq={w.Hq} Hkv={w.Hkv} d={w.d} P={t['k_cache'].shape[2]} "
-          f"B={w.B} {w.dtype} impl={impl} kv_chunk={kv_chunk}", flush=True)
-    out, lse, st = _run(t, w, impl=impl, kv_chunk=kv_chunk, pos_d=pos_d, mask_mode=mask_mode)
-    ref, ref_lse, ref_st = oracle_for(t, w, b_idx=b_idx, pos_d=pos_d, mask_mode=mask_mode)
+          f"B={w.B} {w.dtype} impl={impl} kv_chunk={kv_chunk} rope_mode={rope_mode}", flush=True)
+    out, lse, st = _run(t, w, impl=impl, kv_chunk=kv_chunk, pos_d=pos_d, mask_mode=mask_mode, rope_mode=rope_mode)
+    ref, ref_lse, ref_st = oracle_for(t, w, b_idx=b_idx, pos_d=pos_d, mask_mode=mask_mode, rope_mode=rope_mode)
     sel = slice(None) if b_idx is None else list(b_idx)
     assert np.array_equal(st[sel].cpu().numpy(), ref_st)
     compare(out[sel], ref, w.dtype, label)
@@ -129,6 +129,45 @@ def test_custom_positions_and_full_mode(impl):
     pos_d = torch.stack([torch.randperm(6, generator=g) * 3 + 1000 for _ in range(3)]).to(torch.int32).to(dev())
     _check(t, w, "pos_d", impl=impl, pos_d=pos_d)
     _check(t, w, "full mode", impl=impl, mask_mode=sd.MASK_FULL)
+
+
+# Without the RoPE copy (the ablation): D~_k at pos(D_k) + B.  Block-dominated
+# prompts (P = 0, 17) make a wrong position visible; B = 32 at d = 128 runs
+# the MFMA kernel with its 2B-entry table beside a 3-stage ring, B = 64 at
+# d = 64 a table of 128 entries.
+SEQ = [
+    ("p0_b8", dict(NB=3, Hq=8, Hkv=2, P=0, p_lo=0, B=8)),
+    ("p17_b6", dict(NB=3, Hq=8, Hkv=2, P=17, p_lo=0, B=6)),
+    ("p300_b16", dict(NB=2, Hq=8, Hkv=2, P=300, B=16)),
+    ("p200_b32", dict(NB=2, Hq=4, Hkv=2, P=200, B=32)),
+    ("d64_b64", dict(NB=2, Hq=4, Hkv=1, d=64, P=150, B=64)),
+]
+
+
+@pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
+@pytest.mark.parametrize("label,ov", SEQ, ids=[s[0] for s in SEQ])
+def test_without_rope_copy(label, ov, impl):
+    w = _w(**ov)
+    t = gpu_inputs(w, 91 + len(label))
+    _check(t, w, f"seq {label} impl={impl}", impl=impl, rope_mode=sd.ROPE_SEQUENTIAL)
+    if label == "p17_b6":
+        g = torch.Generator().manual_seed(9)
+        pos_d = torch.stack([torch.randperm(w.B, generator=g) * 5 + 77 for _ in range(w.NB)])
+        _check(t, w, f"seq pos_d impl={impl}", impl=impl, rope_mode=sd.ROPE_SEQUENTIAL,
+               pos_d=pos_d.to(torch.int32).to(dev()))
+
+
+def test_without_rope_copy_fp32_and_wide_block():
+    # fp32 at 1e-5 on a block-dominated case (VALU kernel)
+    w = _w(NB=2, Hq=4, Hkv=2, d=128, P=17, p_lo=0, B=8, dtype=torch.float32)
+    _check(gpu_inputs(w, 95), w, "seq fp32", rope_mode=sd.ROPE_SEQUENTIAL)
+    # d = 128, B = 64: the table of 128 positions does not fit beside the MFMA
+    # ring, so AUTO runs the VALU kernel and an explicit MFMA request is refused
+    w = _w(NB=1, Hq=4, Hkv=1, P=100, B=64)
+    t = gpu_inputs(w, 96)
+    _check(t, w, "seq b64 auto", rope_mode=sd.ROPE_SEQUENTIAL)
+    with pytest.raises(sd.SimsdError):
+        _run(t, w, impl=sd.IMPL_MFMA, rope_mode=sd.ROPE_SEQUENTIAL)
 
 
 @pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
