@@ -170,6 +170,32 @@ def test_without_rope_copy_fp32_and_wide_block():
         _run(t, w, impl=sd.IMPL_MFMA, rope_mode=sd.ROPE_SEQUENTIAL)
 
 
+# Stage labels with ties: several positions committed at one step (threshold
+# decoding), all positions at stage 1 (a plain bidirectional block step over
+# the mask slots), and random repeats.  The mask rules stay defined and the
+# oracle applies them literally.
+def _tied_tau(kind, NB, B, g):
+    if kind == "all1":
+        return torch.ones(NB, B, dtype=torch.int32)
+    if kind == "steps":
+        base = torch.arange(B) // 3 + 1  # 1,1,1,2,2,2,...
+        return torch.stack([base[torch.randperm(B, generator=g)] for _ in range(NB)]).to(torch.int32)
+    return torch.randint(1, B + 1, (NB, B), generator=g, dtype=torch.int32)
+
+
+@pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
+@pytest.mark.parametrize("kind", ["all1", "steps", "random"])
+@pytest.mark.parametrize("B,P", [(4, 17), (8, 0), (16, 130)])
+def test_tied_stage_labels(kind, B, P, impl):
+    w = _w(NB=3, Hq=8, Hkv=2, P=P, p_lo=0, B=B)
+    t = gpu_inputs(w, 101 + B + P)
+    g = torch.Generator().manual_seed(B * 31 + P)
+    t["tau"] = _tied_tau(kind, w.NB, B, g).to(dev())
+    _check(t, w, f"ties {kind} B={B} P={P} impl={impl}", impl=impl)
+    if kind == "steps":
+        _check(t, w, f"ties {kind} seq impl={impl}", impl=impl, rope_mode=sd.ROPE_SEQUENTIAL)
+
+
 @pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
 def test_faulted_sequences(impl):
     w = _w(NB=4, Hq=8, Hkv=2, P=80, B=4)
