@@ -222,12 +222,12 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   static_assert(ROWT == 1 || ROWT == 2, "row tiles per wave");
   static_assert((KSPLIT - 1) * ROWS * XSTR * 4 <= 2 * NSTAGE * L::TILEB, "exchange buffer fits the ring");
   static_assert(NT % HALF == 0, "each lane keeps one RoPE frequency");
-  // Probabilities are taken relative to a per-row reference fixed at the
-  // row's first tile with a visible key (no rescaling of the accumulators
-  // inside the loop).  A row whose probabilities could reach past this bound
-  // (log2 units) makes the workgroup run its keys a second time with the
-  // exact row maximum as the reference.
-  constexpr float kRefSlack = 64.0f;
+  // Probabilities are taken relative to a per-row reference set at the
+  // row's first tile with a visible key.  It is raised (and the
+  // accumulators rescaled) only when a later score passes it by more than
+  // this many log2 units, so probabilities stay below 2^kRaise and the
+  // rescale is rare.
+  constexpr float kRaise = 16.0f;
 
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -513,14 +513,12 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
 
   // ---- online-softmax state of this wave's share of the keys, per row tile
   float mref[ROWT], lpart[ROWT];  // reference (log2 units, -inf until set), partial sum
-  float lmax[ROWT];               // this lane's largest raw score so far
   const float scale = pl.scale_log2;
   f32x4 acc[ROWT][DTILES];
 #pragma unroll
   for (int rt = 0; rt < ROWT; ++rt) {
     mref[rt] = -INFINITY;
     lpart[rt] = 0.0f;
-    lmax[rt] = -INFINITY;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) acc[rt][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
@@ -622,11 +620,21 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
           tmax = fmaxf(tmax, x);
         }
       }
-      lmax[rt] = fmaxf(lmax[rt], tmax);
-      if (__any(mref[rt] == -INFINITY)) {  // first tile with a visible key for some row of this wave
+      // a row's first visible key sets its reference; a score more than
+      // kRaise above it raises it.  The four lanes of a row reduce the same
+      // maximum, so they take the same decision.
+      const bool need = mref[rt] == -INFINITY ? tmax != -INFINITY : tmax * scale > mref[rt] + kRaise;
+      if (__any(need)) {
         float rmax = fmaxf(tmax, __shfl_xor(tmax, 16));
         rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-        if (mref[rt] == -INFINITY) mref[rt] = rmax * scale;  // stays -inf while the row sees nothing
+        const float nref = rmax * scale;
+        if (mref[rt] == -INFINITY ? nref != -INFINITY : nref > mref[rt] + kRaise) {
+          const float f = mref[rt] == -INFINITY ? 0.0f : exp2f(mref[rt] - nref);
+          lpart[rt] *= f;
+#pragma unroll
+          for (int dt = 0; dt < DTILES; ++dt) acc[rt][dt] = acc[rt][dt] * f;
+          mref[rt] = nref;
+        }
       }
       const float muse = (mref[rt] == -INFINITY) ? 0.0f : mref[rt];
       float pv[NSUB][4];
@@ -669,9 +677,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   // Scores of the next tile: the softmax of tile t reads them before the
   // score MFMAs of tile t+1 overwrite them, so one buffer serves.
   f32x4 sb[ROWT][NSUB];
-  int* pass_flag = reinterpret_cast<int*>(smem + S::TPREG + 512 - 4);  // after the positions
   const int nfull = (c1 - c0) / KT;  // whole prompt tiles: nbt .. nbt + nfull - 1
-  for (int pass = 0;; ++pass) {
   if (T >= NSTAGE)
     lds_barrier<(NSTAGE - 1) * LPW>();  // tile 0 landed
   else
@@ -730,39 +736,6 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   int t0 = nbt;
   for (; t0 < nbt + nfull; ++t0) step(IC<0>{}, t0);
   for (; t0 < T; ++t0) step(IC<1>{}, t0);
-
-  // ---- a second pass when some row's probabilities may have grown past
-  //      2^kRefSlack (or the sums are not finite): the exact row maximum
-  //      over this wave's keys becomes the reference
-  float rowmax[ROWT];
-  bool bad = false;
-#pragma unroll
-  for (int rt = 0; rt < ROWT; ++rt) {
-    rowmax[rt] = fmaxf(lmax[rt], __shfl_xor(lmax[rt], 16));
-    rowmax[rt] = fmaxf(rowmax[rt], __shfl_xor(rowmax[rt], 32));
-    bad |= !(lpart[rt] <= 0x1p60f);  // a lane's share; also catches NaN
-#pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bad |= !__builtin_isfinite(acc[rt][dt][j]);
-    bad |= mref[rt] != -INFINITY && rowmax[rt] * scale > mref[rt] + kRefSlack;
-  }
-  if (pass > 0) break;
-  wait_counts<0, 15>();
-  if (tid == 0) *pass_flag = 0;
-  lds_barrier<0>();
-  if (__any(bad) && lane == 0) *pass_flag = 1;
-  lds_barrier<0>();
-  if (*pass_flag == 0) break;
-#pragma unroll
-  for (int rt = 0; rt < ROWT; ++rt) {
-    mref[rt] = rowmax[rt] == -INFINITY ? -INFINITY : rowmax[rt] * scale;
-    lpart[rt] = 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) acc[rt][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  issue_range(0, min(NSTAGE, T), c1);
-  }
 
   // ---- combine the key splits of each row (through the drained ring)
   wait_counts<0, 15>();  // no ring load may land after the workgroup ends

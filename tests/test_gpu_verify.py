@@ -246,6 +246,23 @@ def test_late_keys_far_above_the_first_tiles(impl, big):
         assert torch.isfinite(out).all() and torch.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
+def test_scores_rising_in_steps_across_tiles(impl):
+    # keys whose scores climb tile after tile, each step a few tens of log2
+    # units: the row's reference has to move up several times within one
+    # split, and the rows of the wider block (128 rows per workgroup) too
+    for B, Hq in ((4, 8), (16, 8)):
+        w = _w(NB=2, Hq=Hq, Hkv=2, P=900, p_lo=800, B=B)
+        t = gpu_inputs(w, 111 + B)
+        for i in range(1, 9):
+            t["k_cache"][:, :, 100 * i + 7] = 1.5 * i
+        pos_d = torch.zeros((2, B), dtype=torch.int32, device=dev())
+        for kv_chunk in (0, 320):
+            out, lse, _ = _check(t, w, f"rising keys B={B} chunk={kv_chunk}", impl=impl, kv_chunk=kv_chunk,
+                                 pos_d=pos_d)
+            assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+
+
 def test_mask_mistake_is_visible_in_block_dominated_case():
     # With no prompt the block mask decides the result: the kernel must sit far
     # closer to the temporal-mask oracle than to the all-visible one.
