@@ -118,8 +118,8 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   pl.nsplit = static_cast<int>(nsplit);
   const int64_t grid = nsplit * pl.nrg * static_cast<int64_t>(pl.NB) * pl.Hkv;
   if (grid > 0x7fffffffLL) return SIMSD_ERR_SHAPE;
-  // the MFMA kernel's grid is (nsplit, Hkv, NB * nrg): y and z stay below 2^16
-  if (pl.impl == SIMSD_IMPL_MFMA && (pl.Hkv > 65535 || static_cast<int64_t>(pl.NB) * pl.nrg > 65535))
+  // the MFMA kernel's grid is (Hkv, NB * nrg, nsplit): y and z stay below 2^16
+  if (pl.impl == SIMSD_IMPL_MFMA && (pl.nsplit > 65535 || static_cast<int64_t>(pl.NB) * pl.nrg > 65535))
     return SIMSD_ERR_SHAPE;
   if (pl.nsplit > 1) {
     pl.part_o_floats = static_cast<size_t>(pl.NB) * pl.Hkv * pl.nsplit * pl.M * pl.d;

@@ -239,14 +239,16 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const int rw = wave % RW;  // row wave: rows (rw*ROWT + rt)*16 .. +15 of the row group, rt < ROWT
   const int ks = wave / RW;  // key split: keys [ks*64/KSPLIT, (ks+1)*64/KSPLIT) of every tile
 
-  // Workgroup -> (split, KV head, sequence and row group) straight from the
-  // 3-D grid (no integer division on the way to the first loads).  The
-  // hardware hands consecutive workgroups (x fastest) to consecutive XCDs, so
-  // with nsplit*Hkv a multiple of 8 the row groups of one K/V stream share an
-  // XCD and the later ones find its tiles in that XCD's L2.
-  const int s = blockIdx.x;
-  const int kvh = blockIdx.y;
-  int b = blockIdx.z, rg = 0;
+  // Workgroup -> (KV head, sequence and row group, split) straight from the
+  // 3-D grid.  The hardware hands consecutive workgroups (x fastest) to
+  // consecutive XCDs, so with Hkv a multiple of 8 XCD j streams KV head j of
+  // every sequence and every split: the same work on every XCD whatever the
+  // prompt lengths.  The row groups of one K/V stream share an XCD and run
+  // side by side, the later ones finding its tiles in that XCD's L2, and
+  // the splits go out in order, so the ragged last splits come last.
+  const int kvh = blockIdx.x;
+  int b = blockIdx.y, rg = 0;
+  const int s = blockIdx.z;
   if (pl.nrg > 1) {
     rg = b % pl.nrg;
     b /= pl.nrg;
@@ -827,8 +829,8 @@ hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = static_cast<int>(lds);
   }
-  const dim3 grid(static_cast<unsigned>(pl.nsplit), static_cast<unsigned>(pl.Hkv),
-                  static_cast<unsigned>(pl.NB) * static_cast<unsigned>(pl.nrg));
+  const dim3 grid(static_cast<unsigned>(pl.Hkv), static_cast<unsigned>(pl.NB) * static_cast<unsigned>(pl.nrg),
+                  static_cast<unsigned>(pl.nsplit));
   hipLaunchKernelGGL(kern, grid, dim3(RW * KSPLIT * 64), lds, s, pl, a);
   return hipGetLastError();
 }

@@ -57,7 +57,8 @@ extern "C" {
 #define SIMSD_OK               0
 #define SIMSD_ERR_NULL        (-1) /* a required pointer is NULL */
 #define SIMSD_ERR_SHAPE       (-2) /* negative size, Hq % Hkv != 0, head_dim not 64/128, B > 64;
-                                       bf16: Hkv or batch x ceil(Hq/Hkv*2B/128) above 65535 */
+                                       bf16: prompt splits or batch x ceil(Hq/Hkv*2B/128)
+                                       above 65535 */
 #define SIMSD_ERR_DTYPE       (-3) /* unknown dtype, mask mode, RoPE mode or implementation */
 #define SIMSD_ERR_WORKSPACE   (-4) /* workspace NULL or smaller than the query says */
 #define SIMSD_ERR_GAMMA       (-5) /* gamma outside [0, B] */

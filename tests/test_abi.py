@@ -95,6 +95,20 @@ def test_workspace_query_rejects(lib, kw, code):
     assert _ws(lib, **kw)[0] == code
 
 
+def test_mfma_grid_limits(lib):
+    # the MFMA grid is (Hkv, batch x row groups, splits): y and z must stay below 2^16
+    assert _ws(lib, batch=65535, B=4, n_q_heads=8, n_kv_heads=2, p_max=64)[0] == 0
+    assert _ws(lib, batch=65536, B=4, n_q_heads=8, n_kv_heads=2, p_max=64, impl=L.IMPL_MFMA)[0] == L.ERR_SHAPE
+    # 128 rows per workgroup: 8 query heads per KV head x 2B = 64 -> 512 rows, 4 row groups
+    assert _ws(lib, batch=16383, B=32, n_q_heads=8, n_kv_heads=1, p_max=64, impl=L.IMPL_MFMA)[0] == 0
+    assert _ws(lib, batch=16384, B=32, n_q_heads=8, n_kv_heads=1, p_max=64, impl=L.IMPL_MFMA)[0] == L.ERR_SHAPE
+    # splits of 64 keys: 65535 of them fit, one more does not
+    assert _ws(lib, batch=1, p_max=64 * 65535, kv_chunk=64, impl=L.IMPL_MFMA)[0] == 0
+    assert _ws(lib, batch=1, p_max=64 * 65536, kv_chunk=64, impl=L.IMPL_MFMA)[0] == L.ERR_SHAPE
+    # many KV heads are fine (x has no such limit)
+    assert _ws(lib, batch=1, n_q_heads=70000, n_kv_heads=70000, p_max=64)[0] == 0
+
+
 def test_descriptor_layout():
     # int32 x 10, double, float, int32: the C struct is 56 bytes with the
     # double at offset 40
