@@ -11,7 +11,7 @@ namespace {
 constexpr int kKeyTile = 64;        // prompt keys per tile (both kernels iterate in multiples of it)
 constexpr int kNumCUs = 256;        // MI355X compute units
 constexpr size_t kLdsPerCu = 163840;  // bytes of LDS per CU (and per workgroup at most)
-constexpr int kMaxChunk = 4096;     // default split length cap (load balance of ragged prompts)
+constexpr int kMaxChunk = 8192;     // default split length cap (tail of ragged prompts)
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -91,7 +91,8 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   // Split the prompt so that the grid fills every CU about once: one MFMA
   // workgroup per CU for head dim 128 (its LDS ring takes most of the CU),
   // two for 64; the VALU kernel aims at two per CU.  Splits are capped at
-  // kMaxChunk keys so ragged prompt lengths still spread evenly.
+  // kMaxChunk keys: the grid gives every XCD the same share of every
+  // sequence, so longer splits (fewer partials to merge) cost little tail.
   int64_t target = 2 * kNumCUs;
   if (pl.impl == SIMSD_IMPL_MFMA) {
     const size_t per_wg = mfma_lds_bytes(pl.d, pl.nstage, pl.tab_rows, pl.rows_wg, pl.qsep != 0) + 1024;
