@@ -32,6 +32,7 @@ WORKLOAD = "sdar8b_p4096_b8"
 VOCAB = 151936
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("diffusion_lm_speculative_amd/csrc/verify_mfma.hip",
+                  "diffusion_lm_speculative_amd/csrc/mfma_common.hpp",
                   "diffusion_lm_speculative_amd/csrc/simsd_common.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_mfma_sdar8b_p4096_b8_traffic.json")
 
@@ -158,6 +159,54 @@ def coupled_measure(torch, sd, synth, dev, stream, steps, warmup):
             "algorithmic_bytes": nbytes, "achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def projection_measure(torch, sd, synth, dev, stream, steps, warmup):
+    """The projections around the attention at the same layer shape (32
+    sequences x 16 block rows = 512 rows, hidden 4096, 32 query / 8 KV heads
+    of 128): the fused QKV projection (4096 -> 6144 channels) and the output
+    projection (4096 -> 4096).  Eight weight sets rotate (400 MB, more than
+    the last-level cache), as the layers of a model would; each timed block
+    is 8 back-to-back calls between two events on the launch stream.
+    """
+    M, H, Hq, Hkv, d = 512, 4096, 32, 8, 128
+    nsets = 8
+    res = {}
+    for name, N, K in (("qkv_proj", (Hq + 2 * Hkv) * d, H), ("o_proj", H, Hq * d)):
+        calls = []
+        for i in range(nsets):
+            x, w = synth.make_linear_inputs(M, K, N, seed=4000 + 10 * i + (name == "o_proj"), device=dev)
+            if name == "qkv_proj":
+                q = torch.empty((32, 16, Hq, d), dtype=torch.bfloat16, device=dev)
+                k = torch.empty((32, 16, Hkv, d), dtype=torch.bfloat16, device=dev)
+                v = torch.empty_like(k)
+                calls.append(sd.bind_qkv_proj(x.view(32, 16, H), w, Hq, Hkv, d, q, k, v, stream=stream))
+            else:
+                out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                calls.append(sd.bind_linear(x, w, out, stream=stream))
+        torch.cuda.synchronize()
+        for i in range(max(warmup, nsets)):
+            calls[i % nsets]()
+        per_call = []
+        for _ in range(max(steps // nsets, 4)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for c in calls:
+                c()
+            e1.record(stream)
+            e1.synchronize()
+            per_call.append(e0.elapsed_time(e1) / nsets)
+        per_call.sort()
+        us = sum(per_call) / len(per_call) * 1e3
+        flops = 2.0 * M * N * K
+        tflops = flops / (us * 1e-6) / 1e12
+        res[name] = {"M": M, "N": N, "K": K, "us": {"mean": us, "median": per_call[len(per_call) // 2] * 1e3},
+                     "tflops": tflops, "frac_mfma_bf16": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "weight_gbs": N * K * 2 / (us * 1e-6) / 1e9}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -259,6 +308,7 @@ def main():
     traffic = measured_traffic()
 
     coupled = coupled_measure(torch, sd, synth, dev, stream, args.steps, args.warmup)
+    projections = projection_measure(torch, sd, synth, dev, stream, args.steps, args.warmup)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -292,6 +342,7 @@ def main():
         "workspace_bytes": sd.verify_workspace_bytes(desc),
         "cpu_baseline": cpu,
         "accept_coupled": coupled,
+        "projections": projections,
     }
     print(json.dumps(rec), flush=True)
 

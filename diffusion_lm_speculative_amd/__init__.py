@@ -14,5 +14,7 @@ from ._lib import (  # noqa: F401
 )
 from .api import (  # noqa: F401
     accept_coupled, accept_coupled_workspace_bytes, accept_prefix, accept_workspace_bytes, bind_accept,
-    bind_accept_coupled, bind_verify, debug_mask, debug_rope, make_desc, verify_attn, verify_workspace_bytes,
+    bind_accept_coupled, bind_linear, bind_qkv_proj, bind_verify, debug_mask, debug_rope, linear, make_desc,
+    qkv_proj, verify_attn,
+    verify_workspace_bytes,
 )

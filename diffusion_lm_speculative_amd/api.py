@@ -189,6 +189,79 @@ def accept_prefix(p_target, q_draft, draft_tok, tau, gamma, seed, offset=0, *, n
     return n_accepted, next_token, status
 
 
+def linear(x, w, *, out=None, stream=None):
+    """y = x w^T for bf16 x [M][K] and w [N][K] (fp32 accumulation); returns y [M][N] bf16."""
+    lib = L.load()
+    _need(x, "x", torch.bfloat16)
+    M, K = x.shape
+    _need(w, "w", torch.bfloat16, None, x.device)
+    N = w.shape[0]
+    if w.dim() != 2 or w.shape[1] != K:
+        raise ValueError(f"w must be [N][{K}], got {tuple(w.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (M, N), x.device)
+    L.check(lib.simsd_linear(_ptr(x), _ptr(w), M, N, K, _ptr(out), _stream_handle(stream)), "simsd_linear")
+    return out
+
+
+def qkv_proj(x, w_qkv, Hq, Hkv, d, *, q=None, k=None, v=None, stream=None):
+    """Fused QKV projection of block hidden states x [NB][2B][H] (bf16) into
+    (q [NB][2B][Hq][d], k, v [NB][2B][Hkv][d])."""
+    lib = L.load()
+    _need(x, "x", torch.bfloat16)
+    NB, twoB, H = x.shape
+    dev = x.device
+    _need(w_qkv, "w_qkv", torch.bfloat16, ((Hq + 2 * Hkv) * d, H), dev)
+    if q is None:
+        q = torch.empty((NB, twoB, Hq, d), dtype=torch.bfloat16, device=dev)
+    if k is None:
+        k = torch.empty((NB, twoB, Hkv, d), dtype=torch.bfloat16, device=dev)
+    if v is None:
+        v = torch.empty((NB, twoB, Hkv, d), dtype=torch.bfloat16, device=dev)
+    _need(q, "q", torch.bfloat16, (NB, twoB, Hq, d), dev)
+    _need(k, "k", torch.bfloat16, (NB, twoB, Hkv, d), dev)
+    _need(v, "v", torch.bfloat16, (NB, twoB, Hkv, d), dev)
+    L.check(lib.simsd_qkv_proj(_ptr(x), _ptr(w_qkv), NB * twoB, H, Hq, Hkv, d, _ptr(q), _ptr(k), _ptr(v),
+                               _stream_handle(stream)), "simsd_qkv_proj")
+    return q, k, v
+
+
+@dataclass
+class BoundCall:
+    """A C-ABI call with every argument marshalled once (for timing loops).
+    `keep` holds the bound tensors."""
+    fn: str
+    args: tuple
+    keep: tuple = ()
+
+    def __call__(self):
+        rc = getattr(L.load(), self.fn)(*self.args)
+        if rc:
+            L.check(rc, self.fn)
+
+
+def bind_linear(x, w, out, stream=None) -> BoundCall:
+    _need(x, "x", torch.bfloat16)
+    M, K = x.shape
+    _need(w, "w", torch.bfloat16, None, x.device)
+    N = w.shape[0]
+    _need(out, "out", torch.bfloat16, (M, N), x.device)
+    return BoundCall("simsd_linear", (_ptr(x), _ptr(w), M, N, K, _ptr(out), _stream_handle(stream)), (x, w, out))
+
+
+def bind_qkv_proj(x, w_qkv, Hq, Hkv, d, q, k, v, stream=None) -> BoundCall:
+    _need(x, "x", torch.bfloat16)
+    NB, twoB, H = x.shape
+    dev = x.device
+    _need(w_qkv, "w_qkv", torch.bfloat16, ((Hq + 2 * Hkv) * d, H), dev)
+    _need(q, "q", torch.bfloat16, (NB, twoB, Hq, d), dev)
+    _need(k, "k", torch.bfloat16, (NB, twoB, Hkv, d), dev)
+    _need(v, "v", torch.bfloat16, (NB, twoB, Hkv, d), dev)
+    return BoundCall("simsd_qkv_proj", (_ptr(x), _ptr(w_qkv), NB * twoB, H, Hq, Hkv, d, _ptr(q), _ptr(k), _ptr(v),
+                                        _stream_handle(stream)), (x, w_qkv, q, k, v))
+
+
 def accept_coupled_workspace_bytes(batch, B, vocab) -> int:
     n = ctypes.c_size_t(0)
     L.check(L.load().simsd_accept_coupled_workspace(int(batch), int(B), int(vocab), ctypes.byref(n)),

@@ -149,6 +149,19 @@ size_t workspace_bytes(const Plan& pl) {
 
 using namespace simsd;
 
+namespace {
+constexpr int kLinMaxK = 1 << 24;  // per-lane 32-bit byte offsets inside a 128-row tile
+
+int linear_checks(const void* x, const void* w, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 16 || N % 16 != 0 || N > 0x7fffffff || K < 64 || K % 64 != 0 || K > kLinMaxK)
+    return SIMSD_ERR_SHAPE;
+  if ((M + 127) / 128 > 65535) return SIMSD_ERR_SHAPE;
+  if (M > 0 && (!x || !w)) return SIMSD_ERR_NULL;
+  if ((x && !aligned(x, 16)) || (w && !aligned(w, 16))) return SIMSD_ERR_ALIGN;
+  return SIMSD_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int simsd_abi_version(void) { return 2; }
@@ -282,6 +295,36 @@ int simsd_accept_coupled(const float* p_target, const float* noise_exp, const in
   if (!aligned(workspace, 256)) return SIMSD_ERR_ALIGN;
   const hipError_t e = launch_accept_coupled(p_target, noise_exp, draft_tok, tau, batch, B, gamma, vocab, n_accepted,
                                              next_token, status, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
+}
+
+int simsd_linear(const void* x, const void* w, int64_t M, int32_t N, int32_t K, void* y, void* stream) {
+  const int rc = linear_checks(x, w, M, N, K);
+  if (rc != SIMSD_OK) return rc;
+  if (M == 0) return SIMSD_OK;
+  if (!y) return SIMSD_ERR_NULL;
+  if (!aligned(y, 16)) return SIMSD_ERR_ALIGN;
+  uint16_t* out = static_cast<uint16_t*>(y);
+  const hipError_t e = launch_linear(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), M, N, K, N, N,
+                                     out, N, out, N, out, N, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
+}
+
+int simsd_qkv_proj(const void* x, const void* w_qkv, int64_t M, int32_t H, int32_t Hq, int32_t Hkv, int32_t d,
+                   void* q, void* k, void* v, void* stream) {
+  if (Hq < 1 || Hkv < 1 || d < 16 || d % 16 != 0) return SIMSD_ERR_SHAPE;
+  const int64_t nq = static_cast<int64_t>(Hq) * d, nk = static_cast<int64_t>(Hkv) * d;
+  const int64_t N = nq + 2 * nk;
+  const int rc = linear_checks(x, w_qkv, M, N, H);
+  if (rc != SIMSD_OK) return rc;
+  if (M == 0) return SIMSD_OK;
+  if (!q || !k || !v) return SIMSD_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return SIMSD_ERR_ALIGN;
+  const hipError_t e = launch_linear(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_qkv), M,
+                                     static_cast<int>(N), H, static_cast<int>(nq), static_cast<int>(nq + nk),
+                                     static_cast<uint16_t*>(q), static_cast<int>(nq), static_cast<uint16_t*>(k),
+                                     static_cast<int>(nk), static_cast<uint16_t*>(v), static_cast<int>(nk),
+                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
 }
 

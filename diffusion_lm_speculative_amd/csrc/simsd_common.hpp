@@ -200,6 +200,13 @@ __device__ __forceinline__ int valid_splits(int plen, int chunk, int nsplit) {
 hipError_t launch_verify_valu(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 size_t mfma_lds_bytes(int hd, int nstage, int tab_rows, int rows_wg, bool qsep);
+
+// y = x W^T (bf16, fp32 accumulation); output channels [0, cut1) go to
+// out0, [cut1, cut2) to out1, [cut2, N) to out2, row-major with row lengths
+// ld0..ld2.
+int linear_tile(int64_t M, int N);
+hipError_t launch_linear(const uint16_t* x, const uint16_t* w, int64_t M, int N, int K, int cut1, int cut2,
+                         uint16_t* out0, int ld0, uint16_t* out1, int ld1, uint16_t* out2, int ld2, hipStream_t s);
 hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 void accept_plan(int NB, int64_t V, int& nch, int& cpw, int& ngrp);
 int coupled_chunks(int64_t V);

@@ -127,6 +127,15 @@ def make_noise_exp(NB, B, V, seed, device="cpu"):
     return e.clamp_min_(torch.finfo(torch.float32).tiny).contiguous()
 
 
+def make_linear_inputs(M, K, N, seed, device="cpu"):
+    """x [M][K] ~ N(0, 1) and w [N][K] ~ N(0, 1/K) (the usual fan-in scale of
+    a projection), both rounded to bf16."""
+    g = _gen(device, seed)
+    x = torch.randn((M, K), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    w = torch.randn((N, K), generator=g, device=device, dtype=torch.float32).mul_(K ** -0.5).to(torch.bfloat16)
+    return x.contiguous(), w.contiguous()
+
+
 def to_numpy64(t):
     """Exact float64 copy of a float32 / bfloat16 tensor (for the oracle)."""
     return t.detach().to("cpu").to(torch.float32).double().numpy()

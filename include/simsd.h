@@ -250,6 +250,35 @@ int simsd_debug_rope(const simsd_verify_desc* desc, const void* q_blk, const voi
                      const int32_t* prompt_len, const int32_t* pos_d,
                      void* q_rot, void* k_rot, void* stream);
 
+/* ---- projections around the attention ---------------------------------------------
+ * Section 4: the target model checks every candidate in ONE forward pass over
+ * the paired layout.  Inside each layer of that pass the attention above is
+ * fed by a linear projection of the block rows' hidden states to queries,
+ * keys and values and followed by the output projection.  Both are
+ * y = x W^T (the nn.Linear convention: W is [out][in], row-major, no bias),
+ * bf16 operands, fp32 accumulation, bf16 results rounded to nearest even.
+ * RoPE is not applied here: simsd_verify_attn rotates q and k (its RoPE copy).
+ *
+ * Shapes: M >= 0 rows (M == 0 is a valid no-op); K (the input width) a
+ * multiple of 64, at most 2^24; N (the output width) a multiple of 16;
+ * ceil(M/128) <= 65535.  x, W and the outputs are 16-byte aligned device
+ * memory.  Errors: SIMSD_ERR_SHAPE, _NULL, _ALIGN, _HIP.  No workspace. */
+
+/* y [M][N] = x [M][K] * w [N][K]^T.  Used as the output projection: x is
+ * the attention output [NB*2B][Hq*d] and w is [H][Hq*d]. */
+int simsd_linear(const void* x, const void* w, int64_t M, int32_t N, int32_t K, void* y, void* stream);
+
+/* Fused QKV projection of the block rows straight into the layouts
+ * simsd_verify_attn reads.  x [M][H] holds the hidden states of the 2B block
+ * rows of every sequence in layout order (D_0..D_{B-1}, D~_0..D~_{B-1}),
+ * sequence after sequence, so M = NB*2B.  w_qkv [(Hq + 2*Hkv)*d][H]: the Hq
+ * query heads (d rows each), then the Hkv key heads, then the Hkv value
+ * heads.  Writes q [M][Hq][d], k [M][Hkv][d], v [M][Hkv][d] (that is
+ * q_blk [NB][2B][Hq][d] and k_blk, v_blk [NB][2B][Hkv][d]).  d a multiple
+ * of 16, H a multiple of 64. */
+int simsd_qkv_proj(const void* x, const void* w_qkv, int64_t M, int32_t H, int32_t Hq, int32_t Hkv, int32_t d,
+                   void* q, void* k, void* v, void* stream);
+
 /* Human-readable text for a return code (static storage). */
 const char* simsd_strerror(int code);
 

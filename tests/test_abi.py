@@ -37,7 +37,7 @@ def _declared():
 def test_header_declarations_match_binding():
     decl = _declared()
     assert decl == set(L.SIGNATURES), decl ^ set(L.SIGNATURES)
-    assert len(decl) == 10
+    assert len(decl) == 12
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -206,6 +206,34 @@ def test_accept_rejects_on_host(lib):
         assert call(**{k: A + 2}) == L.ERR_ALIGN, k
     # the residual draw (next_token != NULL) needs the workspace
     assert call(nx=A) == L.ERR_WORKSPACE
+
+
+@no_gpu_only
+def test_projections_reject_on_host(lib):
+    def lin(x=A, w=A, M=512, N=4096, K=4096, y=A):
+        return lib.simsd_linear(x, w, M, N, K, y, None)
+    assert lin(M=0, x=None, w=None, y=None) == 0
+    assert lin(M=-1) == L.ERR_SHAPE
+    assert lin(N=8) == L.ERR_SHAPE          # below 16
+    assert lin(N=4104) == L.ERR_SHAPE       # not a multiple of 16
+    assert lin(K=100) == L.ERR_SHAPE        # not a multiple of 64
+    assert lin(K=0) == L.ERR_SHAPE
+    assert lin(K=(1 << 24) + 64) == L.ERR_SHAPE
+    assert lin(M=65536 * 128) == L.ERR_SHAPE
+    for kw in ("x", "w", "y"):
+        assert lin(**{kw: None}) == L.ERR_NULL, kw
+        assert lin(**{kw: A + 8}) == L.ERR_ALIGN, kw
+
+    def qkv(x=A, w=A, M=512, H=4096, Hq=32, Hkv=8, d=128, q=A, k=A, v=A):
+        return lib.simsd_qkv_proj(x, w, M, H, Hq, Hkv, d, q, k, v, None)
+    assert qkv(M=0, x=None, w=None, q=None, k=None, v=None) == 0
+    assert qkv(d=72) == L.ERR_SHAPE
+    assert qkv(Hq=0) == L.ERR_SHAPE
+    assert qkv(Hkv=0) == L.ERR_SHAPE
+    assert qkv(H=4000) == L.ERR_SHAPE
+    for kw in ("x", "w", "q", "k", "v"):
+        assert qkv(**{kw: None}) == L.ERR_NULL, kw
+        assert qkv(**{kw: A + 4}) == L.ERR_ALIGN, kw
 
 
 @no_gpu_only

@@ -20,11 +20,12 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
-def test_every_lds_dma_load_follows_five_wait_states(tmp_path):
-    out = tmp_path / "verify_mfma.s"
+@pytest.mark.parametrize("src", ["verify_mfma.hip", "linear.hip"])
+def test_every_lds_dma_load_follows_five_wait_states(tmp_path, src):
+    out = tmp_path / (src + ".s")
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
            "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
-           "-o", str(out), os.path.join(CSRC, "verify_mfma.hip")]
+           "-o", str(out), os.path.join(CSRC, src)]
     subprocess.run(cmd, check=True, capture_output=True, timeout=600)
     lines = [l.strip() for l in out.read_text().splitlines()]
     code = [l for l in lines if l and not l.startswith((";", ".", "//")) and not l.endswith(":")]
