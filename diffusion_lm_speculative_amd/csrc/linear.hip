@@ -14,8 +14,11 @@
 //
 // Tiling.  A workgroup computes BM = 128 x rows (64 when M fits) by BN
 // output channels (BN = 64, 96 or 128, chosen so the grid covers the 256 CUs
-// in as few rounds as possible) with 4 waves in a 2 x 2 layout: each wave
-// owns BN/2 channels by BM/2 rows.  K advances in slices of 64 through a ring of NSTAGE LDS stages
+// in as few rounds as possible) with 8 waves in a 2 x 4 layout: each wave
+// owns BN/2 channels by BM/4 rows, two waves per SIMD so that one wave's
+// operand reads overlap the other's MFMAs.  A stage's 1 KiB loads are spread
+// over the waves; where they do not divide evenly the last waves issue fewer
+// (their vmcnt waits then pass at once).  K advances in slices of 64 through a ring of NSTAGE LDS stages
 // filled by direct-to-LDS loads (global_load_lds_dwordx4, 1 KiB per wave
 // instruction, no register staging); one barrier per slice.  Rows are 128
 // bytes (8 granules of 16 bytes) stored XOR-swizzled so that the 16 rows a
@@ -33,7 +36,7 @@ namespace {
 
 constexpr int kLinBK = 64;      // k per stage
 constexpr int kLinRowB = 128;   // bytes per staged row (64 bf16)
-constexpr int kLinThreads = 256;
+constexpr int kLinThreads = 512;
 constexpr int kLinStages = 4;
 constexpr size_t kLinLdsPerCu = 163840;
 
@@ -67,16 +70,15 @@ __global__ __launch_bounds__(kLinThreads) void linear_kernel(LinearArgs a) {
   constexpr int NW = kLinThreads / 64;
   constexpr int IA = BM / 8;                         // 1 KiB load instructions for the x tile
   constexpr int IW = BN / 8;                         // ... for the W tile
-  static_assert((IA + IW) % NW == 0, "stage loads split evenly over the waves");
-  constexpr int LPW = (IA + IW) / NW;                // loads per wave per stage
+  constexpr int LPW = (IA + IW + NW - 1) / NW;       // loads per wave per stage (the last waves may have fewer)
   static_assert((kLinStages - 1) * LPW <= 63, "vmcnt range");
   constexpr int TN = BN / 32;                        // 16-channel tiles per wave
-  constexpr int TM = BM / 32;                        // 16-row tiles per wave (BM/2 rows)
+  constexpr int TM = BM / (8 * NW);                  // 16-row tiles per wave
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave & 1, wm = wave >> 1;  // NW/2 row groups of BM/(NW/2) rows
   const int n0 = blockIdx.x * BN;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
   const int K = a.K;
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_kernel(LinearArgs a) {
   uint32_t loff[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
-    const int ins = wave * LPW + j;
+    const int ins = min(wave * LPW + j, IA + IW - 1);  // past the last: reloads it (harmless, see issue)
     const bool w = ins >= IA;
     const int r = (w ? ins - IA : ins) * 8 + (lane >> 3);
     const int slot = lane & 7;
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_kernel(LinearArgs a) {
     const int st = ks % kLinStages;
 #pragma unroll
     for (int j = 0; j < LPW; ++j)
-      dma16s((isw[j] ? wb : xb) + ks * kLinBK, goff[j], sbase + st * STAGEB + loff[j]);
+      if (wave * LPW + j < IA + IW) dma16s((isw[j] ? wb : xb) + ks * kLinBK, goff[j], sbase + st * STAGEB + loff[j]);
   };
 
   // Operand read offsets: W rows (MFMA A operand) n = wn*BN/2 + 16*i + l%16,
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_kernel(LinearArgs a) {
 #pragma unroll
     for (int i = 0; i < TN; ++i) aoff[i][kk] = ATILE + lin_swz(wn * (BN / 2) + 16 * i + (lane & 15), 4 * kk + (lane >> 4));
 #pragma unroll
-    for (int i = 0; i < TM; ++i) boff[i][kk] = lin_swz(wm * (BM / 2) + 16 * i + (lane & 15), 4 * kk + (lane >> 4));
+    for (int i = 0; i < TM; ++i) boff[i][kk] = lin_swz(wm * (BM * 2 / NW) + 16 * i + (lane & 15), 4 * kk + (lane >> 4));
   }
 
   f32x4 acc[TN][TM];
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_kernel(LinearArgs a) {
   // lane: channels n .. n+3 of x row m for every (i, j) tile
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
-    const int64_t m = m0 + wm * (BM / 2) + 16 * j + (lane & 15);
+    const int64_t m = m0 + wm * (BM * 2 / NW) + 16 * j + (lane & 15);
     if (m >= a.M) continue;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
