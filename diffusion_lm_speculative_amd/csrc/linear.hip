@@ -14,11 +14,14 @@
 //
 // Tiling.  A workgroup computes BM = 128 x rows (64 when M fits) by BN
 // output channels (BN = 64, 96 or 128, chosen so the grid covers the 256 CUs
-// in as few rounds as possible) with 8 waves in a 2 x 4 layout: each wave
-// owns BN/2 channels by BM/4 rows, two waves per SIMD so that one wave's
-// operand reads overlap the other's MFMAs.  A stage's 1 KiB loads are spread
-// over the waves; where they do not divide evenly the last waves issue fewer
-// (their vmcnt waits then pass at once).  K advances in slices of 64 through a ring of NSTAGE LDS stages
+// in as few rounds as possible) with 8 waves: two groups of four, one per
+// 32-k half of every 64-k slice, each group 2 x 2 waves of BN/2 channels by
+// BM/2 rows.  Two waves share a SIMD, so one wave's operand reads overlap
+// the other's MFMAs, while each wave keeps the large tile (few LDS reads per
+// MFMA); the second group's partial sums join the first's through LDS at the
+// end.  A stage's 1 KiB loads are spread over the waves; where they do not
+// divide evenly the last waves issue fewer (their vmcnt waits then pass at
+// once).  K advances in slices of 64 through a ring of NSTAGE LDS stages
 // filled by direct-to-LDS loads (global_load_lds_dwordx4, 1 KiB per wave
 // instruction, no register staging); one barrier per slice.  Rows are 128
 // bytes (8 granules of 16 bytes) stored XOR-swizzled so that the 16 rows a
@@ -73,12 +76,13 @@ __global__ __launch_bounds__(kLinThreads) void linear_kernel(LinearArgs a) {
   constexpr int LPW = (IA + IW + NW - 1) / NW;       // loads per wave per stage (the last waves may have fewer)
   static_assert((kLinStages - 1) * LPW <= 63, "vmcnt range");
   constexpr int TN = BN / 32;                        // 16-channel tiles per wave
-  constexpr int TM = BM / (8 * NW);                  // 16-row tiles per wave
+  constexpr int TM = BM / 32;                        // 16-row tiles per wave (BM/2 rows)
+  static_assert(NW == 8, "two groups of four waves, one per 32-k half of every slice");
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave & 1, wm = wave >> 1;  // NW/2 row groups of BM/(NW/2) rows
+  const int wn = wave & 1, wm = (wave >> 1) & 1, kh = wave >> 2;
   const int n0 = blockIdx.x * BN;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
   const int K = a.K;
@@ -122,14 +126,11 @@ __global__ __launch_bounds__(kLinThreads) void linear_kernel(LinearArgs a) {
 
   // Operand read offsets: W rows (MFMA A operand) n = wn*BN/2 + 16*i + l%16,
   // x rows (MFMA B operand) m = wm*BM/2 + 16*i + l%16; k granule 4*kk + l/16.
-  int aoff[TN][2], boff[TM][2];
+  int aoff[TN], boff[TM];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int i = 0; i < TN; ++i) aoff[i] = ATILE + lin_swz(wn * (BN / 2) + 16 * i + (lane & 15), 4 * kh + (lane >> 4));
 #pragma unroll
-    for (int i = 0; i < TN; ++i) aoff[i][kk] = ATILE + lin_swz(wn * (BN / 2) + 16 * i + (lane & 15), 4 * kk + (lane >> 4));
-#pragma unroll
-    for (int i = 0; i < TM; ++i) boff[i][kk] = lin_swz(wm * (BM * 2 / NW) + 16 * i + (lane & 15), 4 * kk + (lane >> 4));
-  }
+  for (int i = 0; i < TM; ++i) boff[i] = lin_swz(wm * (BM / 2) + 16 * i + (lane & 15), 4 * kh + (lane >> 4));
 
   f32x4 acc[TN][TM];
 #pragma unroll
@@ -150,25 +151,41 @@ __global__ __launch_bounds__(kLinThreads) void linear_kernel(LinearArgs a) {
       lds_barrier<0>();
     if (ks + kLinStages - 1 < nks) issue(ks + kLinStages - 1);
     const unsigned char* sb = smem + (ks % kLinStages) * STAGEB;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    {
       bf16x8 av[TN], bv[TM];
 #pragma unroll
-      for (int i = 0; i < TN; ++i) av[i] = *reinterpret_cast<const bf16x8*>(sb + aoff[i][kk]);
+      for (int i = 0; i < TN; ++i) av[i] = *reinterpret_cast<const bf16x8*>(sb + aoff[i]);
 #pragma unroll
-      for (int j = 0; j < TM; ++j) bv[j] = *reinterpret_cast<const bf16x8*>(sb + boff[j][kk]);
+      for (int j = 0; j < TM; ++j) bv[j] = *reinterpret_cast<const bf16x8*>(sb + boff[j]);
 #pragma unroll
       for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int j = 0; j < TM; ++j) acc[i][j] = mfma(av[i], bv[j], acc[i][j]);
     }
   }
-  wait_counts<0, 15>();  // nothing may land after the workgroup ends
+  // the second k half's partial sums join the first's through LDS
+  lds_barrier<0>();  // every wave is done with the ring; nothing lands after this
+  float4* xb4 = reinterpret_cast<float4*>(smem) + ((wn * 2 + wm) * TN * TM) * 64 + lane;
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) xb4[(i * TM + j) * 64] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+  }
+  lds_barrier<0>();
+  if (kh == 1) return;
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const float4 o = xb4[(i * TM + j) * 64];
+      acc[i][j] += f32x4{o.x, o.y, o.z, o.w};
+    }
 
   // lane: channels n .. n+3 of x row m for every (i, j) tile
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
-    const int64_t m = m0 + wm * (BM * 2 / NW) + 16 * j + (lane & 15);
+    const int64_t m = m0 + wm * (BM / 2) + 16 * j + (lane & 15);
     if (m >= a.M) continue;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
