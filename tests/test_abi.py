@@ -7,6 +7,8 @@ must never reach a launch, and on a machine without a GPU a launch could not
 touch memory anyway.
 """
 import ctypes
+import subprocess
+import sys
 import os
 import re
 
@@ -279,3 +281,32 @@ def test_debug_entry_points_reject_on_host(lib):
     assert lib.simsd_debug_rope(None, A, A, None, None, A, A, None) == L.ERR_NULL
     assert lib.simsd_debug_rope(ctypes.byref(d), None, A, None, None, A, A, None) == L.ERR_NULL
     assert lib.simsd_debug_rope(ctypes.byref(d), A + 8, A, None, None, A, A, None) == L.ERR_ALIGN
+
+
+def test_missing_library_raises_and_nothing_falls_back(tmp_path):
+    # a fresh interpreter: loading a library that is not there raises, and
+    # importing the package pulls in nothing from the oracle
+    code = (
+        "import sys\n"
+        "import diffusion_lm_speculative_amd as sd\n"
+        "from diffusion_lm_speculative_amd import _lib\n"
+        "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), 'oracle imported'\n"
+        "try:\n"
+        f"    _lib.load({str(tmp_path / 'absent.so')!r})\n"
+        "except RuntimeError as e:\n"
+        "    print('raised', e)\n"
+        "    sys.exit(0)\n"
+        "sys.exit(3)\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr[-2000:])
+    assert "is not built" in r.stdout
+
+
+def test_product_sources_do_not_reference_the_oracle():
+    pkg = os.path.join(ROOT, "diffusion_lm_speculative_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
