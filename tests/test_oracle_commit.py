@@ -1,0 +1,115 @@
+"""Pins of the commit-step oracle (CPU).
+
+Source: page "SimSD - Simple Speculative Decoding in Diffusion Language
+Models", section 4 (the accepted prefix is committed and the process
+repeats) and "Key contributions" item 3 (KV cache and blockwise decoding).
+The pins check hand-worked rounds, counts, permutation invariance, and that
+keys appended to the cache reproduce, under torch's float64 SDPA with RoPE
+by complex multiplication, the attention over the finished block.
+"""
+import numpy as np
+import torch
+
+from oracle.commit import append_kv_ref, block_done, commit_ref
+
+
+def test_commit_hand_example():
+    # B = 4, tau = (3, 1, 4, 2): stage 1 -> position 1, 2 -> 3, 3 -> 0, 4 -> 2
+    tau = np.array([[3, 1, 4, 2], [3, 1, 4, 2], [3, 1, 4, 2]])
+    draft = np.array([[10, 11, 12, 13]] * 3)
+    n = np.array([2, 0, -1])
+    nxt = np.array([99, 7, 5])
+    c0 = np.zeros(3, dtype=np.uint64)
+    t0 = np.full((3, 4), -1, dtype=np.int32)
+    c, t = commit_ref(tau, draft, n, nxt, c0, t0)
+    # sequence 0: stages 1, 2 keep drafts at positions 1, 3; stage 3 (position 0) takes 99
+    assert t[0].tolist() == [99, 11, -1, 13] and int(c[0]) == 0b1011
+    # sequence 1: nothing accepted; stage 1 (position 1) takes 7
+    assert t[1].tolist() == [-1, 7, -1, -1] and int(c[1]) == 0b0010
+    # sequence 2: faulted round, unchanged
+    assert t[2].tolist() == [-1, -1, -1, -1] and int(c[2]) == 0
+
+
+def test_commit_counts_and_full_acceptance():
+    rng = np.random.default_rng(4)
+    NB, B = 50, 8
+    tau = np.stack([rng.permutation(B) + 1 for _ in range(NB)])
+    draft = rng.integers(0, 1000, size=(NB, B))
+    n = rng.integers(0, B + 1, size=NB)
+    nxt = np.where(n < B, rng.integers(0, 1000, size=NB), -1)
+    c, t = commit_ref(tau, draft, n, nxt, np.zeros(NB, dtype=np.uint64), np.full((NB, B), -1))
+    for b in range(NB):
+        want = int(n[b]) + (1 if nxt[b] >= 0 else 0)
+        assert bin(int(c[b])).count("1") == want
+        assert (t[b] >= 0).sum() == want
+    full = block_done(c, B)
+    assert all(full[b] == (n[b] + (nxt[b] >= 0) == B) for b in range(NB))
+
+
+def test_commit_joint_permutation_invariance():
+    rng = np.random.default_rng(6)
+    NB, B = 20, 6
+    tau = np.stack([rng.permutation(B) + 1 for _ in range(NB)])
+    draft = rng.integers(0, 50, size=(NB, B))
+    n = rng.integers(0, B, size=NB)
+    nxt = rng.integers(0, 50, size=NB)
+    c, t = commit_ref(tau, draft, n, nxt, np.zeros(NB, dtype=np.uint64), np.full((NB, B), -1))
+    perm = rng.permutation(B)
+    c2, t2 = commit_ref(tau[:, perm], draft[:, perm], n, nxt, np.zeros(NB, dtype=np.uint64), np.full((NB, B), -1))
+    np.testing.assert_array_equal(t2, t[:, perm])
+    for b in range(NB):
+        bits = [(int(c[b]) >> k) & 1 for k in range(B)]
+        bits2 = [(int(c2[b]) >> k) & 1 for k in range(B)]
+        assert bits2 == [bits[p] for p in perm]
+
+
+def _rope_complex(x, pos, base):
+    d = x.shape[-1]
+    z = x[..., : d // 2] + 1j * x[..., d // 2:]
+    zr = z * np.exp(1j * np.asarray(pos, dtype=np.float64)[..., None] * base ** (-np.arange(0, d, 2) / d))
+    return np.concatenate([zr.real, zr.imag], axis=-1)
+
+
+def test_appended_block_acts_as_prompt():
+    # After the append, a query at position P + B attends over the cached
+    # prefix, block included, exactly as over the prompt keys followed by the
+    # block's keys rotated at P .. P + B - 1 (torch SDPA, complex RoPE).
+    rng = np.random.default_rng(8)
+    NB, B, Hkv, d, p_max, base = 2, 4, 2, 16, 40, 1e4
+    P = np.array([10, 23])
+    k_blk = rng.standard_normal((NB, 2 * B, Hkv, d))
+    v_blk = rng.standard_normal((NB, 2 * B, Hkv, d))
+    kc = rng.standard_normal((NB, Hkv, p_max, d))
+    vc = rng.standard_normal((NB, Hkv, p_max, d))
+    full = np.full(NB, (1 << B) - 1, dtype=np.uint64)
+    kc2, vc2, plen2, st = append_kv_ref(k_blk, v_blk, None, full, P, kc, vc, base)
+    assert (st == 0).all() and plen2.tolist() == (P + B).tolist()
+    for b in range(NB):
+        q = rng.standard_normal((1, d))
+        qh = _rope_complex(q, np.array([P[b] + B]), base)
+        for h in range(Hkv):
+            keys = np.concatenate([kc[b, h, :P[b]], _rope_complex(k_blk[b, :B, h], P[b] + np.arange(B), base)])
+            vals = np.concatenate([vc[b, h, :P[b]], v_blk[b, :B, h]])
+            tq = lambda a: torch.from_numpy(np.ascontiguousarray(a))[None, None]
+            want = torch.nn.functional.scaled_dot_product_attention(tq(qh), tq(keys), tq(vals))[0, 0].numpy()
+            got = torch.nn.functional.scaled_dot_product_attention(
+                tq(qh), tq(kc2[b, h, :plen2[b]]), tq(vc2[b, h, :plen2[b]]))[0, 0].numpy()
+            np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+        # rows past the block are untouched
+        np.testing.assert_array_equal(kc2[b, :, plen2[b]:], kc[b, :, plen2[b]:])
+
+
+def test_append_skips_open_blocks_and_flags_full_caches():
+    rng = np.random.default_rng(9)
+    NB, B, Hkv, d, p_max = 3, 4, 1, 8, 12
+    k_blk = rng.standard_normal((NB, 2 * B, Hkv, d))
+    v_blk = rng.standard_normal((NB, 2 * B, Hkv, d))
+    kc = rng.standard_normal((NB, Hkv, p_max, d))
+    vc = rng.standard_normal((NB, Hkv, p_max, d))
+    committed = np.array([0b0111, 0b1111, 0b1111], dtype=np.uint64)
+    P = np.array([2, 9, 8])
+    kc2, vc2, plen2, st = append_kv_ref(k_blk, v_blk, None, committed, P, kc, vc, 1e4)
+    assert plen2.tolist() == [2, 9, 12]           # open block, no room, appended
+    assert st.tolist() == [0, 4, 0]
+    np.testing.assert_array_equal(kc2[:2], kc[:2])
+    np.testing.assert_array_equal(vc2[2, 0, 8:12], v_blk[2, :B, 0])
