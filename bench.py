@@ -207,6 +207,46 @@ def projection_measure(torch, sd, synth, dev, stream, steps, warmup):
     return res
 
 
+def commit_measure(torch, sd, w, sets, dev, stream, steps):
+    """The commit step of the headline workload: simsd_commit of one round
+    (the accept outputs of an input set) and simsd_append_kv of the finished
+    blocks (every block counted as finished: 32 sequences x 8 data rows x 8
+    KV heads of K and V, keys rotated) into a cache with room for the 8 calls
+    of a timed block (the lengths are reset between blocks, outside the
+    events).  Mean per call over blocks of 8 calls between two events."""
+    NB, B = w.NB, w.B
+    s = sets[0]
+    committed = torch.zeros(NB, dtype=torch.int64, device=dev)
+    block_tok = torch.full((NB, B), -1, dtype=torch.int32, device=dev)
+    p_max = w.P + 8 * B
+    kc = torch.zeros((NB, w.Hkv, p_max, w.d), dtype=w.dtype, device=dev)
+    vc = torch.zeros_like(kc)
+    plen = torch.full((NB,), w.P, dtype=torch.int32, device=dev)
+    calls = {
+        "commit": sd.bind_commit(s["a"]["tau"], s["a"]["draft_tok"], s["n_acc"], s["nxt"], committed, block_tok,
+                                 stream=stream),
+        "append_kv": sd.bind_append_kv(s["t"]["k_blk"], s["t"]["v_blk"], kc, vc, plen, rope_base=w.rope_base,
+                                       stream=stream),
+    }
+    res = {}
+    for name, call in calls.items():
+        times = []
+        for it in range(max(steps // 8, 4) + 1):
+            plen.fill_(w.P)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(8):
+                call()
+            e1.record(stream)
+            e1.synchronize()
+            if it:  # the first block is the warmup
+                times.append(e0.elapsed_time(e1) / 8 * 1e3)
+        res[name + "_us"] = sum(times) / len(times)
+    # K and V rows read from the block and written to the cache
+    res["append_bytes_moved"] = 4 * NB * B * w.Hkv * w.d * (2 if w.dtype == torch.bfloat16 else 4)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,6 +349,7 @@ def main():
 
     coupled = coupled_measure(torch, sd, synth, dev, stream, args.steps, args.warmup)
     projections = projection_measure(torch, sd, synth, dev, stream, args.steps, args.warmup)
+    commit_times = commit_measure(torch, sd, w, sets, dev, stream, args.steps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -343,6 +384,7 @@ def main():
         "cpu_baseline": cpu,
         "accept_coupled": coupled,
         "projections": projections,
+        "commit_step": commit_times,
     }
     print(json.dumps(rec), flush=True)
 

@@ -79,6 +79,10 @@ SIGNATURES = {
     "simsd_debug_rope": (c_int32, [ctypes.POINTER(VerifyDesc)] + [c_void_p] * 7),
     "simsd_strerror": (ctypes.c_char_p, [c_int32]),
     "simsd_abi_version": (c_int32, []),
+    "simsd_commit": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                               c_void_p]),
+    "simsd_append_kv": (c_int32, [ctypes.POINTER(VerifyDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_void_p, c_void_p]),
     "simsd_linear": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p]),
     "simsd_qkv_proj": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32,
                                  c_void_p, c_void_p, c_void_p, c_void_p]),

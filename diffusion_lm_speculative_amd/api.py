@@ -227,6 +227,54 @@ def qkv_proj(x, w_qkv, Hq, Hkv, d, *, q=None, k=None, v=None, stream=None):
     return q, k, v
 
 
+def commit(tau, draft_tok, n_accepted, next_token, committed, block_tok, stream=None):
+    """Commit one round's accepted prefix (and replacement) into the block state
+    (committed [NB] int64 view of the uint64 masks, block_tok [NB][B] int32), in place."""
+    lib = L.load()
+    _need(tau, "tau", torch.int32)
+    NB, B = tau.shape
+    dev = tau.device
+    _need(draft_tok, "draft_tok", torch.int32, (NB, B), dev)
+    _need(n_accepted, "n_accepted", torch.int32, (NB,), dev)
+    if next_token is not None:
+        _need(next_token, "next_token", torch.int32, (NB,), dev)
+    _need(committed, "committed", torch.int64, (NB,), dev)
+    _need(block_tok, "block_tok", torch.int32, (NB, B), dev)
+    L.check(lib.simsd_commit(_ptr(tau), _ptr(draft_tok), _ptr(n_accepted), _ptr(next_token), NB, B, _ptr(committed),
+                             _ptr(block_tok), _stream_handle(stream)), "simsd_commit")
+    return committed, block_tok
+
+
+def append_kv(k_blk, v_blk, k_cache, v_cache, prompt_len, *, rope_base, committed=None, pos_d=None, status=None,
+              stream=None):
+    """Append finished blocks' data rows to the cache (in place); prompt_len grows by B
+    for every appended sequence.  Returns status [NB]."""
+    lib = L.load()
+    dt = k_blk.dtype
+    NB, twoB, Hkv, d = k_blk.shape
+    B = twoB // 2
+    dev = k_blk.device
+    _need(k_blk, "k_blk", dt)
+    _need(v_blk, "v_blk", dt, tuple(k_blk.shape), dev)
+    _need(k_cache, "k_cache", dt, None, dev)
+    _need(v_cache, "v_cache", dt, tuple(k_cache.shape), dev)
+    if tuple(k_cache.shape[:2]) != (NB, Hkv) or k_cache.shape[3] != d:
+        raise ValueError(f"k_cache must be [NB][Hkv][p_max][d], got {tuple(k_cache.shape)}")
+    _need(prompt_len, "prompt_len", torch.int32, (NB,), dev)
+    if committed is not None:
+        _need(committed, "committed", torch.int64, (NB,), dev)
+    if pos_d is not None:
+        _need(pos_d, "pos_d", torch.int32, (NB, B), dev)
+    if status is None:
+        status = torch.empty((NB,), dtype=torch.int32, device=dev)
+    _need(status, "status", torch.int32, (NB,), dev)
+    desc = L.VerifyDesc(NB, Hkv, Hkv, d, B, k_cache.shape[2], _DT[dt], 0, 0, 0, float(rope_base), 0.0, 0)
+    L.check(lib.simsd_append_kv(ctypes.byref(desc), _ptr(k_blk), _ptr(v_blk), _ptr(pos_d), _ptr(committed),
+                                _ptr(prompt_len), _ptr(k_cache), _ptr(v_cache), _ptr(status), _stream_handle(stream)),
+            "simsd_append_kv")
+    return status
+
+
 @dataclass
 class BoundCall:
     """A C-ABI call with every argument marshalled once (for timing loops).
@@ -239,6 +287,32 @@ class BoundCall:
         rc = getattr(L.load(), self.fn)(*self.args)
         if rc:
             L.check(rc, self.fn)
+
+
+def bind_commit(tau, draft_tok, n_accepted, next_token, committed, block_tok, stream=None) -> BoundCall:
+    NB, B = tau.shape
+    for t, name in ((tau, "tau"), (draft_tok, "draft_tok"), (block_tok, "block_tok")):
+        _need(t, name, torch.int32, (NB, B), tau.device)
+    _need(n_accepted, "n_accepted", torch.int32, (NB,), tau.device)
+    _need(committed, "committed", torch.int64, (NB,), tau.device)
+    return BoundCall("simsd_commit", (_ptr(tau), _ptr(draft_tok), _ptr(n_accepted), _ptr(next_token), NB, B,
+                                      _ptr(committed), _ptr(block_tok), _stream_handle(stream)),
+                     (tau, draft_tok, n_accepted, next_token, committed, block_tok))
+
+
+def bind_append_kv(k_blk, v_blk, k_cache, v_cache, prompt_len, *, rope_base, committed=None, pos_d=None, status=None,
+                   stream=None) -> BoundCall:
+    dt = k_blk.dtype
+    NB, twoB, Hkv, d = k_blk.shape
+    _need(v_blk, "v_blk", dt, tuple(k_blk.shape), k_blk.device)
+    _need(k_cache, "k_cache", dt, None, k_blk.device)
+    _need(v_cache, "v_cache", dt, tuple(k_cache.shape), k_blk.device)
+    _need(prompt_len, "prompt_len", torch.int32, (NB,), k_blk.device)
+    desc = L.VerifyDesc(NB, Hkv, Hkv, d, twoB // 2, k_cache.shape[2], _DT[dt], 0, 0, 0, float(rope_base), 0.0, 0)
+    return BoundCall("simsd_append_kv", (ctypes.byref(desc), _ptr(k_blk), _ptr(v_blk), _ptr(pos_d), _ptr(committed),
+                                         _ptr(prompt_len), _ptr(k_cache), _ptr(v_cache), _ptr(status),
+                                         _stream_handle(stream)),
+                     (desc, k_blk, v_blk, k_cache, v_cache, prompt_len, committed, pos_d, status))
 
 
 def bind_linear(x, w, out, stream=None) -> BoundCall:

@@ -328,6 +328,40 @@ int simsd_qkv_proj(const void* x, const void* w_qkv, int64_t M, int32_t H, int32
   return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
 }
 
+int simsd_commit(const int32_t* tau, const int32_t* draft_tok, const int32_t* n_accepted, const int32_t* next_token,
+                 int32_t batch, int32_t B, uint64_t* committed, int32_t* block_tok, void* stream) {
+  if (batch < 0 || B < 0 || B > 64) return SIMSD_ERR_SHAPE;
+  if (batch == 0 || B == 0) return SIMSD_OK;
+  if (!tau || !draft_tok || !n_accepted || !committed || !block_tok) return SIMSD_ERR_NULL;
+  if (!aligned(tau, 4) || !aligned(draft_tok, 4) || !aligned(n_accepted, 4) || (next_token && !aligned(next_token, 4)) ||
+      !aligned(committed, 8) || !aligned(block_tok, 4))
+    return SIMSD_ERR_ALIGN;
+  return launch_commit(tau, draft_tok, n_accepted, next_token, batch, B, committed, block_tok,
+                       static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SIMSD_OK
+             : SIMSD_ERR_HIP;
+}
+
+int simsd_append_kv(const simsd_verify_desc* desc, const void* k_blk, const void* v_blk, const int32_t* pos_d,
+                    const uint64_t* committed, int32_t* prompt_len, void* k_cache, void* v_cache, int32_t* status,
+                    void* stream) {
+  if (!desc) return SIMSD_ERR_NULL;
+  Plan pl;
+  const int rc = make_plan(*desc, pl);
+  if (rc != SIMSD_OK) return rc;
+  if (pl.NB == 0 || pl.B == 0) return SIMSD_OK;
+  if (!k_blk || !v_blk || !prompt_len || !k_cache || !v_cache) return SIMSD_ERR_NULL;
+  const size_t el = pl.dtype == SIMSD_BF16 ? 2 : 4;
+  if (!aligned(k_blk, el) || !aligned(v_blk, el) || !aligned(k_cache, el) || !aligned(v_cache, el) ||
+      !aligned(prompt_len, 4) || (pos_d && !aligned(pos_d, 4)) || (committed && !aligned(committed, 8)) ||
+      (status && !aligned(status, 4)))
+    return SIMSD_ERR_ALIGN;
+  return launch_append_kv(pl, k_blk, v_blk, pos_d, committed, prompt_len, k_cache, v_cache, status,
+                          static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SIMSD_OK
+             : SIMSD_ERR_HIP;
+}
+
 int simsd_debug_mask(const int32_t* tau, int32_t batch, int32_t B, int32_t mask_mode, uint64_t* bits,
                      void* stream) {
   if (batch < 0 || B < 0 || B > 64) return SIMSD_ERR_SHAPE;

@@ -1,0 +1,111 @@
+// The commit step between verification rounds (page "SimSD - Simple
+// Speculative Decoding in Diffusion Language Models", section 4: the longest
+// accepted prefix is committed and the process repeats; "Key contributions"
+// item 3: the method runs with a KV cache and blockwise decoding).
+//
+// commit: one wave per sequence, lane k = response position k.  The
+// positions of stages 1..n take their drafted tokens, the position of stage
+// n+1 the replacement token when the walk drew one; a ballot over the lanes
+// gives the new committed bits.
+//
+// append: one workgroup per sequence whose block is finished (all B
+// positions committed).  The data rows' keys are rotated at their RoPE
+// positions with the same angle reduction and rounding as the attention
+// kernels (so the cached keys equal the ones the verification pass used for
+// D_0..D_{B-1}), the values copied, both written at cache rows P_b .. P_b+B-1,
+// and then P_b grows by B.  The rows and the length update of a sequence stay
+// in one workgroup, so the old length is read before it is replaced.
+#include "simsd_common.hpp"
+
+namespace simsd {
+namespace {
+
+__global__ __launch_bounds__(64) void commit_kernel(const int32_t* __restrict__ tau, const int32_t* __restrict__ draft,
+                                                    const int32_t* __restrict__ n_acc,
+                                                    const int32_t* __restrict__ next_tok, int B,
+                                                    uint64_t* committed, int32_t* block_tok) {
+  const int b = blockIdx.x;
+  const int k = threadIdx.x;
+  const int n = n_acc[b];
+  if (n < 0) return;  // a faulted round commits nothing
+  const int nx = next_tok ? next_tok[b] : -1;
+  int t = 0, tok = -1;
+  if (k < B) {
+    t = tau[static_cast<size_t>(b) * B + k];
+    tok = draft[static_cast<size_t>(b) * B + k];
+  }
+  const bool accepted = k < B && t >= 1 && t <= n;
+  const bool replaced = k < B && nx >= 0 && t == n + 1;
+  if (accepted || replaced) block_tok[static_cast<size_t>(b) * B + k] = accepted ? tok : nx;
+  const uint64_t bits = __ballot(accepted || replaced);
+  if (k == 0) committed[b] |= bits;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void append_kv_kernel(Plan pl, const T* __restrict__ k_blk,
+                                                        const T* __restrict__ v_blk, const int32_t* __restrict__ pos_d,
+                                                        const uint64_t* __restrict__ committed, int32_t* prompt_len,
+                                                        T* k_cache, T* v_cache, int32_t* status) {
+  const int b = blockIdx.x;
+  const int B = pl.B, Hkv = pl.Hkv, d = pl.d, half = d / 2;
+  const uint64_t full = B >= 64 ? ~0ull : ((1ull << B) - 1ull);
+  if (committed && committed[b] != full) {  // block still open
+    if (status && threadIdx.x == 0) status[b] = 0;
+    return;
+  }
+  const int P = prompt_len[b];
+  if (P < 0 || static_cast<int64_t>(P) + B > pl.p_max) {
+    if (status && threadIdx.x == 0) status[b] = SIMSD_ST_PROMPT_LEN;
+    return;
+  }
+  const int32_t* pos_b = pos_d ? pos_d + static_cast<size_t>(b) * B : nullptr;
+  // keys: one rotation pair (f, f + d/2) per item
+  for (int i = threadIdx.x; i < B * Hkv * half; i += blockDim.x) {
+    const int f = i % half, h = (i / half) % Hkv, k = i / (half * Hkv);
+    const T* src = k_blk + ((static_cast<size_t>(b) * pl.twoB + k) * Hkv + h) * d;
+    T* dst = k_cache + ((static_cast<size_t>(b) * Hkv + h) * pl.p_max + P + k) * d;
+    const int64_t pos = pos_b ? static_cast<int64_t>(pos_b[k]) : static_cast<int64_t>(P) + k;
+    float xo, yo;
+    rope_apply(Elem<T>::load(src, f), Elem<T>::load(src, f + half), rope_cos_sin(pos, rope_inv_freq(f, d, pl.log2_base)),
+               xo, yo);
+    Elem<T>::store(dst, f, xo);
+    Elem<T>::store(dst, f + half, yo);
+  }
+  // values
+  for (int i = threadIdx.x; i < B * Hkv * d; i += blockDim.x) {
+    const int e = i % d, h = (i / d) % Hkv, k = i / (d * Hkv);
+    const T* src = v_blk + ((static_cast<size_t>(b) * pl.twoB + k) * Hkv + h) * d;
+    T* dst = v_cache + ((static_cast<size_t>(b) * Hkv + h) * pl.p_max + P + k) * d;
+    dst[e] = src[e];
+  }
+  __syncthreads();  // every thread has used the old length
+  if (threadIdx.x == 0) {
+    prompt_len[b] = P + B;
+    if (status) status[b] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_commit(const int32_t* tau, const int32_t* draft, const int32_t* n_acc, const int32_t* next_tok,
+                         int NB, int B, uint64_t* committed, int32_t* block_tok, hipStream_t s) {
+  hipLaunchKernelGGL(commit_kernel, dim3(NB), dim3(64), 0, s, tau, draft, n_acc, next_tok, B, committed, block_tok);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_kv(const Plan& pl, const void* k_blk, const void* v_blk, const int32_t* pos_d,
+                            const uint64_t* committed, int32_t* prompt_len, void* k_cache, void* v_cache,
+                            int32_t* status, hipStream_t s) {
+  if (pl.dtype == SIMSD_BF16) {
+    hipLaunchKernelGGL(append_kv_kernel<uint16_t>, dim3(pl.NB), dim3(256), 0, s, pl,
+                       static_cast<const uint16_t*>(k_blk), static_cast<const uint16_t*>(v_blk), pos_d, committed,
+                       prompt_len, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), status);
+  } else {
+    hipLaunchKernelGGL(append_kv_kernel<float>, dim3(pl.NB), dim3(256), 0, s, pl, static_cast<const float*>(k_blk),
+                       static_cast<const float*>(v_blk), pos_d, committed, prompt_len, static_cast<float*>(k_cache),
+                       static_cast<float*>(v_cache), status);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace simsd

@@ -205,6 +205,12 @@ size_t mfma_lds_bytes(int hd, int nstage, int tab_rows, int rows_wg, bool qsep);
 // out0, [cut1, cut2) to out1, [cut2, N) to out2, row-major with row lengths
 // ld0..ld2.
 int linear_tile(int64_t M, int N);
+
+hipError_t launch_commit(const int32_t* tau, const int32_t* draft, const int32_t* n_acc, const int32_t* next_tok,
+                         int NB, int B, uint64_t* committed, int32_t* block_tok, hipStream_t s);
+hipError_t launch_append_kv(const Plan& pl, const void* k_blk, const void* v_blk, const int32_t* pos_d,
+                            const uint64_t* committed, int32_t* prompt_len, void* k_cache, void* v_cache,
+                            int32_t* status, hipStream_t s);
 hipError_t launch_linear(const uint16_t* x, const uint16_t* w, int64_t M, int N, int K, int cut1, int cut2,
                          uint16_t* out0, int ld0, uint16_t* out1, int ld1, uint16_t* out2, int ld2, hipStream_t s);
 hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s);

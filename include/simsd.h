@@ -279,6 +279,42 @@ int simsd_linear(const void* x, const void* w, int64_t M, int32_t N, int32_t K, 
 int simsd_qkv_proj(const void* x, const void* w_qkv, int64_t M, int32_t H, int32_t Hq, int32_t Hkv, int32_t d,
                    void* q, void* k, void* v, void* stream);
 
+/* ---- the commit step between rounds ---------------------------------------------
+ * Section 4: the longest accepted prefix is committed and the process
+ * repeats; "Key contributions" item 3: the method runs with a KV cache and
+ * blockwise decoding.  The block state of a sequence is a committed mask
+ * (bit k: response position k is committed) and the committed token of each
+ * position. */
+
+/* Commit one round.  For every sequence b with n_accepted[b] >= 0: the
+ * positions of stages 1..n_accepted[b] take their drafted tokens, and when
+ * next_token (may be NULL) holds a token >= 0 the position of stage n+1 takes
+ * it; block_tok[b][k] receives the token and bit k of committed[b] is set
+ * (bits set by earlier rounds stay set).  Sequences with n_accepted[b] < 0
+ * (a faulted round) are left unchanged.
+ *  tau, draft_tok [NB][B] int32, n_accepted, next_token [NB] int32 (the
+ *  outputs of simsd_accept_prefix / simsd_accept_coupled); committed [NB]
+ *  uint64 (in/out, 8-byte aligned); block_tok [NB][B] int32 (in/out).
+ * Errors: SIMSD_ERR_SHAPE (B outside 0..64), _NULL, _ALIGN, _HIP. */
+int simsd_commit(const int32_t* tau, const int32_t* draft_tok, const int32_t* n_accepted, const int32_t* next_token,
+                 int32_t batch, int32_t B, uint64_t* committed, int32_t* block_tok, void* stream);
+
+/* Append finished blocks to the KV cache.  For every sequence whose
+ * committed[b] has all B bits set (every sequence when committed is NULL):
+ * key rows D_0..D_{B-1} of k_blk, rotated at their RoPE positions (pos_d, or
+ * P_b + k when NULL) with the rounding of simsd_verify_attn, are written to
+ * k_cache[b][h][P_b + k], the value rows to v_cache, and prompt_len[b] grows
+ * by B.  Uses desc's shape, dtype and rope_base (desc->p_max is the cache
+ * capacity).  status [NB] (or NULL): 0, or SIMSD_ST_PROMPT_LEN when
+ * P_b + B > p_max (that sequence is left unchanged).  The caller provides
+ * k_blk / v_blk computed for the committed tokens.
+ *  k_blk, v_blk [NB][2B][Hkv][d] (rows 0..B-1 are read); prompt_len [NB]
+ *  int32 in/out; k_cache, v_cache [NB][Hkv][p_max][d] in/out.
+ * Errors: as for simsd_verify_attn. */
+int simsd_append_kv(const simsd_verify_desc* desc, const void* k_blk, const void* v_blk, const int32_t* pos_d,
+                    const uint64_t* committed, int32_t* prompt_len, void* k_cache, void* v_cache, int32_t* status,
+                    void* stream);
+
 /* Human-readable text for a return code (static storage). */
 const char* simsd_strerror(int code);
 

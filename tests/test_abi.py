@@ -39,7 +39,7 @@ def _declared():
 def test_header_declarations_match_binding():
     decl = _declared()
     assert decl == set(L.SIGNATURES), decl ^ set(L.SIGNATURES)
-    assert len(decl) == 12
+    assert len(decl) == 14
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -208,6 +208,33 @@ def test_accept_rejects_on_host(lib):
         assert call(**{k: A + 2}) == L.ERR_ALIGN, k
     # the residual draw (next_token != NULL) needs the workspace
     assert call(nx=A) == L.ERR_WORKSPACE
+
+
+@no_gpu_only
+def test_commit_and_append_reject_on_host(lib):
+    def com(tau=A, x=A, n=A, nx=A, NB=4, B=8, c=A, t=A):
+        return lib.simsd_commit(tau, x, n, nx, NB, B, c, t, None)
+    assert com(NB=0, tau=None, x=None, n=None, c=None, t=None) == 0
+    assert com(B=65) == L.ERR_SHAPE
+    assert com(NB=-1) == L.ERR_SHAPE
+    for k in ("tau", "x", "n", "c", "t"):
+        assert com(**{k: None}) == L.ERR_NULL, k
+    for k in ("tau", "x", "n", "nx", "t"):
+        assert com(**{k: A + 2}) == L.ERR_ALIGN, k
+    assert com(c=A + 4) == L.ERR_ALIGN
+
+    def app(desc=None, kb=A, vb=A, pos=None, c=None, plen=A, kc=A, vc=A, st=None):
+        d = desc if desc is not None else _desc()
+        return lib.simsd_append_kv(ctypes.byref(d), kb, vb, pos, c, plen, kc, vc, st, None)
+    assert lib.simsd_append_kv(None, A, A, None, None, A, A, A, None, None) == L.ERR_NULL
+    assert app(desc=_desc(B=65)) == L.ERR_SHAPE
+    assert app(desc=_desc(dtype=7)) == L.ERR_DTYPE
+    assert app(desc=_desc(batch=0), kb=None, vb=None, plen=None, kc=None, vc=None) == 0
+    for k in ("kb", "vb", "plen", "kc", "vc"):
+        assert app(**{k: None}) == L.ERR_NULL, k
+    for k in ("kb", "vb", "kc", "vc", "plen", "pos", "st"):
+        assert app(**{k: A + 1}) == L.ERR_ALIGN, k
+    assert app(c=A + 4) == L.ERR_ALIGN
 
 
 @no_gpu_only
