@@ -8,13 +8,13 @@
 // n+1 the replacement token when the walk drew one; a ballot over the lanes
 // gives the new committed bits.
 //
-// append: one workgroup per sequence whose block is finished (all B
-// positions committed).  The data rows' keys are rotated at their RoPE
+// append: one workgroup per (KV head, sequence) whose block is finished (all
+// B positions committed).  The data rows' keys are rotated at their RoPE
 // positions with the same angle reduction and rounding as the attention
 // kernels (so the cached keys equal the ones the verification pass used for
-// D_0..D_{B-1}), the values copied, both written at cache rows P_b .. P_b+B-1,
-// and then P_b grows by B.  The rows and the length update of a sequence stay
-// in one workgroup, so the old length is read before it is replaced.
+// D_0..D_{B-1}) and the values copied, both to cache rows P_b .. P_b+B-1.  A
+// second launch on the same stream then grows P_b by B and writes the status,
+// so no row workgroup can see the new length.
 #include "simsd_common.hpp"
 
 namespace simsd {
@@ -41,29 +41,33 @@ __global__ __launch_bounds__(64) void commit_kernel(const int32_t* __restrict__ 
   if (k == 0) committed[b] |= bits;
 }
 
+// Whether sequence b's block is appended this call: finished (or no mask
+// given) and room for B more rows.
+__device__ __forceinline__ bool append_ok(const Plan& pl, const uint64_t* committed, int P, int b) {
+  const uint64_t full = pl.B >= 64 ? ~0ull : ((1ull << pl.B) - 1ull);
+  if (committed && committed[b] != full) return false;
+  return P >= 0 && static_cast<int64_t>(P) + pl.B <= pl.p_max;
+}
+
+// Rows of one (KV head, sequence): B keys rotated and B values copied.
 template <typename T>
-__global__ __launch_bounds__(256) void append_kv_kernel(Plan pl, const T* __restrict__ k_blk,
-                                                        const T* __restrict__ v_blk, const int32_t* __restrict__ pos_d,
-                                                        const uint64_t* __restrict__ committed, int32_t* prompt_len,
-                                                        T* k_cache, T* v_cache, int32_t* status) {
-  const int b = blockIdx.x;
+__global__ __launch_bounds__(128) void append_rows_kernel(Plan pl, const T* __restrict__ k_blk,
+                                                          const T* __restrict__ v_blk,
+                                                          const int32_t* __restrict__ pos_d,
+                                                          const uint64_t* __restrict__ committed,
+                                                          const int32_t* __restrict__ prompt_len, T* k_cache,
+                                                          T* v_cache) {
+  const int h = blockIdx.x, b = blockIdx.y;
   const int B = pl.B, Hkv = pl.Hkv, d = pl.d, half = d / 2;
-  const uint64_t full = B >= 64 ? ~0ull : ((1ull << B) - 1ull);
-  if (committed && committed[b] != full) {  // block still open
-    if (status && threadIdx.x == 0) status[b] = 0;
-    return;
-  }
   const int P = prompt_len[b];
-  if (P < 0 || static_cast<int64_t>(P) + B > pl.p_max) {
-    if (status && threadIdx.x == 0) status[b] = SIMSD_ST_PROMPT_LEN;
-    return;
-  }
+  if (!append_ok(pl, committed, P, b)) return;
   const int32_t* pos_b = pos_d ? pos_d + static_cast<size_t>(b) * B : nullptr;
+  const size_t cache0 = (static_cast<size_t>(b) * Hkv + h) * pl.p_max + P;
   // keys: one rotation pair (f, f + d/2) per item
-  for (int i = threadIdx.x; i < B * Hkv * half; i += blockDim.x) {
-    const int f = i % half, h = (i / half) % Hkv, k = i / (half * Hkv);
+  for (int i = threadIdx.x; i < B * half; i += blockDim.x) {
+    const int f = i % half, k = i / half;
     const T* src = k_blk + ((static_cast<size_t>(b) * pl.twoB + k) * Hkv + h) * d;
-    T* dst = k_cache + ((static_cast<size_t>(b) * Hkv + h) * pl.p_max + P + k) * d;
+    T* dst = k_cache + (cache0 + k) * d;
     const int64_t pos = pos_b ? static_cast<int64_t>(pos_b[k]) : static_cast<int64_t>(P) + k;
     float xo, yo;
     rope_apply(Elem<T>::load(src, f), Elem<T>::load(src, f + half), rope_cos_sin(pos, rope_inv_freq(f, d, pl.log2_base)),
@@ -72,17 +76,24 @@ __global__ __launch_bounds__(256) void append_kv_kernel(Plan pl, const T* __rest
     Elem<T>::store(dst, f + half, yo);
   }
   // values
-  for (int i = threadIdx.x; i < B * Hkv * d; i += blockDim.x) {
-    const int e = i % d, h = (i / d) % Hkv, k = i / (d * Hkv);
-    const T* src = v_blk + ((static_cast<size_t>(b) * pl.twoB + k) * Hkv + h) * d;
-    T* dst = v_cache + ((static_cast<size_t>(b) * Hkv + h) * pl.p_max + P + k) * d;
-    dst[e] = src[e];
+  for (int i = threadIdx.x; i < B * d; i += blockDim.x) {
+    const int e = i % d, k = i / d;
+    v_cache[(cache0 + k) * d + e] = v_blk[((static_cast<size_t>(b) * pl.twoB + k) * Hkv + h) * d + e];
   }
-  __syncthreads();  // every thread has used the old length
-  if (threadIdx.x == 0) {
-    prompt_len[b] = P + B;
-    if (status) status[b] = 0;
-  }
+}
+
+// Length and status of each sequence; launched after the rows so that every
+// row workgroup has read the old length.
+__global__ __launch_bounds__(64) void append_len_kernel(Plan pl, const uint64_t* __restrict__ committed,
+                                                        int32_t* prompt_len, int32_t* status) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= pl.NB) return;
+  const int P = prompt_len[b];
+  const uint64_t full = pl.B >= 64 ? ~0ull : ((1ull << pl.B) - 1ull);
+  const bool open = committed && committed[b] != full;
+  const bool ok = append_ok(pl, committed, P, b);
+  if (ok) prompt_len[b] = P + pl.B;
+  if (status) status[b] = (ok || open) ? 0 : SIMSD_ST_PROMPT_LEN;
 }
 
 }  // namespace
@@ -96,15 +107,19 @@ hipError_t launch_commit(const int32_t* tau, const int32_t* draft, const int32_t
 hipError_t launch_append_kv(const Plan& pl, const void* k_blk, const void* v_blk, const int32_t* pos_d,
                             const uint64_t* committed, int32_t* prompt_len, void* k_cache, void* v_cache,
                             int32_t* status, hipStream_t s) {
+  const dim3 grid(pl.Hkv, pl.NB);
   if (pl.dtype == SIMSD_BF16) {
-    hipLaunchKernelGGL(append_kv_kernel<uint16_t>, dim3(pl.NB), dim3(256), 0, s, pl,
-                       static_cast<const uint16_t*>(k_blk), static_cast<const uint16_t*>(v_blk), pos_d, committed,
-                       prompt_len, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), status);
+    hipLaunchKernelGGL(append_rows_kernel<uint16_t>, grid, dim3(128), 0, s, pl, static_cast<const uint16_t*>(k_blk),
+                       static_cast<const uint16_t*>(v_blk), pos_d, committed, prompt_len,
+                       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache));
   } else {
-    hipLaunchKernelGGL(append_kv_kernel<float>, dim3(pl.NB), dim3(256), 0, s, pl, static_cast<const float*>(k_blk),
+    hipLaunchKernelGGL(append_rows_kernel<float>, grid, dim3(128), 0, s, pl, static_cast<const float*>(k_blk),
                        static_cast<const float*>(v_blk), pos_d, committed, prompt_len, static_cast<float*>(k_cache),
-                       static_cast<float*>(v_cache), status);
+                       static_cast<float*>(v_cache));
   }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(append_len_kernel, dim3((pl.NB + 63) / 64), dim3(64), 0, s, pl, committed, prompt_len, status);
   return hipGetLastError();
 }
 

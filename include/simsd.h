@@ -310,7 +310,7 @@ int simsd_commit(const int32_t* tau, const int32_t* draft_tok, const int32_t* n_
  * k_blk / v_blk computed for the committed tokens.
  *  k_blk, v_blk [NB][2B][Hkv][d] (rows 0..B-1 are read); prompt_len [NB]
  *  int32 in/out; k_cache, v_cache [NB][Hkv][p_max][d] in/out.
- * Errors: as for simsd_verify_attn. */
+ * Errors: as for simsd_verify_attn, and SIMSD_ERR_SHAPE for batch > 65535. */
 int simsd_append_kv(const simsd_verify_desc* desc, const void* k_blk, const void* v_blk, const int32_t* pos_d,
                     const uint64_t* committed, int32_t* prompt_len, void* k_cache, void* v_cache, int32_t* status,
                     void* stream);

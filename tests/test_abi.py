@@ -229,6 +229,7 @@ def test_commit_and_append_reject_on_host(lib):
     assert lib.simsd_append_kv(None, A, A, None, None, A, A, A, None, None) == L.ERR_NULL
     assert app(desc=_desc(B=65)) == L.ERR_SHAPE
     assert app(desc=_desc(dtype=7)) == L.ERR_DTYPE
+    assert app(desc=_desc(batch=65536)) == L.ERR_SHAPE  # one grid row per sequence
     assert app(desc=_desc(batch=0), kb=None, vb=None, plen=None, kc=None, vc=None) == 0
     for k in ("kb", "vb", "plen", "kc", "vc"):
         assert app(**{k: None}) == L.ERR_NULL, k
