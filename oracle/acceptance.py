@@ -16,6 +16,11 @@ draw uses counter (b, n+1, 1, offset) and keeps the top 53 bits.  Keying by
 stage (not by position) makes the accepted length invariant under a joint
 permutation of positions and tau.
 
+Stage label 0 marks a position committed in an earlier round of the block
+(the process repeats, section 4): no walk visits it.  The other labels must
+be exactly 1..m, m the number of open positions, and the walk covers stages
+1..min(gamma, m); n = min(gamma, m) is a full acceptance.
+
 The acceptance test ``u * q(x) < p(x)`` is exact in float64: u has 24
 significant bits and q is a float32, so the product needs at most 48 bits.
 The residual CDF is the sequential float64 prefix sum; ``next_token`` is the
@@ -26,8 +31,9 @@ full acceptance (n = gamma) there is no extra slot, so ``next_token`` = -1.
 Pins (tests/test_oracle_accept.py): greedy state equality with one-hot
 targets, p = q, zero target mass, the first-stage acceptance probability
 sum_v min(p_v, q_v) and the committed-token distribution p (chi-square over
-many seeds), the residual distribution, and invariance of n under a joint
-permutation.
+many seeds), the residual distribution, invariance of n under a joint
+permutation, and committed positions (label 0) reducing the walk to the one
+over the open positions alone.
 """
 
 from __future__ import annotations
@@ -46,16 +52,22 @@ def accept_status_ref(tau_b, draft_tok_b, gamma, vocab):
     tau_b = [int(t) for t in tau_b]
     B = len(tau_b)
     st = 0
-    if any(t < 1 or t > B for t in tau_b):
+    if any(t < 0 or t > B for t in tau_b):
         return ST_TAU_RANGE
-    if sorted(tau_b) != list(range(1, B + 1)):
+    open_labels = sorted(t for t in tau_b if t > 0)
+    if open_labels != list(range(1, len(open_labels) + 1)):
         return ST_TAU_NOT_PERM
     kinv = {t: k for k, t in enumerate(tau_b)}
-    for t in range(1, gamma + 1):
+    for t in range(1, walked_stages(tau_b, gamma) + 1):
         x = int(draft_tok_b[kinv[t]])
         if x < 0 or x >= vocab:
             st |= ST_TOKEN_RANGE
     return st
+
+
+def walked_stages(tau_b, gamma):
+    """Stages the walk covers: 1..min(gamma, m), m = open positions (label > 0)."""
+    return min(int(gamma), sum(1 for t in tau_b if int(t) > 0))
 
 
 def _draw(cdf_src, u):
@@ -72,7 +84,8 @@ def accept_ref(p, q, draft_tok, tau, gamma, seed, offset=0):
 
     p, q: [NB][B][V] float32 target / draft probabilities; row k belongs to
     response position k (p is read at the D~_k slot).
-    draft_tok: [NB][B] tokens placed in D_k.  tau: [NB][B] permutation of 1..B.
+    draft_tok: [NB][B] tokens placed in D_k.  tau: [NB][B] stage labels: 0
+    for committed positions, a permutation of 1..m over the m open ones.
     Returns (n_accepted [NB], next_token [NB], status [NB]) as int32 arrays;
     faulted sequences get n = next = -1.
     """
@@ -94,8 +107,9 @@ def accept_ref(p, q, draft_tok, tau, gamma, seed, offset=0):
         kinv = [0] * (B + 1)
         for k in range(B):
             kinv[int(tau[b, k])] = k
-        n = gamma
-        for t in range(1, gamma + 1):
+        g = walked_stages(tau[b], gamma)
+        n = g
+        for t in range(1, g + 1):
             k = kinv[t]
             x = int(draft_tok[b, k])
             u = uniform24(philox4x64_10((b, t, 0, offset), key)[0])
@@ -105,7 +119,7 @@ def accept_ref(p, q, draft_tok, tau, gamma, seed, offset=0):
                 n = t - 1
                 break
         n_out[b] = n
-        if n < gamma:
+        if n < g:
             ks = kinv[n + 1]
             u2 = uniform53(philox4x64_10((b, n + 1, 1, offset), key)[0])
             p64 = np.asarray(p[b, ks], dtype=np.float64)

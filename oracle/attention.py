@@ -29,7 +29,11 @@ notes):
 * RoPE is the rotate-half (non-interleaved) form with frequencies
   base^(-2f/d); D_k and D~_k sit at pos_d[b][k], by default P_b + k;
   prompt keys are stored already rotated;
-* softmax scale 1/sqrt(d); query head h reads KV head h // (Hq/Hkv).
+* softmax scale 1/sqrt(d); query head h reads KV head h // (Hq/Hkv);
+* stage label 0 marks a response position committed in an earlier round of
+  the same block (section 4: the process repeats): its token sits in D as
+  context and, 0 being below every stage, every mask slot sees it; the open
+  positions carry stages 1..m.  The predicates below apply unchanged.
 
 The result is the plain definition: for every (sequence, query head, row)
 the softmax over the explicitly constructed visible key set, in float64.
@@ -88,8 +92,9 @@ def block_visibility(tau, mode=MASK_TEMPORAL):
     """Boolean [2B, 2B]: entry [r, c] is True when block row r sees block column c.
 
     Rows and columns 0..B-1 are D_0..D_{B-1}; B..2B-1 are D~_0..D~_{B-1}.
-    ``tau`` holds the stage of each response position (1-based).  Ties are
-    allowed: the predicates below stay well defined.
+    ``tau`` holds the stage of each response position (1-based; 0 for a
+    position committed in an earlier round).  Ties are allowed: the
+    predicates below stay well defined.
     """
     tau = [int(t) for t in tau]
     B = len(tau)
@@ -115,7 +120,7 @@ def verify_status_ref(tau, prompt_len, pos_d, p_max):
     NB, B = tau.shape if tau.ndim == 2 else (tau.shape[0], 0)
     st = np.zeros(NB, dtype=np.int32)
     for b in range(NB):
-        if B and (np.any(tau[b] < 1) or np.any(tau[b] > B)):
+        if B and (np.any(tau[b] < 0) or np.any(tau[b] > B)):
             st[b] |= ST_TAU_RANGE
         if prompt_len is not None:
             P = int(prompt_len[b])

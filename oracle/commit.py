@@ -21,10 +21,15 @@ Readings taken where the page is silent (also listed in the design notes):
   (pos_d[b][k], by default P_b + k, as in the verification pass) and value k
   as is, at cache rows P_b .. P_b + B - 1, and P_b grows by B; a sequence
   without room (P_b + B > p_max) is flagged and left unchanged;
-* faulted rounds (n < 0) change nothing.
+* faulted rounds (n < 0) change nothing;
+* the next round of the block (section 4: the process repeats; the drafter
+  that proposes tokens and their order is outside this oracle) labels the
+  committed positions with stage 0 and carries their tokens in D, and gives
+  the open positions stages 1..m in the drafter's order (its rank per
+  position, ties to the smaller position) with the drafter's tokens.
 
 Pins (tests/test_oracle_commit.py): brute-force expectations on hand-built
-rounds, the committed count growing by n (+1 with a replacement), invariance
+rounds, the next round's labels as a stable sort of the open positions, the committed count growing by n (+1 with a replacement), invariance
 under a joint permutation of positions and tau, and the appended keys
 reproducing, under torch's float64 SDPA with RoPE by complex multiplication,
 the attention of a query over the block written into the cache.
@@ -60,6 +65,31 @@ def commit_ref(tau, draft_tok, n_accepted, next_token, committed, block_tok):
             block_tok[b, k] = nx
             committed[b] |= np.uint64(1) << np.uint64(k)
     return committed, block_tok
+
+
+def next_round_ref(committed, block_tok, rank, draft_tok):
+    """Stage labels and data tokens of the block's next round.
+
+    committed [NB] masks, block_tok [NB][B]; rank [NB][B] (the drafter's
+    order of the open positions, smaller first; None = position order);
+    draft_tok [NB][B] (the drafter's tokens, read at open positions).
+    Returns (tau [NB][B], tok [NB][B]) as int32 arrays.
+    """
+    block_tok = np.asarray(block_tok)
+    NB, B = block_tok.shape
+    tau = np.zeros((NB, B), dtype=np.int32)
+    tok = np.zeros((NB, B), dtype=np.int32)
+    for b in range(NB):
+        c = int(np.uint64(committed[b]))
+        open_pos = [k for k in range(B) if not (c >> k) & 1]
+        key = (lambda k: (int(rank[b][k]), k)) if rank is not None else (lambda k: k)
+        for t, k in enumerate(sorted(open_pos, key=key)):
+            tau[b, k] = t + 1
+            tok[b, k] = int(draft_tok[b][k])
+        for k in range(B):
+            if (c >> k) & 1:
+                tok[b, k] = int(block_tok[b][k])
+    return tau, tok
 
 
 def block_done(committed, B):

@@ -21,21 +21,25 @@ Readings:
   a row with no positive p_v has no target token (a_k = -1).
 - Walk: stages t = 1..gamma, k = tau^-1(t): keep the draft iff it equals
   a_k.  n = number kept; next_token = a_k at the first mismatch, or -1 after
-  a full acceptance (no extra slot).
+  a full acceptance (no extra slot).  Positions with stage label 0 were
+  committed in an earlier round of the block and are not walked; the walk
+  covers stages 1..min(gamma, m), m the open positions (as in the
+  rejection-sampling walk).
 
 Pins (tests/test_oracle_coupled.py): the Gumbel-max distribution (the
 stage-1 target token is distributed as p over many noise draws), brute-force
 comparison with exact rational arithmetic, ties to the smaller index, the
 noiseless limit (equal E: plain argmax of p), the walk's prefix semantics
-with drafts planted from the target tokens, and invariance of n under a
-joint permutation of positions and tau.
+with drafts planted from the target tokens, invariance of n under a
+joint permutation of positions and tau, and committed positions (label 0)
+reducing the walk to the one over the open positions alone.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .acceptance import accept_status_ref
+from .acceptance import accept_status_ref, walked_stages
 
 
 def target_token_ref(p_row, e_row):
@@ -91,7 +95,8 @@ def accept_coupled_ref(p, e, draft_tok, tau, gamma):
     """Walk every sequence in tau order with the coupled-noise match.
 
     p, e: [NB][B][V] float32 target probabilities and exponential noise;
-    draft_tok: [NB][B]; tau: [NB][B] permutation of 1..B.
+    draft_tok: [NB][B]; tau: [NB][B] stage labels (0 for committed positions,
+    a permutation of 1..m over the open ones).
     Returns (n_accepted, next_token, status) as int32 arrays [NB]; faulted
     sequences get n = next = -1.
     """
@@ -111,8 +116,9 @@ def accept_coupled_ref(p, e, draft_tok, tau, gamma):
         kinv = [0] * (B + 1)
         for k in range(B):
             kinv[int(tau[b, k])] = k
-        n = gamma
-        for t in range(1, gamma + 1):
+        g = walked_stages(tau[b], gamma)
+        n = g
+        for t in range(1, g + 1):
             k = kinv[t]
             a = int(target_tokens_ref(p[b, k], e[b, k]))
             if a != int(draft_tok[b, k]):

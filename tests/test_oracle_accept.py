@@ -109,11 +109,50 @@ def test_status_flags():
     rng = np.random.default_rng(9)
     p, q = _probs(rng, 4, 3, 5)
     x = np.zeros((4, 3), np.int32)
-    tau = np.array([[1, 2, 3], [0, 2, 3], [1, 1, 3], [3, 2, 1]], np.int32)
+    tau = np.array([[1, 2, 3], [-1, 2, 3], [1, 1, 3], [3, 2, 1]], np.int32)
     x[3, 2] = 5                      # stage 1 of sequence 3 holds an out-of-range token
     n, nxt, st = accept_ref(p, q, x, tau, 3, seed=1)
     assert st.tolist() == [0, 1, 2, 8]
     assert n.tolist()[1:] == [-1, -1, -1] and nxt.tolist()[1:] == [-1, -1, -1]
+    # label 0 (committed earlier): the open labels must be exactly 1..m, and a
+    # committed position's token is never checked
+    tau = np.array([[0, 2, 3], [0, 1, 2], [0, 0, 0], [2, 0, 1]], np.int32)
+    x = np.zeros((4, 3), np.int32)
+    x[1, 0] = x[2, 1] = x[3, 1] = -7
+    n, nxt, st = accept_ref(p, q, x, tau, 3, seed=1)
+    assert st.tolist() == [2, 0, 0, 0]
+    assert n[2] == 0 and nxt[2] == -1  # nothing left to walk: a full acceptance
+
+
+def _committed_inputs(rng, NB, B, c):
+    """tau with c positions labelled 0 per sequence and the open ones 1..B-c."""
+    tau = np.zeros((NB, B), np.int32)
+    for b in range(NB):
+        open_pos = np.sort(rng.permutation(B)[: B - c])
+        tau[b, open_pos] = rng.permutation(B - c) + 1
+    return tau
+
+
+@pytest.mark.parametrize("c", [1, 3, 7])
+def test_committed_positions_reduce_to_the_open_walk(c):
+    # Positions committed in an earlier round (label 0) are not walked: the
+    # result equals the walk over the open positions alone, a batch of B - c
+    # positions with the same rows (stage-keyed uniforms keep the draws).
+    rng = np.random.default_rng(30 + c)
+    NB, B, V = 20, 8, 40
+    p, q = _probs(rng, NB, B, V)
+    x = _draft(rng, q)
+    x[:, :] = np.where(rng.random((NB, B)) < 0.3, x, np.argmax(p, -1))  # some long prefixes
+    tau = _committed_inputs(rng, NB, B, c)
+    sel = np.stack([np.nonzero(tau[b])[0] for b in range(NB)])  # open positions, in order
+    take = lambda a: np.stack([a[b, sel[b]] for b in range(NB)])
+    for gamma in (0, 2, B - c, B):
+        n, nxt, st = accept_ref(p, q, x, tau, gamma, seed=5, offset=3)
+        n2, nxt2, st2 = accept_ref(take(p), take(q), take(x), take(tau), min(gamma, B - c), seed=5, offset=3)
+        assert not st.any() and not st2.any()
+        np.testing.assert_array_equal(n, n2)
+        np.testing.assert_array_equal(nxt, nxt2)
+        assert (n <= min(gamma, B - c)).all()
 
 
 def _many_first_stage(p1, q1, trials, seed):

@@ -250,7 +250,7 @@ def test_all_ties_reduce_to_bidirectional_block_steps():
 
 def test_faulted_sequences_are_zero():
     q, kb, vb, kc, vc, plen, tau = _inputs(91, 4, 2, 1, 8, 6, 3)
-    tau[1, 0] = 0                  # stage out of range
+    tau[1, 0] = -1                 # stage out of range
     plen[2] = 7                    # beyond P_max
     pos_d = np.stack([int(plen[b]) + np.arange(3) for b in range(4)])
     pos_d[3, 2] = -1               # negative position
@@ -258,6 +258,64 @@ def test_faulted_sequences_are_zero():
     assert st.tolist() == [0, 1, 4, 16]
     assert not out[1:].any() and np.all(np.isneginf(lse[1:]))
     assert np.abs(out[0]).sum() > 0
+
+
+def _with_committed(rng, tau, c):
+    """Label c positions of every sequence 0 (committed in an earlier round)
+    and the open ones 1..B-c."""
+    NB, B = tau.shape
+    tau = np.zeros_like(tau)
+    for b in range(NB):
+        open_pos = np.sort(rng.permutation(B)[: B - c])
+        tau[b, open_pos] = rng.permutation(B - c) + 1
+    return tau
+
+
+@pytest.mark.parametrize("seed,c", [(61, 1), (62, 3), (63, 5)])
+def test_committed_positions_are_context_for_every_slot(seed, c):
+    # A mask slot of an open position sees the prompt, the tokens committed in
+    # earlier rounds, the open data tokens of earlier stages and the open
+    # slots of its own or later stages (torch float64 SDPA on that state).
+    NB, Hq, Hkv, d, P, B = 2, 4, 2, 16, 7, 6
+    q, kb, vb, kc, vc, plen, tau = _inputs(seed, NB, Hq, Hkv, d, P, B)
+    rng = np.random.default_rng(seed + 100)
+    tau = _with_committed(rng, tau, c)
+    out, _, st = verify_attn_ref(q, kb, vb, kc, vc, plen, tau, rope_base=1e4)
+    assert not st.any()
+    for b in range(NB):
+        Pb = int(plen[b])
+        qh, kh = _rot_block(q, kb, Pb, None, b, 1e4)
+        done = [k for k in range(B) if tau[b, k] == 0]
+        for i in [k for k in range(B) if tau[b, k] > 0]:
+            s = tau[b, i]
+            cols = done + [k for k in range(B) if 0 < tau[b, k] < s] + \
+                [B + k for k in range(B) if tau[b, k] >= s]
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                keys = np.concatenate([kc[b, g, :Pb], kh[cols, g]])
+                vals = np.concatenate([vc[b, g, :Pb], vb[b, cols, g]])
+                ref = _sdpa(qh[B + i, h][None], keys, vals)[0]
+                np.testing.assert_allclose(out[b, B + i, h], ref, rtol=0, atol=1e-12)
+
+
+def test_committed_label_acts_as_the_earliest_stages():
+    # Relabelling the committed positions 1..c (any order) and shifting the
+    # open stages by c leaves every open position's rows unchanged.
+    NB, Hq, Hkv, d, P, B, c = 3, 4, 2, 8, 5, 7, 3
+    q, kb, vb, kc, vc, plen, tau = _inputs(71, NB, Hq, Hkv, d, P, B)
+    rng = np.random.default_rng(72)
+    tau = _with_committed(rng, tau, c)
+    tau2 = tau.copy()
+    for b in range(NB):
+        done = np.nonzero(tau[b] == 0)[0]
+        tau2[b, tau[b] > 0] += c
+        tau2[b, done] = rng.permutation(c) + 1
+    out, lse, _ = verify_attn_ref(q, kb, vb, kc, vc, plen, tau)
+    out2, lse2, _ = verify_attn_ref(q, kb, vb, kc, vc, plen, tau2)
+    for b in range(NB):
+        rows = [r for r in range(2 * B) if tau[b, r % B] > 0]
+        np.testing.assert_allclose(out[b, rows], out2[b, rows], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[b, rows], lse2[b, rows], rtol=0, atol=1e-12)
 
 
 # ----------------------------------------------------------------------------- brute force

@@ -10,7 +10,9 @@ by complex multiplication, the attention over the finished block.
 import numpy as np
 import torch
 
-from oracle.commit import append_kv_ref, block_done, commit_ref
+from oracle.acceptance import accept_ref
+from oracle.attention import block_visibility
+from oracle.commit import append_kv_ref, block_done, commit_ref, next_round_ref
 
 
 def test_commit_hand_example():
@@ -61,6 +63,70 @@ def test_commit_joint_permutation_invariance():
         bits = [(int(c[b]) >> k) & 1 for k in range(B)]
         bits2 = [(int(c2[b]) >> k) & 1 for k in range(B)]
         assert bits2 == [bits[p] for p in perm]
+
+
+def test_next_round_hand_example():
+    # B = 5, positions 1 and 3 committed (tokens 40, 41); the drafter ranks
+    # the open positions 0, 2, 4 as 7, 2, 7: position 2 first, then the tie
+    # 7 / 7 by position, 0 before 4.
+    committed = np.array([0b01010], dtype=np.uint64)
+    block_tok = np.array([[-1, 40, -1, 41, -1]])
+    rank = np.array([[7, 0, 2, 0, 7]])
+    draft = np.array([[10, 11, 12, 13, 14]])
+    tau, tok = next_round_ref(committed, block_tok, rank, draft)
+    assert tau.tolist() == [[2, 0, 1, 0, 3]]
+    assert tok.tolist() == [[10, 40, 12, 41, 14]]
+    tau, _ = next_round_ref(committed, block_tok, None, draft)  # no ranks: position order
+    assert tau.tolist() == [[1, 0, 2, 0, 3]]
+
+
+def test_next_round_labels_are_a_stable_sort_of_the_open_positions():
+    rng = np.random.default_rng(12)
+    NB, B = 40, 16
+    committed = rng.integers(0, 1 << B, size=NB).astype(np.uint64)
+    block_tok = rng.integers(0, 99, size=(NB, B))
+    rank = rng.integers(0, 5, size=(NB, B))
+    draft = rng.integers(100, 200, size=(NB, B))
+    tau, tok = next_round_ref(committed, block_tok, rank, draft)
+    for b in range(NB):
+        bits = np.array([(int(committed[b]) >> k) & 1 for k in range(B)], bool)
+        assert (tau[b, bits] == 0).all() and (tok[b, bits] == block_tok[b, bits]).all()
+        assert (tok[b, ~bits] == draft[b, ~bits]).all()
+        open_pos = np.nonzero(~bits)[0]
+        order = open_pos[np.argsort(rank[b, open_pos], kind="stable")]
+        assert tau[b, order].tolist() == list(range(1, len(open_pos) + 1))
+
+
+def test_rounds_commit_the_whole_block():
+    # Rounds of draft -> walk -> commit -> next labels: every round with an
+    # open position commits at least one (the walk's replacement at the
+    # first rejection, or every walked stage), so B rounds finish a block;
+    # committed positions are visible to every open mask slot.
+    rng = np.random.default_rng(13)
+    NB, B, V = 16, 6, 12
+    committed = np.zeros(NB, dtype=np.uint64)
+    block_tok = np.full((NB, B), -1, dtype=np.int32)
+    for rnd in range(B):
+        lp = rng.normal(0, 1.5, (NB, B, V))
+        p = np.exp(lp); p = (p / p.sum(-1, keepdims=True)).astype(np.float32)
+        lq = rng.normal(0, 1.5, (NB, B, V))
+        q = np.exp(lq); q = (q / q.sum(-1, keepdims=True)).astype(np.float32)
+        draft = rng.integers(0, V, size=(NB, B)).astype(np.int32)
+        tau, tok = next_round_ref(committed, block_tok, rng.integers(0, 100, size=(NB, B)), draft)
+        for b in range(NB):
+            vis = block_visibility(tau[b])
+            done = tau[b] == 0
+            for i in np.nonzero(~done)[0]:
+                assert vis[B + i, :B][done].all() and not vis[B + i, B:][done].any()
+        before = [bin(int(c)).count("1") for c in committed]
+        n, nx, st = accept_ref(p, q, tok, tau, B, seed=3, offset=rnd)
+        assert not st.any()
+        committed, block_tok = commit_ref(tau, tok, n, nx, committed, block_tok)
+        after = [bin(int(c)).count("1") for c in committed]
+        for b in range(NB):
+            assert after[b] - before[b] == (B - before[b] if before[b] == B else n[b] + (nx[b] >= 0))
+            assert after[b] > before[b] or before[b] == B
+    assert block_done(committed, B).all() and (block_tok >= 0).all()
 
 
 def _rope_complex(x, pos, base):

@@ -111,6 +111,30 @@ def test_prefix_semantics_with_planted_drafts():
             assert nx[b] == (-1 if m == gamma else a[b, kinv[m + 1]])
 
 
+def test_committed_positions_reduce_to_the_open_walk():
+    # Positions committed in an earlier round (label 0) are not walked, and
+    # their drafts are not checked: the result equals the walk over the open
+    # positions alone.
+    rng = np.random.default_rng(23)
+    NB, B, V, c = 7, 6, 40, 2
+    p, e, _ = _inputs(rng, NB, B, V)
+    a = target_tokens_ref(p, e)
+    tau = np.zeros((NB, B), np.int32)
+    sel = np.zeros((NB, B - c), int)
+    for b in range(NB):
+        sel[b] = np.sort(rng.permutation(B)[: B - c])
+        tau[b, sel[b]] = rng.permutation(B - c) + 1
+    draft = np.where(rng.random((NB, B)) < 0.8, a, (a + 3) % V).astype(np.int32)
+    draft[tau == 0] = -5  # never checked
+    take = lambda x: np.stack([x[b, sel[b]] for b in range(NB)])
+    for gamma in (1, B - c, B):
+        n, nx, st = accept_coupled_ref(p, e, draft, tau, gamma)
+        n2, nx2, st2 = accept_coupled_ref(take(p), take(e), take(draft), take(tau), min(gamma, B - c))
+        assert not st.any() and not st2.any()
+        np.testing.assert_array_equal(n, n2)
+        np.testing.assert_array_equal(nx, nx2)
+
+
 def test_joint_permutation_invariance():
     rng = np.random.default_rng(21)
     NB, B, V = 5, 6, 48
