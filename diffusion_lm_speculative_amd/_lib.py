@@ -81,6 +81,8 @@ SIGNATURES = {
     "simsd_abi_version": (c_int32, []),
     "simsd_commit": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                c_void_p]),
+    "simsd_next_round": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                   c_void_p]),
     "simsd_append_kv": (c_int32, [ctypes.POINTER(VerifyDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_void_p, c_void_p]),
     "simsd_linear": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p]),

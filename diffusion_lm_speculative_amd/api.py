@@ -245,6 +245,40 @@ def commit(tau, draft_tok, n_accepted, next_token, committed, block_tok, stream=
     return committed, block_tok
 
 
+def next_round(committed, block_tok, draft_tok, rank=None, tau_out=None, tok_out=None, stream=None):
+    """Stage labels and data tokens of the block's next round: committed
+    positions get stage 0 and their tokens, open ones stages 1..m in the
+    drafter's order (rank, ties by position; position order without rank)
+    and the drafter's tokens.  Returns (tau, tok) [NB][B] int32."""
+    lib = L.load()
+    _need(block_tok, "block_tok", torch.int32)
+    NB, B = block_tok.shape
+    dev = block_tok.device
+    _need(committed, "committed", torch.int64, (NB,), dev)
+    _need(draft_tok, "draft_tok", torch.int32, (NB, B), dev)
+    if rank is not None:
+        _need(rank, "rank", torch.int32, (NB, B), dev)
+    tau_out = torch.empty((NB, B), dtype=torch.int32, device=dev) if tau_out is None else tau_out
+    tok_out = torch.empty((NB, B), dtype=torch.int32, device=dev) if tok_out is None else tok_out
+    _need(tau_out, "tau_out", torch.int32, (NB, B), dev)
+    _need(tok_out, "tok_out", torch.int32, (NB, B), dev)
+    L.check(lib.simsd_next_round(_ptr(committed), _ptr(block_tok), _ptr(rank), _ptr(draft_tok), NB, B, _ptr(tau_out),
+                                 _ptr(tok_out), _stream_handle(stream)), "simsd_next_round")
+    return tau_out, tok_out
+
+
+def bind_next_round(committed, block_tok, draft_tok, rank, tau_out, tok_out, stream=None) -> BoundCall:
+    NB, B = block_tok.shape
+    for t, name in ((block_tok, "block_tok"), (draft_tok, "draft_tok"), (tau_out, "tau_out"), (tok_out, "tok_out")):
+        _need(t, name, torch.int32, (NB, B), block_tok.device)
+    _need(committed, "committed", torch.int64, (NB,), block_tok.device)
+    if rank is not None:
+        _need(rank, "rank", torch.int32, (NB, B), block_tok.device)
+    return BoundCall("simsd_next_round", (_ptr(committed), _ptr(block_tok), _ptr(rank), _ptr(draft_tok), NB, B,
+                                          _ptr(tau_out), _ptr(tok_out), _stream_handle(stream)),
+                     (committed, block_tok, draft_tok, rank, tau_out, tok_out))
+
+
 def append_kv(k_blk, v_blk, k_cache, v_cache, prompt_len, *, rope_base, committed=None, pos_d=None, status=None,
               stream=None):
     """Append finished blocks' data rows to the cache (in place); prompt_len grows by B

@@ -5,7 +5,9 @@
 //
 // Read as the textbook rule: the candidate x drafted from q at stage t is
 // kept with probability min(1, p(x)/q(x)); at the first rejection a
-// replacement is drawn from max(0, p - q) normalised.
+// replacement is drawn from max(0, p - q) normalised.  A position labelled
+// 0 was committed in an earlier round of the block and is not walked; the
+// open labels are 1..m and the walk covers stages 1..min(gamma, m).
 //
 // Two launches, both starting with the walk of their sequence in wave 0 (tau
 // inverse and validation, one stage per lane: gamma <= 64 Philox draws and
@@ -71,7 +73,7 @@ __device__ __forceinline__ uint64_t philox_word0(uint64_t c0, uint64_t c1, uint6
 // The walk's outcome for a sequence, stored by the chunk-sum launch for the
 // select launch.
 struct WalkRecord {
-  int32_t n, st, krow, pad;
+  int32_t n, st, krow, g;  // g: stages walked
   unsigned long long draw;  // word 0 of the replacement draw (stage n + 1)
   unsigned long long pad2;
 };
@@ -83,7 +85,8 @@ struct Walk {
   int tok[64];   // draft token of each position
   unsigned long long draw[64];  // word 0 of the replacement draw's counter (b, t, 1, offset), stage t = index + 1
   int st;        // status flags
-  int n;         // accepted prefix length (gamma when no stage rejects)
+  int n;         // accepted prefix length (g when no stage rejects)
+  int g;         // stages walked: min(gamma, open positions)
 };
 
 // Validate tau and the walked tokens, then decide every stage in parallel
@@ -94,27 +97,30 @@ __device__ void tau_walk(Walk& w, const float* p, const float* q, const int32_t*
   const int tid = threadIdx.x;
   for (int i = tid; i <= 64; i += blockDim.x) w.kinv[i] = -1;
   __syncthreads();
-  bool range_bad = false;
+  bool range_bad = false, open = false;
   if (tid < B) {  // stage label and draft token of position tid, loaded together
     const int t = tau_b[tid];
     w.tok[tid] = draft_b[tid];
-    range_bad = t < 1 || t > B;
-    if (!range_bad) w.kinv[t] = tid;
+    range_bad = t < 0 || t > B;
+    open = !range_bad && t >= 1;  // label 0: committed in an earlier round, not walked
+    if (open) w.kinv[t] = tid;
   }
   __syncthreads();
-  if (tid < 64) {  // wave 0
-    // a permutation leaves no stage 1..B without a position
-    const bool missing = tid < B && w.kinv[tid + 1] < 0;
+  if (tid < 64) {  // wave 0 (every position's thread is in it)
+    // the m open labels must be exactly 1..m: none of them left without a position
+    const int m = __popcll(__ballot(open));
+    const int g = min(gamma, m);
+    const bool missing = tid < m && w.kinv[tid + 1] < 0;
     int st = __any(range_bad) ? SIMSD_ST_TAU_RANGE : (__any(missing) ? SIMSD_ST_TAU_NOT_PERM : 0);
     int k = 0, x = 0;
-    if (st == 0 && tid < gamma) {
+    if (st == 0 && tid < g) {
       k = w.kinv[tid + 1];
       x = w.tok[k];
     }
-    const bool tok_bad = st == 0 && tid < gamma && (x < 0 || static_cast<int64_t>(x) >= V);
+    const bool tok_bad = st == 0 && tid < g && (x < 0 || static_cast<int64_t>(x) >= V);
     if (__any(tok_bad)) st = SIMSD_ST_TOKEN_RANGE;
     bool reject = false;
-    if (st == 0 && tid < gamma) {
+    if (st == 0 && tid < g) {
       const int t = tid + 1;
       const uint64_t r = philox_word0(static_cast<uint64_t>(b), static_cast<uint64_t>(t), 0ull, offset, seed, 0ull);
       const double u = static_cast<double>(r >> 40) * 0x1p-24;
@@ -123,12 +129,13 @@ __device__ void tau_walk(Walk& w, const float* p, const float* q, const int32_t*
       const double qv = static_cast<double>(q[row + x]);
       reject = !(u * qv < pv);
     }
-    if (draws && tid < gamma)  // the replacement draw of every stage that could be the first rejected one
+    if (draws && tid < g)  // the replacement draw of every stage that could be the first rejected one
       w.draw[tid] = philox_word0(static_cast<uint64_t>(b), static_cast<uint64_t>(tid + 1), 1ull, offset, seed, 0ull);
     const uint64_t rej = __ballot(reject);
     if (tid == 0) {
       w.st = st;
-      w.n = rej ? __builtin_ctzll(rej) : gamma;
+      w.n = rej ? __builtin_ctzll(rej) : g;
+      w.g = g;
     }
   }
   __syncthreads();
@@ -154,11 +161,12 @@ __global__ __launch_bounds__(kAccThreads) void accept_chunks_kernel(
     WalkRecord r{};
     r.n = n;
     r.st = w.st;
-    r.krow = (w.st == 0 && n < gamma) ? w.kinv[n + 1] : 0;
-    r.draw = (w.st == 0 && n < gamma) ? w.draw[n] : 0ull;
+    r.g = w.g;
+    r.krow = (w.st == 0 && n < w.g) ? w.kinv[n + 1] : 0;
+    r.draw = (w.st == 0 && n < w.g) ? w.draw[n] : 0ull;
     records[b] = r;
   }
-  if (w.st || n >= gamma) return;
+  if (w.st || n >= w.g) return;
   const size_t row = (static_cast<size_t>(b) * B + w.kinv[n + 1]) * static_cast<size_t>(V);
   const float* pr = p + row;
   const float* qr = q + row;
@@ -253,7 +261,7 @@ __global__ __launch_bounds__(64) void accept_select_kernel(
     pre[i][1] = ok ? cs[2 * c + 1] : 0.0;
   }
   const int n = rec.n;
-  if (rec.st || n >= gamma) {
+  if (rec.st || n >= rec.g) {
     if (lane == 0) {
       n_acc[b] = rec.st ? -1 : n;
       next_tok[b] = -1;

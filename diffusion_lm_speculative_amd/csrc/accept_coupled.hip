@@ -20,8 +20,10 @@
 //      (p, E, index) over lanes and waves with the exact comparison.
 //   2. walk, one workgroup per sequence: the reduction of every walked row's
 //      chunk winners (stages spread over the waves), then validation (labels
-//      1..B, a permutation, drafted tokens in range) and the compare of each
-//      draft with its stage's target token.
+//      0..B, the nonzero ones exactly 1..m, drafted tokens in range) and the
+//      compare of each draft with its stage's target token.
+// Label 0 marks a position committed in an earlier round of the block: no
+// stage finds it, and the walk covers stages 1..min(gamma, m).
 #include "simsd_common.hpp"
 
 namespace simsd {
@@ -176,15 +178,17 @@ __global__ __launch_bounds__(kWalkWaves * 64) void coupled_walk_kernel(
   if (wave != 0) return;
 
   int st = 0;
-  if (__any(lane < B && (lab < 1 || lab > B))) {
+  const int m = __popcll(__ballot(lane < B && lab >= 1));  // open positions
+  const int g = min(gamma, m);                              // stages walked
+  if (__any(lane < B && (lab < 0 || lab > B))) {
     st = SIMSD_ST_TAU_RANGE;
   } else {
-    // a permutation leaves no stage 1..B without a position
+    // the m open labels must be exactly 1..m: none of them without a position
     bool missing = false;
-    for (int t = 1; t <= B; ++t) missing |= __ballot(lane < B && lab == t) == 0ull;
+    for (int t = 1; t <= m; ++t) missing |= __ballot(lane < B && lab == t) == 0ull;
     if (missing) {
       st = SIMSD_ST_TAU_NOT_PERM;
-    } else if (__any(lane < B && lab <= gamma && (tok < 0 || static_cast<int64_t>(tok) >= V))) {
+    } else if (__any(lane < B && lab >= 1 && lab <= g && (tok < 0 || static_cast<int64_t>(tok) >= V))) {
       st = SIMSD_ST_TOKEN_RANGE;
     }
   }
@@ -192,9 +196,9 @@ __global__ __launch_bounds__(kWalkWaves * 64) void coupled_walk_kernel(
   if (st == 0) {
     // the lane of position k compares its draft with its stage's target
     // token; the first mismatch in stage order ends the walk
-    const bool walked = lane < B && lab <= gamma;
+    const bool walked = lane < B && lab >= 1 && lab <= g;
     const uint64_t miss = __ballot(walked && s_target[walked ? lab - 1 : 0] != tok);
-    n = gamma;
+    n = g;
     if (miss) {
       int first = kMaxB + 1;  // smallest stage label among the mismatching lanes
       for (uint64_t m = miss; m; m &= m - 1) first = min(first, __shfl(lab, __builtin_ctzll(m)));

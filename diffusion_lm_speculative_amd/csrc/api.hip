@@ -342,6 +342,21 @@ int simsd_commit(const int32_t* tau, const int32_t* draft_tok, const int32_t* n_
              : SIMSD_ERR_HIP;
 }
 
+int simsd_next_round(const uint64_t* committed, const int32_t* block_tok, const int32_t* rank,
+                     const int32_t* draft_tok, int32_t batch, int32_t B, int32_t* tau_out, int32_t* tok_out,
+                     void* stream) {
+  if (batch < 0 || B < 0 || B > 64) return SIMSD_ERR_SHAPE;
+  if (batch == 0 || B == 0) return SIMSD_OK;
+  if (!committed || !block_tok || !draft_tok || !tau_out || !tok_out) return SIMSD_ERR_NULL;
+  if (!aligned(committed, 8) || !aligned(block_tok, 4) || (rank && !aligned(rank, 4)) || !aligned(draft_tok, 4) ||
+      !aligned(tau_out, 4) || !aligned(tok_out, 4))
+    return SIMSD_ERR_ALIGN;
+  return launch_next_round(committed, block_tok, rank, draft_tok, batch, B, tau_out, tok_out,
+                           static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SIMSD_OK
+             : SIMSD_ERR_HIP;
+}
+
 int simsd_append_kv(const simsd_verify_desc* desc, const void* k_blk, const void* v_blk, const int32_t* pos_d,
                     const uint64_t* committed, int32_t* prompt_len, void* k_cache, void* v_cache, int32_t* status,
                     void* stream) {

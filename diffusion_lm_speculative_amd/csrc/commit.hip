@@ -3,6 +3,10 @@
 // accepted prefix is committed and the process repeats; "Key contributions"
 // item 3: the method runs with a KV cache and blockwise decoding).
 //
+// The next round of a block labels the committed positions 0 (context for
+// every stage, walked by no one) and the open ones 1..m in the drafter's
+// order.
+//
 // commit: one wave per sequence, lane k = response position k.  The
 // positions of stages 1..n take their drafted tokens, the position of stage
 // n+1 the replacement token when the walk drew one; a ballot over the lanes
@@ -39,6 +43,34 @@ __global__ __launch_bounds__(64) void commit_kernel(const int32_t* __restrict__ 
   if (accepted || replaced) block_tok[static_cast<size_t>(b) * B + k] = accepted ? tok : nx;
   const uint64_t bits = __ballot(accepted || replaced);
   if (k == 0) committed[b] |= bits;
+}
+
+// next round: one wave per sequence, lane k = response position k.  A
+// committed position takes stage 0 and its committed token; an open one
+// takes 1 + the number of open positions ahead of it in the drafter's order
+// (rank, then position), and the drafter's token.
+__global__ __launch_bounds__(64) void next_round_kernel(const uint64_t* __restrict__ committed,
+                                                        const int32_t* __restrict__ block_tok,
+                                                        const int32_t* __restrict__ rank,
+                                                        const int32_t* __restrict__ draft, int B, int32_t* tau_out,
+                                                        int32_t* tok_out) {
+  const int b = blockIdx.x;
+  const int k = threadIdx.x;
+  const size_t i = static_cast<size_t>(b) * B + k;
+  const uint64_t c = committed[b];
+  const bool done = k < B && ((c >> k) & 1ull);
+  const bool open = k < B && !done;
+  const int r = (k < B && rank) ? rank[i] : k;
+  int ahead = 0;
+  for (int j = 0; j < B; ++j) {
+    const int rj = __shfl(r, j);
+    const bool oj = !((c >> j) & 1ull);
+    ahead += (oj && (rj < r || (rj == r && j < k))) ? 1 : 0;
+  }
+  if (k < B) {
+    tau_out[i] = open ? ahead + 1 : 0;
+    tok_out[i] = open ? draft[i] : block_tok[i];
+  }
 }
 
 // Whether sequence b's block is appended this call: finished (or no mask
@@ -101,6 +133,13 @@ __global__ __launch_bounds__(64) void append_len_kernel(Plan pl, const uint64_t*
 hipError_t launch_commit(const int32_t* tau, const int32_t* draft, const int32_t* n_acc, const int32_t* next_tok,
                          int NB, int B, uint64_t* committed, int32_t* block_tok, hipStream_t s) {
   hipLaunchKernelGGL(commit_kernel, dim3(NB), dim3(64), 0, s, tau, draft, n_acc, next_tok, B, committed, block_tok);
+  return hipGetLastError();
+}
+
+hipError_t launch_next_round(const uint64_t* committed, const int32_t* block_tok, const int32_t* rank,
+                             const int32_t* draft, int NB, int B, int32_t* tau_out, int32_t* tok_out, hipStream_t s) {
+  hipLaunchKernelGGL(next_round_kernel, dim3(NB), dim3(64), 0, s, committed, block_tok, rank, draft, B, tau_out,
+                     tok_out);
   return hipGetLastError();
 }
 

@@ -40,7 +40,8 @@ template <> struct Elem<uint16_t> {
 // B-bit words: dbits bit j = the row sees data token D_j, mbits bit j = the
 // row sees mask slot D~_j.  Section 2 of the page gives the mask-slot rows
 // (D_j when tau_j < tau_i, D~_j when tau_j >= tau_i); data rows see D_j with
-// tau_j <= tau_i and no slot.  `tau_at(j)` returns the stage of position j
+// tau_j <= tau_i and no slot.  Stage 0 marks a position committed in an
+// earlier round of the block: every slot row of an open position sees it.  `tau_at(j)` returns the stage of position j
 // (from memory, or from another lane's register).
 template <class TauAt>
 __device__ __forceinline__ void mask_row_bits_at(TauAt tau_at, int B, int r, int mode, uint64_t& dbits,
@@ -64,7 +65,7 @@ __device__ __forceinline__ void mask_row_bits_at(TauAt tau_at, int B, int r, int
 }
 
 // The same bits from a wave's view of the stage labels: lanes 0..B-1 hold
-// tau_j in `tau_lane` (1 <= B <= 64), and every lane of the wave calls this
+// tau_j in `tau_lane` (0..B; 1 <= B <= 64), and every lane of the wave calls this
 // (wave ballots).  The D_j row r sees are those with a stage of at most lim,
 // the ballot of tau_j <= lim for the lim of the row; a slot row sees the
 // slots D~_j whose D_j it does not see.
@@ -75,7 +76,7 @@ __device__ __forceinline__ void mask_row_bits_wave(int tau_lane, int lane, int B
   const bool slot_row = r >= B;
   const int lim = slot_row ? ti - 1 : ti;
   uint64_t d = 0;
-  for (int k = 1; k <= B; ++k) {
+  for (int k = 0; k <= B; ++k) {  // lim = 0: the positions committed in earlier rounds
     const uint64_t pk = __ballot(lane < B && tau_lane <= k);
     d = (lim == k) ? pk : d;
   }
@@ -98,7 +99,7 @@ __device__ __forceinline__ int verify_seq_status(const int32_t* tau_b, int B, in
   int st = 0;
   for (int j = 0; j < B; ++j) {
     const int t = tau_b[j];
-    if (t < 1 || t > B) st |= SIMSD_ST_TAU_RANGE;
+    if (t < 0 || t > B) st |= SIMSD_ST_TAU_RANGE;
     if (pos_b && pos_b[j] < 0) st |= SIMSD_ST_POS_NEG;
   }
   if (plen < 0 || plen > p_max) st |= SIMSD_ST_PROMPT_LEN;
@@ -208,6 +209,8 @@ int linear_tile(int64_t M, int N);
 
 hipError_t launch_commit(const int32_t* tau, const int32_t* draft, const int32_t* n_acc, const int32_t* next_tok,
                          int NB, int B, uint64_t* committed, int32_t* block_tok, hipStream_t s);
+hipError_t launch_next_round(const uint64_t* committed, const int32_t* block_tok, const int32_t* rank,
+                             const int32_t* draft, int NB, int B, int32_t* tau_out, int32_t* tok_out, hipStream_t s);
 hipError_t launch_append_kv(const Plan& pl, const void* k_blk, const void* v_blk, const int32_t* pos_d,
                             const uint64_t* committed, int32_t* prompt_len, void* k_cache, void* v_cache,
                             int32_t* status, hipStream_t s);

@@ -332,7 +332,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     tau_v = tp[lane];
     pos_v = pos_b ? tp[64 + lane] : plen + lane;
   }
-  const bool bad_tau = lane < B && (tau_v < 1 || tau_v > B);
+  const bool bad_tau = lane < B && (tau_v < 0 || tau_v > B);
   const bool bad_pos = lane < B && pos_v < 0;
   int st = (__any(bad_tau) ? SIMSD_ST_TAU_RANGE : 0) | (__any(bad_pos) ? SIMSD_ST_POS_NEG : 0);
   if (plen < 0 || plen > pl.p_max) st |= SIMSD_ST_PROMPT_LEN;

@@ -16,7 +16,12 @@
  *   - section 4, pipeline: one target forward computes the logits of all
  *     candidates under that mask; acceptance is standard rejection sampling
  *     walked in the drafted temporal order, committing the longest accepted
- *     prefix.
+ *     prefix, and the process repeats.
+ *
+ * Stage label 0 (read here for the repeated rounds of one block) marks a
+ * response position committed in an earlier round: its token sits in D as
+ * context, every mask slot sees it (0 is below every stage) and no
+ * acceptance walk visits it.  The open positions carry stages 1..m.
  *
  * Conventions where the page is silent: every block row sees the whole
  * prompt prefix [0, P_b); a data row D_i sees D_j when tau(j) <= tau(i) and
@@ -67,8 +72,8 @@ extern "C" {
 #define SIMSD_ERR_KV_CHUNK    (-8) /* kv_chunk not a non-negative multiple of 64 */
 
 /* ---- per-sequence device status flags (OR-ed together) --------------------------- */
-#define SIMSD_ST_TAU_RANGE     1   /* a stage label outside 1..B */
-#define SIMSD_ST_TAU_NOT_PERM  2   /* stage labels repeat (acceptance only) */
+#define SIMSD_ST_TAU_RANGE     1   /* a stage label outside 0..B */
+#define SIMSD_ST_TAU_NOT_PERM  2   /* the nonzero labels are not 1..m (acceptance only) */
 #define SIMSD_ST_PROMPT_LEN    4   /* prompt_len[b] outside [0, p_max] */
 #define SIMSD_ST_TOKEN_RANGE   8   /* a walked draft token outside [0, vocab) */
 #define SIMSD_ST_POS_NEG      16   /* a negative RoPE position in pos_d */
@@ -126,8 +131,10 @@ int simsd_verify_attn_workspace(const simsd_verify_desc* desc, size_t* bytes);
  *  v_cache [NB][Hkv][p_max][d]
  *          (the caches may be NULL when p_max == 0)
  *  prompt_len [NB] int32 P_b in [0, p_max], or NULL meaning p_max.
- *  tau     [NB][B] int32 stage labels 1..B (a permutation; ties are
- *                            tolerated: the mask rules stay well defined).
+ *  tau     [NB][B] int32 stage labels 0..B (a permutation of 1..B, or 0
+ *                            for committed positions and 1..m for the
+ *                            others; ties are tolerated: the mask rules
+ *                            stay well defined).
  *  pos_d   [NB][B] int32 RoPE position of D_k, or NULL meaning P_b + k;
  *                            D~_k takes the same position (COPY) or that
  *                            position + B (SEQUENTIAL).
@@ -162,20 +169,23 @@ int simsd_accept_prefix_workspace(int32_t batch, int32_t B, int64_t vocab, size_
  *                            row k = response position k.
  *  q_draft  [NB][B][V] fp32  draft probabilities for position k.
  *  draft_tok [NB][B] int32   token placed in D_k.
- *  tau      [NB][B] int32    permutation of 1..B.
- *  gamma    0..B             stages walked: stage t = 1..gamma is position
- *                            k_t with tau[k_t] = t.
+ *  tau      [NB][B] int32    0 for committed positions, a permutation of
+ *                            1..m over the m open ones (m = B in a first
+ *                            round).
+ *  gamma    0..B             stages walked: stage t = 1..min(gamma, m) is
+ *                            position k_t with tau[k_t] = t.
  *  seed, offset              Philox4x64-10 (Salmon et al., SC'11) key
  *                            (seed, 0); the acceptance uniform of stage t of
  *                            sequence b is the top 24 bits of word 0 at
  *                            counter (b, t, 0, offset); stage t accepts iff
  *                            u * q[x] < p[x], evaluated exactly in fp64.
- *  n_accepted [NB] int32     accepted prefix length 0..gamma.
+ *  n_accepted [NB] int32     accepted prefix length 0..min(gamma, m).
  *  next_token [NB] int32     or NULL: at the first rejected stage n+1, a
  *                            draw from max(0, p - q) (fp64 prefix sums; the
  *                            uniform is the top 53 bits of word 0 at counter
  *                            (b, n+1, 1, offset)); from p itself when that
- *                            residual is all zero; -1 when n == gamma.
+ *                            residual is all zero; -1 when
+ *                            n == min(gamma, m).
  *  status   [NB] int32 or NULL: SIMSD_ST_TAU_RANGE, SIMSD_ST_TAU_NOT_PERM,
  *                            SIMSD_ST_TOKEN_RANGE; a faulted sequence gets
  *                            n_accepted = next_token = -1.
@@ -209,18 +219,19 @@ int simsd_accept_coupled_workspace(int32_t batch, int32_t B, int64_t vocab, size
  *                             the table of the position drafted into D_k.
  *  draft_tok [NB][B] int32    token placed in D_k (the drafter's noised
  *                             argmax over its own distribution).
- *  tau       [NB][B] int32    permutation of 1..B.
- *  gamma     0..B             stages walked; stage t is position k_t with
- *                             tau[k_t] = t.
+ *  tau       [NB][B] int32    0 for committed positions, a permutation of
+ *                             1..m over the m open ones.
+ *  gamma     0..B             stages walked: t = 1..min(gamma, m), stage t is
+ *                             position k_t with tau[k_t] = t.
  *  The target token of a row is argmax_v p_v / E_v (= argmax ln p_v + g_v),
  *  decided exactly (p_a * E_b against p_b * E_a in fp64, exact for fp32
  *  inputs; equal scores to the smaller index; p_v <= 0 never wins, a row
  *  without a positive p_v has none: -1).
  *  n_accepted [NB] int32      longest prefix of stages whose draft equals the
- *                             target token, 0..gamma.
+ *                             target token, 0..min(gamma, m).
  *  next_token [NB] int32      or NULL: the target token of stage n+1 (a draw
  *                             from p once the noise is marginalised); -1 when
- *                             n == gamma.
+ *                             n == min(gamma, m).
  *  status    [NB] int32 or NULL: SIMSD_ST_TAU_RANGE, SIMSD_ST_TAU_NOT_PERM,
  *                             SIMSD_ST_TOKEN_RANGE; a faulted sequence gets
  *                             n_accepted = next_token = -1.
@@ -298,6 +309,20 @@ int simsd_qkv_proj(const void* x, const void* w_qkv, int64_t M, int32_t H, int32
  * Errors: SIMSD_ERR_SHAPE (B outside 0..64), _NULL, _ALIGN, _HIP. */
 int simsd_commit(const int32_t* tau, const int32_t* draft_tok, const int32_t* n_accepted, const int32_t* next_token,
                  int32_t batch, int32_t B, uint64_t* committed, int32_t* block_tok, void* stream);
+
+/* Stage labels and data tokens of the block's next round.  Position k of
+ * sequence b gets tau 0 and token block_tok[b][k] when bit k of committed[b]
+ * is set; the open positions get stages 1..m in the drafter's order (rank,
+ * smaller first, equal ranks by position; position order when rank is NULL)
+ * and the drafter's tokens draft_tok[b][k].  The drafter itself (its tokens
+ * and order) is the caller's.
+ *  committed [NB] uint64 (8-byte aligned), block_tok, rank, draft_tok
+ *  [NB][B] int32 in; tau_out, tok_out [NB][B] int32 out.
+ * Errors: SIMSD_ERR_SHAPE (batch < 0, B outside 0..64), _NULL, _ALIGN,
+ * _HIP. */
+int simsd_next_round(const uint64_t* committed, const int32_t* block_tok, const int32_t* rank,
+                     const int32_t* draft_tok, int32_t batch, int32_t B, int32_t* tau_out, int32_t* tok_out,
+                     void* stream);
 
 /* Append finished blocks to the KV cache.  For every sequence whose
  * committed[b] has all B bits set (every sequence when committed is NULL):

@@ -39,7 +39,7 @@ def _declared():
 def test_header_declarations_match_binding():
     decl = _declared()
     assert decl == set(L.SIGNATURES), decl ^ set(L.SIGNATURES)
-    assert len(decl) == 14
+    assert len(decl) == 15
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -222,6 +222,16 @@ def test_commit_and_append_reject_on_host(lib):
     for k in ("tau", "x", "n", "nx", "t"):
         assert com(**{k: A + 2}) == L.ERR_ALIGN, k
     assert com(c=A + 4) == L.ERR_ALIGN
+
+    def nxt(c=A, bt=A, r=A, x=A, NB=4, B=8, t=A, o=A):
+        return lib.simsd_next_round(c, bt, r, x, NB, B, t, o, None)
+    assert nxt(NB=0, c=None, bt=None, x=None, t=None, o=None) == 0
+    assert nxt(B=65) == L.ERR_SHAPE and nxt(NB=-2) == L.ERR_SHAPE
+    for k in ("c", "bt", "x", "t", "o"):
+        assert nxt(**{k: None}) == L.ERR_NULL, k
+    for k in ("bt", "r", "x", "t", "o"):
+        assert nxt(**{k: A + 2}) == L.ERR_ALIGN, k
+    assert nxt(c=A + 4) == L.ERR_ALIGN
 
     def app(desc=None, kb=A, vb=A, pos=None, c=None, plen=A, kc=A, vc=A, st=None):
         d = desc if desc is not None else _desc()

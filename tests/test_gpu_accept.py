@@ -97,11 +97,35 @@ def test_greedy_and_equal_distributions():
 
 def test_status_flags():
     inp = synth.make_accept_inputs(4, 3, 20, seed=9)
-    inp["tau"] = torch.tensor([[1, 2, 3], [0, 2, 3], [1, 1, 3], [3, 2, 1]], dtype=torch.int32)
+    inp["tau"] = torch.tensor([[1, 2, 3], [-1, 2, 3], [1, 1, 3], [3, 2, 1]], dtype=torch.int32)
     inp["draft_tok"] = inp["draft_tok"].clone()
     inp["draft_tok"][3, 2] = 20
     n, nx = _check(inp, 3, 1, 0)
     assert n.tolist()[1:] == [-1, -1, -1]
+    # label 0 (committed in an earlier round): open labels must be 1..m, and a
+    # committed position's token is not checked
+    inp["tau"] = torch.tensor([[0, 2, 3], [0, 1, 2], [0, 0, 0], [2, 0, 1]], dtype=torch.int32)
+    inp["draft_tok"][3, 2] = 0
+    inp["draft_tok"][1, 0] = inp["draft_tok"][2, 1] = inp["draft_tok"][3, 1] = -7
+    n, nx = _check(inp, 3, 1, 0)
+    assert n[0] == -1 and n[1] >= 0 and n[2] == 0 and nx[2] == -1 and n[3] >= 0
+
+
+@pytest.mark.parametrize("NB,B,V,gamma", [(48, 8, 1000, 8), (20, 16, 30000, 5), (6, 64, 300, 64)])
+def test_committed_positions_are_not_walked(NB, B, V, gamma):
+    g = torch.Generator().manual_seed(B + V)
+    inp = synth.make_accept_inputs(NB, B, V, seed=B * 3 + gamma)
+    tau = torch.zeros(NB, B, dtype=torch.int32)
+    for b in range(NB):
+        c = b % (B + 1)  # 0..B committed positions
+        open_pos = torch.randperm(B, generator=g)[: B - c]
+        tau[b, open_pos] = (torch.randperm(B - c, generator=g) + 1).to(torch.int32)
+    inp["tau"] = tau
+    inp["draft_tok"] = inp["draft_tok"].clone()
+    inp["draft_tok"][tau == 0] = -3  # never checked
+    inp["q"] = inp["p"] * 0.999 if B == 64 else inp["q"]  # long prefixes on the widest block
+    n, _ = _check(inp, gamma, 41, 2)
+    assert (n >= 0).all()
 
 
 def test_workspace_reused_across_calls_needs_no_clearing():

@@ -26,7 +26,10 @@ def _plant(p, e, x, tau, gamma, seed):
     for b in range(NB):
         m = int(rng.integers(0, gamma + 1)) if gamma else 0
         for t in range(1, m + 1):
-            k = int(np.nonzero(tau[b] == t)[0][0])
+            hit = np.nonzero(tau[b] == t)[0]
+            if not hit.size:  # fewer open positions than stages
+                break
+            k = int(hit[0])
             a = int(target_tokens_ref(p[b, k], e[b, k]))
             if a >= 0:
                 x[b, k] = a
@@ -125,10 +128,27 @@ def test_zero_mass_row_has_no_target_token():
     n, nx = _check(p, e, x, tau, B)
 
 
+@pytest.mark.parametrize("NB,B,V,gamma", [(40, 8, 1000, 8), (17, 16, 8193, 6), (5, 64, 300, 64)])
+def test_committed_positions_are_not_walked(NB, B, V, gamma):
+    inp = synth.make_accept_inputs(NB, B, V, seed=B + gamma)
+    p = inp["p"].numpy()
+    e = synth.make_noise_exp(NB, B, V, seed=B + gamma + 1).numpy()
+    rng = np.random.default_rng(B * 7 + V)
+    tau = np.zeros((NB, B), np.int32)
+    for b in range(NB):
+        c = b % (B + 1)
+        open_pos = rng.permutation(B)[: B - c]
+        tau[b, open_pos] = rng.permutation(B - c) + 1
+    x = _plant(p, e, inp["draft_tok"].numpy(), tau, min(gamma, B), seed=B)
+    x[tau == 0] = -9  # never checked
+    n, _ = _check(p, e, x, tau, gamma)
+    assert (n >= 0).all()
+
+
 def test_faults_and_status():
     NB, B, V, gamma = 8, 8, 500, 6
     p, e, x, tau = _inputs(NB, B, V, gamma, seed=9)
-    tau[1, 3] = 0            # label out of range
+    tau[1, 3] = -1           # label out of range
     tau[2, 3] = tau[2, 4]    # not a permutation
     x[3, int(np.nonzero(tau[3] == 2)[0][0])] = V       # drafted token out of range at a walked stage
     x[4, int(np.nonzero(tau[4] == 7)[0][0])] = -5      # ... at a stage beyond gamma: not checked

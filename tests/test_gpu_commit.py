@@ -1,13 +1,14 @@
 """GPU parity of the commit step between rounds (simsd_commit,
-simsd_append_kv, through the C ABI) against the oracle.
+simsd_next_round, simsd_append_kv, through the C ABI) against the oracle.
 
 Commit is integer work and must match bit for bit.  Appended keys are the
 rotation of the attention kernels (fp32 from an fp64-reduced angle, rounded
 to the cache dtype): within one bf16 ulp of the float64 oracle (fp32: 2e-6),
 and bit-identical to the rotated data rows the attention path itself uses
 (simsd_debug_rope).  Values, untouched cache rows, lengths and flags are
-exact.  A multi-round loop (accept, commit, until the block is full, then
-append) follows the oracle chain round by round.
+exact.  The next round's labels and tokens (simsd_next_round) match the
+oracle exactly, and a multi-round loop (next labels, accept, commit, until
+the block is full, then append) follows the oracle chain round by round.
 """
 import numpy as np
 import pytest
@@ -16,7 +17,8 @@ import torch
 import diffusion_lm_speculative_amd as sd
 from diffusion_lm_speculative_amd import synth
 from oracle.acceptance import accept_ref
-from oracle.commit import append_kv_ref, commit_ref
+from oracle.commit import append_kv_ref, block_done, commit_ref, next_round_ref
+from oracle.coupled import accept_coupled_ref, target_tokens_ref
 from tests.gpu_helpers import dev
 
 pytestmark = pytest.mark.gpu
@@ -104,49 +106,72 @@ def test_appended_keys_equal_the_attention_rotation():
             assert torch.equal(kc[b, h, P:P + B], k_rot[b, :B, h]), (b, h)
 
 
-def test_multi_round_loop_follows_the_oracle_chain():
-    # One block of B positions decoded over rounds: committed positions take
-    # the first stages (in commit order) and carry their tokens with q = p, so
-    # the walk keeps them; open positions are drafted anew in a random order.
+def test_next_round_matches_oracle():
+    g = torch.Generator().manual_seed(3)
+    for NB, B, with_rank in ((64, 8, True), (9, 64, True), (5, 1, False), (33, 16, True), (7, 12, False)):
+        c = torch.randint(0, 2 ** 62, (NB,), generator=g, dtype=torch.int64)
+        if B < 64:
+            c &= (1 << B) - 1
+        c[0] = 0
+        c[1] = (1 << B) - 1 if B < 64 else -1  # every position committed
+        bt = torch.randint(0, 1000, (NB, B), generator=g, dtype=torch.int32)
+        x = torch.randint(1000, 2000, (NB, B), generator=g, dtype=torch.int32)
+        rank = torch.randint(-3, 4, (NB, B), generator=g, dtype=torch.int32) if with_rank else None  # many ties
+        print(f"next_round NB={NB} B={B} rank={with_rank}", flush=True)
+        tau, tok = sd.next_round(c.to(dev()), bt.to(dev()), x.to(dev()), None if rank is None else rank.to(dev()))
+        rtau, rtok = next_round_ref(c.numpy().view(np.uint64), bt.numpy(), None if rank is None else rank.numpy(),
+                                    x.numpy())
+        assert np.array_equal(tau.cpu().numpy(), rtau) and np.array_equal(tok.cpu().numpy(), rtok)
+
+
+@pytest.mark.parametrize("coupled", [False, True])
+def test_multi_round_loop_follows_the_oracle_chain(coupled):
+    # One block of B positions decoded over rounds: each round labels the
+    # committed positions 0 and drafts the open ones in a random order
+    # (simsd_next_round), walks them (rejection sampling, or the coupled-noise
+    # match) and commits the outcome, until the block is finished.
     NB, B, V, Hkv, d, p_max, base = 12, 8, 500, 2, 64, 64, 1e4
-    rng = np.random.default_rng(21)
+    rng = np.random.default_rng(21 + coupled)
     committed = torch.zeros(NB, dtype=torch.int64, device=dev())
     block_tok = torch.full((NB, B), -1, dtype=torch.int32, device=dev())
     r_c = np.zeros(NB, dtype=np.uint64)
     r_t = np.full((NB, B), -1, dtype=np.int32)
-    order = [[] for _ in range(NB)]  # commit order of positions per sequence
     seed = 77
-    for rnd in range(B + 1):
+    rounds = 0
+    for rnd in range(B):
         inp = synth.make_accept_inputs(NB, B, V, seed=100 + rnd)
-        p, q, x = inp["p"].numpy().copy(), inp["q"].numpy().copy(), inp["draft_tok"].numpy().copy()
-        tau = np.zeros((NB, B), dtype=np.int32)
-        for b in range(NB):
-            done = order[b]
-            rest = [k for k in rng.permutation(B).tolist() if k not in done]
-            for t, k in enumerate(done + rest):
-                tau[b, k] = t + 1
-            for k in done:
-                x[b, k] = r_t[b, k]
-                q[b, k] = p[b, k]
-        n, nx, st = sd.accept_prefix(torch.from_numpy(p).to(dev()), torch.from_numpy(q).to(dev()),
-                                     torch.from_numpy(x).to(dev()), torch.from_numpy(tau).to(dev()), B, seed, rnd)
-        rn, rnx, rst = accept_ref(p, q, x, tau, B, seed, rnd)
-        assert np.array_equal(n.cpu().numpy(), rn) and np.array_equal(st.cpu().numpy(), rst)
-        # the replacement token may differ only at a CDF boundary (tested elsewhere); commit the oracle's
-        nx = torch.from_numpy(rnx).to(dev())
-        sd.commit(torch.from_numpy(tau).to(dev()), torch.from_numpy(x).to(dev()), n, nx, committed, block_tok)
-        r_c, r_t = commit_ref(tau, x, rn, rnx, r_c, r_t)
+        p, q = inp["p"].numpy(), inp["q"].numpy()
+        draft = inp["draft_tok"].numpy()
+        rank = rng.integers(0, 4, size=(NB, B)).astype(np.int32)
+        tau, tok = sd.next_round(committed, block_tok, torch.from_numpy(draft).to(dev()),
+                                 torch.from_numpy(rank).to(dev()))
+        rtau, rtok = next_round_ref(r_c, r_t, rank, draft)
+        assert np.array_equal(tau.cpu().numpy(), rtau) and np.array_equal(tok.cpu().numpy(), rtok), rnd
+        if coupled:
+            e = synth.make_noise_exp(NB, B, V, seed=300 + rnd).numpy()
+            a = target_tokens_ref(p, e)
+            rtok = np.where(rng.random((NB, B)) < 0.7, a, rtok).astype(np.int32)  # mostly right drafts
+            rtok[rtau == 0] = r_t[rtau == 0]
+            tok = torch.from_numpy(rtok).to(dev())
+            n, nx, st = sd.accept_coupled(torch.from_numpy(p).to(dev()), torch.from_numpy(e).to(dev()), tok, tau, B)
+            rn, rnx, rst = accept_coupled_ref(p, e, rtok, rtau, B)
+            assert np.array_equal(nx.cpu().numpy(), rnx)
+        else:
+            n, nx, st = sd.accept_prefix(torch.from_numpy(p).to(dev()), torch.from_numpy(q).to(dev()), tok, tau, B,
+                                         seed, rnd)
+            rn, rnx, rst = accept_ref(p, q, rtok, rtau, B, seed, rnd)
+            # the replacement token may differ only at a CDF boundary (tested elsewhere); commit the oracle's
+            nx = torch.from_numpy(rnx).to(dev())
+        assert np.array_equal(n.cpu().numpy(), rn) and np.array_equal(st.cpu().numpy(), rst), rnd
+        sd.commit(tau, tok, n, nx, committed, block_tok)
+        r_c, r_t = commit_ref(rtau, rtok, rn, rnx, r_c, r_t)
         torch.cuda.synchronize()
         assert np.array_equal(_masks_np(committed), r_c) and np.array_equal(block_tok.cpu().numpy(), r_t), rnd
-        for b in range(NB):
-            inv = {int(tau[b, k]): k for k in range(B)}
-            new = [inv[t] for t in range(1, int(rn[b]) + 1) if inv[t] not in order[b]]
-            if rnx[b] >= 0 and int(rn[b]) + 1 in inv:
-                new.append(inv[int(rn[b]) + 1])
-            order[b] += [k for k in new if k not in order[b]]
-        if all(len(o) == B for o in order):
+        rounds += 1
+        if block_done(r_c, B).all():
             break
-    assert all(len(o) == B for o in order), "every block completes within B rounds"
+    assert block_done(r_c, B).all(), "every block completes within B rounds"
+    print(f"  blocks finished in {rounds} rounds", flush=True)
     # the finished blocks join the cache
     g = torch.Generator().manual_seed(5)
     k_blk = (torch.randn(NB, 2 * B, Hkv, d, generator=g) * 0.5).to(torch.bfloat16)

@@ -29,11 +29,17 @@ def _words(vis, B):
 
 
 @pytest.mark.parametrize("B", [1, 2, 3, 4, 7, 8, 16, 31, 32, 33, 63, 64])
-@pytest.mark.parametrize("ties", [False, True])
+@pytest.mark.parametrize("ties", [False, True, "committed"])
 def test_mask_bits_exact(B, ties):
-    g = torch.Generator().manual_seed(B * 7 + ties)
+    g = torch.Generator().manual_seed(B * 7 + (2 if ties == "committed" else int(ties)))
     NB = 6
-    if ties:
+    if ties == "committed":  # label 0 for a random share of positions, the open ones 1..m
+        tau = torch.zeros(NB, B, dtype=torch.int64)
+        for b in range(NB):
+            c = int(torch.randint(0, B + 1, (1,), generator=g)) if b else B  # sequence 0: all committed
+            open_pos = torch.randperm(B, generator=g)[: B - c]
+            tau[b, open_pos] = torch.randperm(B - c, generator=g) + 1
+    elif ties:
         tau = torch.randint(1, B + 1, (NB, B), generator=g)
     else:
         tau = torch.stack([torch.randperm(B, generator=g) + 1 for _ in range(NB)])

@@ -196,6 +196,29 @@ def test_tied_stage_labels(kind, B, P, impl):
         _check(t, w, f"ties {kind} seq impl={impl}", impl=impl, rope_mode=sd.ROPE_SEQUENTIAL)
 
 
+def _committed_tau(NB, B, g):
+    """Label 0 for positions committed in an earlier round (a different
+    count per sequence, all of them in sequence 0), 1..m for the open ones."""
+    tau = torch.zeros(NB, B, dtype=torch.int32)
+    for b in range(NB):
+        c = B if b == 0 else 1 + (b * 5) % B
+        open_pos = torch.randperm(B, generator=g)[: B - c]
+        tau[b, open_pos] = (torch.randperm(B - c, generator=g) + 1).to(torch.int32)
+    return tau
+
+
+@pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
+@pytest.mark.parametrize("B,P", [(4, 17), (8, 300), (16, 130)])
+def test_committed_positions(B, P, impl):
+    # later rounds of a block: committed positions carry label 0
+    w = _w(NB=4, Hq=8, Hkv=2, P=P, p_lo=0, B=B)
+    t = gpu_inputs(w, 131 + B + P)
+    t["tau"] = _committed_tau(w.NB, B, torch.Generator().manual_seed(B + P)).to(dev())
+    _check(t, w, f"committed B={B} P={P} impl={impl}", impl=impl)
+    if B == 8:
+        _check(t, w, f"committed seq impl={impl}", impl=impl, rope_mode=sd.ROPE_SEQUENTIAL)
+
+
 @pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
 def test_faulted_sequences(impl):
     w = _w(NB=4, Hq=8, Hkv=2, P=80, B=4)
