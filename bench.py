@@ -208,8 +208,9 @@ def projection_measure(torch, sd, synth, dev, stream, steps, warmup):
 
 
 def commit_measure(torch, sd, w, sets, dev, stream, steps):
-    """The commit step of the headline workload: simsd_commit of one round
-    (the accept outputs of an input set) and simsd_append_kv of the finished
+    """The commit step of the headline workload: simsd_next_round (the next
+    round's labels and tokens), simsd_commit of one round (the accept outputs
+    of an input set) and simsd_append_kv of the finished
     blocks (every block counted as finished: 32 sequences x 8 data rows x 8
     KV heads of K and V, keys rotated) into a cache with room for the 8 calls
     of a timed block (the lengths are reset between blocks, outside the
@@ -222,7 +223,12 @@ def commit_measure(torch, sd, w, sets, dev, stream, steps):
     kc = torch.zeros((NB, w.Hkv, p_max, w.d), dtype=w.dtype, device=dev)
     vc = torch.zeros_like(kc)
     plen = torch.full((NB,), w.P, dtype=torch.int32, device=dev)
+    rank = torch.randint(0, B, (NB, B), dtype=torch.int32, device=dev)
+    tau_next = torch.empty((NB, B), dtype=torch.int32, device=dev)
+    tok_next = torch.empty_like(tau_next)
     calls = {
+        "next_round": sd.bind_next_round(committed, block_tok, s["a"]["draft_tok"], rank, tau_next, tok_next,
+                                         stream=stream),
         "commit": sd.bind_commit(s["a"]["tau"], s["a"]["draft_tok"], s["n_acc"], s["nxt"], committed, block_tok,
                                  stream=stream),
         "append_kv": sd.bind_append_kv(s["t"]["k_blk"], s["t"]["v_blk"], kc, vc, plen, rope_base=w.rope_base,
