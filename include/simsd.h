@@ -33,8 +33,9 @@
  *   - All array arguments are device pointers to contiguous, caller-owned
  *     memory, 16-byte aligned (4-byte for int32 arrays), except the
  *     descriptor and the size outputs of the *_workspace queries, which are
- *     host pointers.  Inputs are never written; in particular the KV cache is
- *     read-only.
+ *     host pointers.  Inputs are never written; the KV cache is read-only
+ *     for every call except simsd_append_kv, which appends committed blocks
+ *     (buffers documented as in/out are updated in place).
  *   - The library allocates nothing.  Scratch memory is a caller-provided
  *     workspace sized by the matching *_workspace query.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the legacy
