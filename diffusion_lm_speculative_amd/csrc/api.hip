@@ -164,7 +164,7 @@ int linear_checks(const void* x, const void* w, int64_t M, int64_t N, int64_t K)
 
 extern "C" {
 
-int simsd_abi_version(void) { return 2; }
+int simsd_abi_version(void) { return 3; }
 
 const char* simsd_strerror(int code) {
   switch (code) {

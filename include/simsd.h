@@ -344,7 +344,7 @@ int simsd_append_kv(const simsd_verify_desc* desc, const void* k_blk, const void
 /* Human-readable text for a return code (static storage). */
 const char* simsd_strerror(int code);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3. */
 int simsd_abi_version(void);
 
 #ifdef __cplusplus
