@@ -367,41 +367,40 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   }
   issue_range(issued, min(NPRO, T), c1);
 
-  // ---- rotate the staged query rows in place (one granule pair per item)
-  for (int it = tid; it < ROWS * (L::GR / 2); it += NT) {
-    const int lr = it / (L::GR / 2), j = it % (L::GR / 2);
-    const int mq = rg * pl.rows_wg + lr;
-    if (mq >= pl.M) continue;
-    unsigned char* qrow = smem + S::qrow(lr);
-    uint4* px = reinterpret_cast<uint4*>(qrow + ((j ^ (lr & (L::GR - 1))) << 4));
-    uint4* py = reinterpret_cast<uint4*>(qrow + (((j + L::GR / 2) ^ (lr & (L::GR - 1))) << 4));
-    const uint4 x4 = *px, y4 = *py;
-    const float4* csr = reinterpret_cast<const float4*>(cs_tab + ((mq % twoB) % nent) * HALF + 8 * j);
-    float4 c4[4];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) c4[q4] = csr[q4];
-    const uint32_t wx[4] = {x4.x, x4.y, x4.z, x4.w};
-    const uint32_t wy[4] = {y4.x, y4.y, y4.z, y4.w};
-    uint32_t ox[4], oy[4];
-    rotate8(wx, wy, c4, ox, oy);
-    *px = make_uint4(ox[0], ox[1], ox[2], ox[3]);
-    *py = make_uint4(oy[0], oy[1], oy[2], oy[3]);
-  }
-  lds_barrier<63>();
-
-  // ---- Q operands of this lane's rows
+  // ---- Q operands of this lane's rows, rotated in registers: k-steps i and
+  //      i + KSTEPS/2 of a lane hold the two halves of the same RoPE pairs
+  //      (granules 4i + g and 4i + g + GR/2), so no LDS pass is needed.
   bf16x8 qop[ROWT][KSTEPS];
 #pragma unroll
   for (int rt = 0; rt < ROWT; ++rt) {
     const int lr = (rw * ROWT + rt) * 16 + n;
-    const bool rok = row_m(rt) < pl.M;
+    const int mq = row_m(rt);
+    const bool rok = mq < pl.M;
     const unsigned char* qrow = smem + S::qrow(lr);
+    uint4 wq[KSTEPS];
 #pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) {
-      const uint4 w = rok ? *reinterpret_cast<const uint4*>(qrow + (((4 * i + g) ^ (lr & (L::GR - 1))) << 4))
-                          : make_uint4(0u, 0u, 0u, 0u);
-      qop[rt][i] = __builtin_bit_cast(bf16x8, w);
+    for (int i = 0; i < KSTEPS; ++i)
+      wq[i] = rok ? *reinterpret_cast<const uint4*>(qrow + (((4 * i + g) ^ (lr & (L::GR - 1))) << 4))
+                  : make_uint4(0u, 0u, 0u, 0u);
+    if (rok) {
+      const float2* csr_row = cs_tab + ((mq % twoB) % nent) * HALF;
+#pragma unroll
+      for (int i = 0; i < KSTEPS / 2; ++i) {
+        const float4* csr = reinterpret_cast<const float4*>(csr_row + 8 * (4 * i + g));
+        float4 c4[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) c4[q4] = csr[q4];
+        const uint4 x4 = wq[i], y4 = wq[i + KSTEPS / 2];
+        const uint32_t wx[4] = {x4.x, x4.y, x4.z, x4.w};
+        const uint32_t wy[4] = {y4.x, y4.y, y4.z, y4.w};
+        uint32_t ox[4], oy[4];
+        rotate8(wx, wy, c4, ox, oy);
+        wq[i] = make_uint4(ox[0], ox[1], ox[2], ox[3]);
+        wq[i + KSTEPS / 2] = make_uint4(oy[0], oy[1], oy[2], oy[3]);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) qop[rt][i] = __builtin_bit_cast(bf16x8, wq[i]);
   }
   // Block visibility of row tile rt's row in block tile bt (bit k: key k of
   // the tile), from the stage labels held in lanes 0..B-1 (wave ballots).
