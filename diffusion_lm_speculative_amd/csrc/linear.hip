@@ -24,9 +24,8 @@
 // once).  K advances in slices of 64 through a ring of NSTAGE LDS stages
 // filled by direct-to-LDS loads (global_load_lds_dwordx4, 1 KiB per wave
 // instruction, no register staging); one barrier per slice.  Rows are 128
-// bytes (8 granules of 16 bytes) stored XOR-swizzled so that the 16 rows a
-// 16-lane group reads fall on distinct banks both within 128 and within 256
-// bytes.
+// bytes (8 granules of 16 bytes) stored XOR-swizzled so that the operand
+// reads are free of bank conflicts.
 //
 // Grid.  x = channel block (fastest), y = row block: the hardware hands
 // consecutive workgroups to consecutive XCDs, so with a multiple of 8
@@ -43,11 +42,12 @@ constexpr int kLinThreads = 512;
 constexpr int kLinStages = 4;
 constexpr size_t kLinLdsPerCu = 163840;
 
-// Byte offset of granule g (0..7) of row r in a staged tile: slot
-// g ^ f(r) with f(r) = (r & 7) ^ ((r >> 3) & 1), distinct over any 8
-// consecutive rows and over the even (and the odd) rows of any 16.
+// Byte offset of granule g (0..7) of row r in a staged tile: slot g ^ (r & 7).
+// The 16 rows a 16-lane group reads then take ds_read_b128 at the full 256
+// bytes a cycle (an LDS counter probe on gfx950: 4 cycles per instruction;
+// slot g ^ ((r & 7) ^ ((r >> 3) & 1)) took 8, half of them bank conflicts).
 __device__ __forceinline__ int lin_swz(int r, int g) {
-  return r * kLinRowB + ((g ^ ((r & 7) ^ ((r >> 3) & 1))) << 4);
+  return r * kLinRowB + ((g ^ (r & 7)) << 4);
 }
 
 struct LinearArgs {
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_kernel(LinearArgs a) {
     const bool w = ins >= IA;
     const int r = (w ? ins - IA : ins) * 8 + (lane >> 3);
     const int slot = lane & 7;
-    const int g = slot ^ ((r & 7) ^ ((r >> 3) & 1));
+    const int g = slot ^ (r & 7);
     int64_t row;
     if (w) {
       row = min(n0 + r, a.N - 1) - n0;  // channels past N reload the last one (never stored)

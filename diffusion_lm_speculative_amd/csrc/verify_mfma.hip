@@ -25,10 +25,11 @@
 // Memory pipeline.  K and V tiles of 64 keys stream from HBM straight into a
 // ring of NSTAGE LDS stages with global_load_lds_dwordx4 (no register
 // staging): every wave instruction moves 1 KiB of contiguous cache rows.
-// Rows are stored as 16-byte granules XOR-swizzled by row, which makes both
-// operand reads bank-conflict free: K (A operand of S^T) as ds_read_b128 and
-// V^T (A operand of O^T) as two ds_read_b64_tr_b16 transposed reads from the
-// row-major tile.  All K stages come first in LDS, then all V stages, so the
+// Rows are stored as 16-byte granules XOR-swizzled by row (a different
+// swizzle for K and V tiles, each matched to its read), which keeps both
+// operand reads free of bank conflicts: K (A operand of S^T) as ds_read_b128
+// and V^T (A operand of O^T) as two ds_read_b64_tr_b16 transposed reads from
+// the row-major tile.  All K stages come first in LDS, then all V stages, so the
 // loop (unrolled by NSTAGE) addresses every operand as a loop-invariant
 // per-lane register plus an immediate stage offset.
 //
@@ -62,6 +63,22 @@ struct IC {
 template <int HD>
 __device__ __forceinline__ int swz(int row, int j) {
   return row * Layout<HD>::ROWB + ((j ^ (row & (Layout<HD>::GR - 1))) << 4);
+}
+
+// V tiles: the transposed reads take both granules 2p, 2p+1 of a row in one
+// go, so with the K tiles' swizzle (j ^ row) rows r and r^1 would meet in
+// the same banks.  V rows swizzle by an even rotation of the granule pairs
+// instead: row r XORs j with ((r & 7) << 1) | ((r >> 3) & 1), so the pairs of
+// 8 consecutive rows sit in 8 distinct pair slots.  (Head dim 64 keeps the K
+// swizzle: its 128-byte rows put two rows side by side in the banks.)
+template <int HD>
+__device__ __forceinline__ int vsw(int row) {
+  if constexpr (HD == 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+  return row & (Layout<HD>::GR - 1);
+}
+template <int HD>
+__device__ __forceinline__ int swz_v(int row, int j) {
+  return row * Layout<HD>::ROWB + ((j ^ vsw<HD>(row)) << 4);
 }
 
 // Two wave-uniform 4-byte loads through the scalar cache, waited for here.
@@ -236,9 +253,11 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
 #pragma unroll
   for (int mm = 0; mm < LPW; ++mm) {
     const int ins = wave * LPW + mm;
-    const int ii = ins >= L::IPT ? ins - L::IPT : ins;
+    const bool isv = ins >= L::IPT;
+    const int ii = isv ? ins - L::IPT : ins;
     const int grow = ii * L::RPI + lane / L::GR;
-    goff[mm] = grow * L::ROWB + (((lane % L::GR) ^ (grow & (L::GR - 1))) << 4);
+    const int sw = isv ? vsw<HD>(grow) : (grow & (L::GR - 1));
+    goff[mm] = grow * L::ROWB + (((lane % L::GR) ^ sw) << 4);
   }
   const size_t blk_row = static_cast<size_t>(pl.Hkv) * HD;  // elements between block rows
   const uint16_t* kblk_b = kblk + (static_cast<size_t>(b) * twoB * pl.Hkv + kvh) * HD;
@@ -435,7 +454,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     const int vc4 = lane & 3;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt)
-      vadr[dt] = vbase + swz<HD>(32 * ((ks * NSUB) / 2) + vr, 2 * dt + (vc4 >> 1)) + (vc4 & 1) * 8;
+      vadr[dt] = vbase + swz_v<HD>(32 * ((ks * NSUB) / 2) + vr, 2 * dt + (vc4 >> 1)) + (vc4 & 1) * 8;
   }
 
   // ---- online-softmax state of this wave's share of the keys, per row tile
