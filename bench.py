@@ -109,6 +109,28 @@ def copy_calibration(torch, dev, mib, steps, warmup):
                       "gbs_read_plus_write": 2 * n * 4 / (us * 1e-6) / 1e9}), flush=True)
 
 
+def kernel_only(torch, sd, synth, dev, name, calls):
+    """Repeated calls of one kernel and nothing else, for counter runs: a
+    verification workload by name (one input set), or "projection" (the QKV
+    projection at 512 rows x hidden 4096 -> 6144)."""
+    if name == "projection":
+        x, wt = synth.make_linear_inputs(512, 4096, 6144, seed=3, device=dev)
+        y = torch.empty((512, 6144), dtype=torch.bfloat16, device=dev)
+        call = sd.bind_linear(x, wt, y)
+    else:
+        w = synth.WORKLOADS[name]
+        t = synth.make_verify_inputs(w, 5, device=dev)
+        out = torch.empty_like(t["q_blk"])
+        desc = sd.make_desc(t["q_blk"], t["k_blk"], t["k_cache"], rope_base=w.rope_base)
+        ws = torch.empty(max(sd.verify_workspace_bytes(desc), 256), dtype=torch.uint8, device=dev)
+        call = sd.bind_verify(t["q_blk"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], t["tau"],
+                              t["prompt_len"], None, out=out, workspace=ws, rope_base=w.rope_base)
+    for _ in range(calls):
+        call()
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel_only": name, "calls": calls}), flush=True)
+
+
 def coupled_measure(torch, sd, synth, dev, stream, steps, warmup):
     """Coupled-noise acceptance over full vocabulary rows, timed on its own.
 
@@ -260,6 +282,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--kernel-only", default=None,
+                    help="only repeat one kernel --steps times (a verification workload name, or "
+                         "'projection'), for hardware-counter runs; prints no bench line")
     ap.add_argument("--event-stride", type=int, default=4,
                     help="record the HIP events around verify and accept on every N-th timed step (each event "
                          "packet adds a few microseconds to its step)")
@@ -285,6 +310,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         copy_calibration(torch, dev, args.copy_calibration, args.steps, args.warmup)
+        return
+    if args.kernel_only:
+        kernel_only(torch, sd, synth, dev, args.kernel_only, args.steps)
         return
     w = synth.WORKLOADS[WORKLOAD]
     gamma = w.B

@@ -208,10 +208,10 @@ def _committed_tau(NB, B, g):
 
 
 @pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
-@pytest.mark.parametrize("B,P", [(4, 17), (8, 300), (16, 130)])
+@pytest.mark.parametrize("B,P", [(4, 17), (8, 300), (16, 130), (32, 150), (64, 100)])
 def test_committed_positions(B, P, impl):
     # later rounds of a block: committed positions carry label 0
-    w = _w(NB=4, Hq=8, Hkv=2, P=P, p_lo=0, B=B)
+    w = _w(NB=4, Hq=8 if B < 64 else 4, Hkv=2 if B < 64 else 1, P=P, p_lo=0, B=B)
     t = gpu_inputs(w, 131 + B + P)
     t["tau"] = _committed_tau(w.NB, B, torch.Generator().manual_seed(B + P)).to(dev())
     _check(t, w, f"committed B={B} P={P} impl={impl}", impl=impl)
