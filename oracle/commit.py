@@ -20,7 +20,9 @@ Readings taken where the page is silent (also listed in the design notes):
   D_0..D_{B-1} then join the cache: key k rotated at its RoPE position
   (pos_d[b][k], by default P_b + k, as in the verification pass) and value k
   as is, at cache rows P_b .. P_b + B - 1, and P_b grows by B; a sequence
-  without room (P_b + B > p_max) is flagged and left unchanged;
+  without room (P_b + B > p_max) is flagged and left unchanged, and so is one
+  whose given positions hold a negative entry (the attention's fault flag
+  for such positions);
 * faulted rounds (n < 0) change nothing;
 * the next round of the block (section 4: the process repeats; the drafter
   that proposes tokens and their order is outside this oracle) labels the
@@ -39,7 +41,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import ST_PROMPT_LEN, rope_rotate
+from .attention import ST_POS_NEG, ST_PROMPT_LEN, rope_rotate
 
 
 def commit_ref(tau, draft_tok, n_accepted, next_token, committed, block_tok):
@@ -121,6 +123,9 @@ def append_kv_ref(k_blk, v_blk, pos_d, committed, prompt_len, k_cache, v_cache, 
         P = int(plen[b])
         if P < 0 or P + B > p_max:
             status[b] = ST_PROMPT_LEN
+        if pos_d is not None and np.any(np.asarray(pos_d[b]) < 0):
+            status[b] |= ST_POS_NEG
+        if status[b]:
             continue
         pos = P + np.arange(B) if pos_d is None else np.asarray(pos_d[b], dtype=np.int64)
         kr = rope_rotate(k_blk[b, :B], pos[:, None], rope_base)  # [B][Hkv][d]

@@ -179,3 +179,11 @@ def test_append_skips_open_blocks_and_flags_full_caches():
     assert st.tolist() == [0, 4, 0]
     np.testing.assert_array_equal(kc2[:2], kc[:2])
     np.testing.assert_array_equal(vc2[2, 0, 8:12], v_blk[2, :B, 0])
+    # a negative given position is the attention's fault flag (16), and the
+    # sequence is left unchanged; both flags together when there is no room
+    pos = np.array([[5, 6, 7, 8], [9, 10, -1, 12], [0, 1, 2, -3]])
+    full = np.full(NB, 0b1111, dtype=np.uint64)
+    P = np.array([0, 2, 9])
+    kc3, _, plen3, st3 = append_kv_ref(k_blk, v_blk, pos, full, P, kc, vc, 1e4)
+    assert st3.tolist() == [0, 16, 4 | 16] and plen3.tolist() == [4, 2, 9]
+    np.testing.assert_array_equal(kc3[1:], kc[1:])
