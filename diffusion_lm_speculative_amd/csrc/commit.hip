@@ -73,12 +73,19 @@ __global__ __launch_bounds__(64) void next_round_kernel(const uint64_t* __restri
   }
 }
 
-// Whether sequence b's block is appended this call: finished (or no mask
-// given) and room for B more rows.
-__device__ __forceinline__ bool append_ok(const Plan& pl, const uint64_t* committed, int P, int b) {
+// Whether sequence b's block is finished (every block counts as finished
+// without a mask).
+__device__ __forceinline__ bool block_finished(const Plan& pl, const uint64_t* committed, int b) {
   const uint64_t full = pl.B >= 64 ? ~0ull : ((1ull << pl.B) - 1ull);
-  if (committed && committed[b] != full) return false;
-  return P >= 0 && static_cast<int64_t>(P) + pl.B <= pl.p_max;
+  return !committed || committed[b] == full;
+}
+
+// Fault flags of a finished block's append: no room for B more rows, or a
+// negative given position (the attention's flag for it).  `neg_pos` says
+// whether pos_d holds a negative entry for this sequence.
+__device__ __forceinline__ int append_flags(const Plan& pl, int P, bool neg_pos) {
+  const bool room = P >= 0 && static_cast<int64_t>(P) + pl.B <= pl.p_max;
+  return (room ? 0 : SIMSD_ST_PROMPT_LEN) | (neg_pos ? SIMSD_ST_POS_NEG : 0);
 }
 
 // Rows of one (KV head, sequence): B keys rotated and B values copied.
@@ -92,8 +99,11 @@ __global__ __launch_bounds__(128) void append_rows_kernel(Plan pl, const T* __re
   const int h = blockIdx.x, b = blockIdx.y;
   const int B = pl.B, Hkv = pl.Hkv, d = pl.d, half = d / 2;
   const int P = prompt_len[b];
-  if (!append_ok(pl, committed, P, b)) return;
+  if (!block_finished(pl, committed, b)) return;
   const int32_t* pos_b = pos_d ? pos_d + static_cast<size_t>(b) * B : nullptr;
+  const int lane = threadIdx.x & 63;  // each wave checks the B <= 64 positions itself
+  const bool neg_pos = pos_b && __any(lane < B && pos_b[lane] < 0);
+  if (append_flags(pl, P, neg_pos)) return;
   const size_t cache0 = (static_cast<size_t>(b) * Hkv + h) * pl.p_max + P;
   // keys: one rotation pair (f, f + d/2) per item
   for (int i = threadIdx.x; i < B * half; i += blockDim.x) {
@@ -116,16 +126,22 @@ __global__ __launch_bounds__(128) void append_rows_kernel(Plan pl, const T* __re
 
 // Length and status of each sequence; launched after the rows so that every
 // row workgroup has read the old length.
-__global__ __launch_bounds__(64) void append_len_kernel(Plan pl, const uint64_t* __restrict__ committed,
+__global__ __launch_bounds__(64) void append_len_kernel(Plan pl, const int32_t* __restrict__ pos_d,
+                                                        const uint64_t* __restrict__ committed,
                                                         int32_t* prompt_len, int32_t* status) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= pl.NB) return;
+  if (!block_finished(pl, committed, b)) {  // open block: nothing to do
+    if (status) status[b] = 0;
+    return;
+  }
   const int P = prompt_len[b];
-  const uint64_t full = pl.B >= 64 ? ~0ull : ((1ull << pl.B) - 1ull);
-  const bool open = committed && committed[b] != full;
-  const bool ok = append_ok(pl, committed, P, b);
-  if (ok) prompt_len[b] = P + pl.B;
-  if (status) status[b] = (ok || open) ? 0 : SIMSD_ST_PROMPT_LEN;
+  bool neg_pos = false;
+  if (pos_d)
+    for (int k = 0; k < pl.B; ++k) neg_pos |= pos_d[static_cast<size_t>(b) * pl.B + k] < 0;
+  const int st = append_flags(pl, P, neg_pos);
+  if (st == 0) prompt_len[b] = P + pl.B;
+  if (status) status[b] = st;
 }
 
 }  // namespace
@@ -158,7 +174,8 @@ hipError_t launch_append_kv(const Plan& pl, const void* k_blk, const void* v_blk
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(append_len_kernel, dim3((pl.NB + 63) / 64), dim3(64), 0, s, pl, committed, prompt_len, status);
+  hipLaunchKernelGGL(append_len_kernel, dim3((pl.NB + 63) / 64), dim3(64), 0, s, pl, pos_d, committed, prompt_len,
+                     status);
   return hipGetLastError();
 }
 

@@ -332,7 +332,8 @@ int simsd_next_round(const uint64_t* committed, const int32_t* block_tok, const 
  * k_cache[b][h][P_b + k], the value rows to v_cache, and prompt_len[b] grows
  * by B.  Uses desc's shape, dtype and rope_base (desc->p_max is the cache
  * capacity).  status [NB] (or NULL): 0, or SIMSD_ST_PROMPT_LEN when
- * P_b + B > p_max (that sequence is left unchanged).  The caller provides
+ * P_b + B > p_max and/or SIMSD_ST_POS_NEG when pos_d holds a negative entry
+ * for the sequence (that sequence is left unchanged).  The caller provides
  * k_blk / v_blk computed for the committed tokens.
  *  k_blk, v_blk [NB][2B][Hkv][d] (rows 0..B-1 are read); prompt_len [NB]
  *  int32 in/out; k_cache, v_cache [NB][Hkv][p_max][d] in/out.

@@ -69,6 +69,8 @@ def test_append_matches_oracle(dtype, d, with_pos):
     full = (1 << B) - 1
     committed = torch.tensor([full, full, full, full, full - 1, full], dtype=torch.int64)  # sequence 4 still open
     pos_d = torch.stack([torch.randperm(B, generator=g) * 3 + 50 for _ in range(NB)]).to(torch.int32) if with_pos else None
+    if with_pos:  # negative positions: flagged when finished (alone, and with no room), ignored when open
+        pos_d[5, 2], pos_d[3, 0], pos_d[4, 1] = -4, -1, -2
     ref_k, ref_v, ref_len, ref_st = append_kv_ref(synth.to_numpy64(k_blk), synth.to_numpy64(v_blk),
                                                   None if pos_d is None else pos_d.numpy(),
                                                   committed.numpy().view(np.uint64), plen.numpy(),
@@ -78,6 +80,7 @@ def test_append_matches_oracle(dtype, d, with_pos):
                       committed=committed.to(dev()), pos_d=None if pos_d is None else pos_d.to(dev()))
     torch.cuda.synchronize()
     assert np.array_equal(len_g.cpu().numpy(), ref_len) and np.array_equal(st.cpu().numpy(), ref_st)
+    assert ref_st.tolist() == ([0, 0, 0, 4 | 16, 0, 16] if with_pos else [0, 0, 0, 4, 0, 0])
     np.testing.assert_array_equal(synth.to_numpy64(vc_g), ref_v)
     got_k = synth.to_numpy64(kc_g)
     diff = np.abs(got_k - ref_k)
