@@ -341,13 +341,32 @@ __global__ __launch_bounds__(64) void accept_select_kernel(
   for (int64_t t0 = static_cast<int64_t>(pick) * kChunk; t0 < V && found < 0; t0 += kChunk) {
     const int64_t v0 = t0 + lane * 16;
     double wv[16], sum = 0.0;
+    // a lane's 16 elements: four 16-byte loads each of p and q where the row
+    // allows (the scalar loads they replace cost about 2.7 us a call at
+    // batch 32), else clamped scalar loads
+    float pf[16], qf[16];
+    if (v0 + 16 <= V && (reinterpret_cast<uintptr_t>(pr + v0) % 16) == 0 && (reinterpret_cast<uintptr_t>(qr + v0) % 16) == 0) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 a = reinterpret_cast<const float4*>(pr + v0)[i4];
+        const float4 c = reinterpret_cast<const float4*>(qr + v0)[i4];
+        pf[4 * i4 + 0] = a.x; pf[4 * i4 + 1] = a.y; pf[4 * i4 + 2] = a.z; pf[4 * i4 + 3] = a.w;
+        qf[4 * i4 + 0] = c.x; qf[4 * i4 + 1] = c.y; qf[4 * i4 + 2] = c.z; qf[4 * i4 + 3] = c.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t v = min(v0 + e, V - 1);
+        pf[e] = pr[v];
+        qf[e] = qr[v];
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int64_t v = min(v0 + e, V - 1);
-      const double pv = static_cast<double>(pr[v]);
+      const double pv = static_cast<double>(pf[e]);
       double x = pv;
       if (residual) {
-        const double r = pv - static_cast<double>(qr[v]);
+        const double r = pv - static_cast<double>(qf[e]);
         x = r > 0.0 ? r : 0.0;
       }
       wv[e] = v0 + e < V ? x : 0.0;
