@@ -28,7 +28,14 @@ __global__ __launch_bounds__(256) void merge_kernel(Plan pl, VerifyArgs a) {
   const int32_t* tau_b = a.tau + static_cast<size_t>(b) * pl.B;
   const int32_t* pos_b = a.pos_d ? a.pos_d + static_cast<size_t>(b) * pl.B : nullptr;
   const int plen = a.prompt_len ? a.prompt_len[b] : pl.p_max;
-  if (verify_seq_status(tau_b, pl.B, plen, pl.p_max, pos_b)) {
+  // the sequence's fault flags, with lane j checking position j (B <= 64):
+  // one round of loads instead of B dependent ones
+  bool bad = false;
+  if (lane < pl.B) {
+    const int t = tau_b[lane];
+    bad = t < 0 || t > pl.B || (pos_b && pos_b[lane] < 0);
+  }
+  if (__any(bad) || plen < 0 || plen > pl.p_max) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) Elem<T>::store(op, lane + 64 * e, 0.0f);
     if (a.lse && lane == 0) a.lse[orow] = -INFINITY;
