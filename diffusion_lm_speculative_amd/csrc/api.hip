@@ -367,8 +367,7 @@ int simsd_append_kv(const simsd_verify_desc* desc, const void* k_blk, const void
   if (pl.NB == 0 || pl.B == 0) return SIMSD_OK;
   if (pl.NB > 65535) return SIMSD_ERR_SHAPE;  // one grid row per sequence
   if (!k_blk || !v_blk || !prompt_len || !k_cache || !v_cache) return SIMSD_ERR_NULL;
-  const size_t el = pl.dtype == SIMSD_BF16 ? 2 : 4;
-  if (!aligned(k_blk, el) || !aligned(v_blk, el) || !aligned(k_cache, el) || !aligned(v_cache, el) ||
+  if (!aligned(k_blk, 16) || !aligned(v_blk, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(prompt_len, 4) || (pos_d && !aligned(pos_d, 4)) || (committed && !aligned(committed, 8)) ||
       (status && !aligned(status, 4)))
     return SIMSD_ERR_ALIGN;

@@ -80,6 +80,34 @@ __device__ __forceinline__ bool block_finished(const Plan& pl, const uint64_t* c
   return !committed || committed[b] == full;
 }
 
+// Four consecutive elements of a row (8 bytes of bf16 or 16 of fp32), held
+// as fp32 for the rotation and rounded like Elem<T>::store.
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  float v[4];
+  __device__ static Vec4 load(const float* p) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    return Vec4{{a.x, a.y, a.z, a.w}};
+  }
+  __device__ float get(int j) const { return v[j]; }
+  __device__ void set(int j, float x) { v[j] = x; }
+  __device__ void store(float* p) const { *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]); }
+};
+template <> struct Vec4<uint16_t> {
+  uint16_t v[4];
+  __device__ static Vec4 load(const uint16_t* p) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    return Vec4{{static_cast<uint16_t>(a.x & 0xffffu), static_cast<uint16_t>(a.x >> 16),
+                 static_cast<uint16_t>(a.y & 0xffffu), static_cast<uint16_t>(a.y >> 16)}};
+  }
+  __device__ float get(int j) const { return bf16_bits_to_f32(v[j]); }
+  __device__ void set(int j, float x) { v[j] = f32_to_bf16_bits(x); }
+  __device__ void store(uint16_t* p) const {
+    *reinterpret_cast<uint2*>(p) = make_uint2(v[0] | (static_cast<uint32_t>(v[1]) << 16),
+                                              v[2] | (static_cast<uint32_t>(v[3]) << 16));
+  }
+};
+
 // Fault flags of a finished block's append: no room for B more rows, or a
 // negative given position (the attention's flag for it).  `neg_pos` says
 // whether pos_d holds a negative entry for this sequence.
@@ -105,22 +133,32 @@ __global__ __launch_bounds__(128) void append_rows_kernel(Plan pl, const T* __re
   const bool neg_pos = pos_b && __any(lane < B && pos_b[lane] < 0);
   if (append_flags(pl, P, neg_pos)) return;
   const size_t cache0 = (static_cast<size_t>(b) * Hkv + h) * pl.p_max + P;
-  // keys: one rotation pair (f, f + d/2) per item
-  for (int i = threadIdx.x; i < B * half; i += blockDim.x) {
-    const int f = i % half, k = i / half;
+  // keys: four rotation pairs (f..f+3, f+d/2..f+d/2+3) per item, each half
+  // one 8- or 16-byte access (d/2 is a multiple of 4)
+  const int q4 = half / 4;
+  for (int i = threadIdx.x; i < B * q4; i += blockDim.x) {
+    const int f = (i % q4) * 4, k = i / q4;
     const T* src = k_blk + ((static_cast<size_t>(b) * pl.twoB + k) * Hkv + h) * d;
     T* dst = k_cache + (cache0 + k) * d;
     const int64_t pos = pos_b ? static_cast<int64_t>(pos_b[k]) : static_cast<int64_t>(P) + k;
-    float xo, yo;
-    rope_apply(Elem<T>::load(src, f), Elem<T>::load(src, f + half), rope_cos_sin(pos, rope_inv_freq(f, d, pl.log2_base)),
-               xo, yo);
-    Elem<T>::store(dst, f, xo);
-    Elem<T>::store(dst, f + half, yo);
+    Vec4<T> x = Vec4<T>::load(src + f), y = Vec4<T>::load(src + f + half), xo, yo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a, c;
+      rope_apply(x.get(j), y.get(j), rope_cos_sin(pos, rope_inv_freq(f + j, d, pl.log2_base)), a, c);
+      xo.set(j, a);
+      yo.set(j, c);
+    }
+    xo.store(dst + f);
+    yo.store(dst + f + half);
   }
-  // values
-  for (int i = threadIdx.x; i < B * d; i += blockDim.x) {
-    const int e = i % d, k = i / d;
-    v_cache[(cache0 + k) * d + e] = v_blk[((static_cast<size_t>(b) * pl.twoB + k) * Hkv + h) * d + e];
+  // values: 16-byte copies
+  constexpr int kPer = 16 / sizeof(T);
+  const int dv = d / kPer;
+  for (int i = threadIdx.x; i < B * dv; i += blockDim.x) {
+    const int e = (i % dv) * kPer, k = i / dv;
+    *reinterpret_cast<uint4*>(v_cache + (cache0 + k) * d + e) =
+        *reinterpret_cast<const uint4*>(v_blk + ((static_cast<size_t>(b) * pl.twoB + k) * Hkv + h) * d + e);
   }
 }
 
