@@ -68,7 +68,7 @@ def cpu_baseline(t_host, a_host, w, budget_s=12.0):
     from oracle.acceptance import accept_ref
     from oracle.attention import verify_attn_ref
 
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    cores = len(os.sched_getaffinity(0))  # every core this process may run on
     with threadpool_limits(limits=cores):
         used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         avail = int(t_host["q_blk"].shape[0])
@@ -84,7 +84,8 @@ def cpu_baseline(t_host, a_host, w, budget_s=12.0):
                        a_host["tau"][b].numpy(), w.B, 1234, 0)
             done += 1
         dt = time.perf_counter() - t0
-    return {"value": done * w.B / dt, "unit": "candidates/s", "cores": int(min(used, cores)), "kind": "oracle",
+    return {"value": done * w.B / dt, "unit": "candidates/s", "cores": int(min(used, cores)), "affinity_cores": cores,
+            "kind": "oracle",
             "sample": f"{done} sequence passes cycling over the {avail} sequences of one input set (each: "
                       f"verification attention of {w.Hq} heads x {2 * w.B} rows over {w.P}+{2 * w.B} keys, then the "
                       f"acceptance walk with its residual draw), {dt:.1f} s"}

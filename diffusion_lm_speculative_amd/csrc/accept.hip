@@ -235,15 +235,16 @@ __global__ __launch_bounds__(64) void accept_select_kernel(
     const float* __restrict__ p, const float* __restrict__ q, const int32_t* __restrict__ draft,
     const int32_t* __restrict__ tau, int B, int gamma, int64_t V, uint64_t seed, uint64_t offset, int nch,
     const double* __restrict__ chunk_sums, const WalkRecord* __restrict__ records, int32_t* n_acc,
-    int32_t* next_tok, int32_t* status) {
+    int32_t* next_tok, int32_t* status, int walk_only) {
   __shared__ Walk w;
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
-  if (!next_tok) {  // no replacement draw: only the walk
+  if (walk_only) {  // no replacement draw (none wanted, or no stage to walk): only the walk
     tau_walk(w, p, q, tau + static_cast<size_t>(b) * B, draft + static_cast<size_t>(b) * B, b, B, gamma, V, seed,
              offset, false);
     if (lane == 0) {
       n_acc[b] = w.st ? -1 : w.n;
+      if (next_tok) next_tok[b] = -1;  // n == min(gamma, m) or a fault: no draw
       if (status) status[b] = w.st;
     }
     return;
@@ -407,14 +408,29 @@ void accept_plan(int NB, int64_t V, int& nch, int& cpw, int& ngrp) {
   ngrp = (nch + cpw - 1) / cpw;
 }
 
+// Workspace of a call that can draw a replacement: fp64 (residual, target)
+// sums per row chunk, then a 32-byte walk record per sequence, each region
+// 256-byte aligned.  Zero when there is nothing to walk (B == 0).
+size_t accept_workspace_bytes(int NB, int B, int64_t V) {
+  if (NB == 0 || B == 0) return 0;
+  int nch, cpw, ngrp;
+  accept_plan(NB, V, nch, cpw, ngrp);
+  return (static_cast<size_t>(NB) * nch * 2 * sizeof(double) + 255) / 256 * 256 +
+         (static_cast<size_t>(NB) * sizeof(WalkRecord) + 255) / 256 * 256;
+}
+
 hipError_t launch_accept(const float* p, const float* q, const int32_t* draft, const int32_t* tau,
                          int NB, int B, int gamma, int64_t V, uint64_t seed, uint64_t offset,
                          int32_t* n_acc, int32_t* next_tok, int32_t* status, void* workspace, hipStream_t s) {
   int nch, cpw, ngrp;
   accept_plan(NB, V, nch, cpw, ngrp);
+  // Only a call that can draw a replacement (next_tok wanted, a stage to
+  // walk) streams rows and touches the workspace; otherwise the select
+  // launch alone walks and writes next_tok = -1.
+  const bool draws = next_tok != nullptr && B > 0 && gamma > 0;
   double* chunk_sums = static_cast<double*>(workspace);
   WalkRecord* records = nullptr;
-  if (next_tok) {
+  if (draws) {
     const size_t off = (static_cast<size_t>(NB) * nch * 2 * sizeof(double) + 255) / 256 * 256;
     records = reinterpret_cast<WalkRecord*>(static_cast<char*>(workspace) + off);
     hipLaunchKernelGGL(accept_chunks_kernel, dim3(ngrp, NB), dim3(kAccThreads), 0, s, p, q, draft, tau, B, gamma, V,
@@ -423,7 +439,7 @@ hipError_t launch_accept(const float* p, const float* q, const int32_t* draft, c
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(accept_select_kernel, dim3(NB), dim3(64), 0, s, p, q, draft, tau, B, gamma, V, seed,
-                     offset, nch, chunk_sums, records, n_acc, next_tok, status);
+                     offset, nch, chunk_sums, records, n_acc, next_tok, status, draws ? 0 : 1);
   return hipGetLastError();
 }
 

@@ -129,16 +129,6 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   return SIMSD_OK;
 }
 
-// Acceptance: fp64 (residual, target) sums per row chunk, then a 32-byte
-// walk record per sequence.
-size_t accept_workspace_bytes(int NB, int B, int64_t V) {
-  if (NB == 0 || B == 0) return 0;
-  int nch, cpw, ngrp;
-  accept_plan(NB, V, nch, cpw, ngrp);
-  return round_up(static_cast<size_t>(NB) * nch * 2 * sizeof(double), 256) +
-         round_up(static_cast<size_t>(NB) * 32, 256);
-}
-
 size_t workspace_bytes(const Plan& pl) {
   if (pl.nsplit <= 1 || pl.NB == 0 || pl.B == 0) return 0;
   return round_up(pl.part_o_floats * sizeof(float), 256) + round_up(pl.part_ml_floats * sizeof(float), 256);
@@ -242,7 +232,8 @@ int simsd_verify_attn(const simsd_verify_desc* desc, const void* q_blk, const vo
 
 int simsd_accept_prefix_workspace(int32_t batch, int32_t B, int64_t vocab, size_t* bytes) {
   if (!bytes) return SIMSD_ERR_NULL;
-  if (batch < 0 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31)) return SIMSD_ERR_SHAPE;
+  if (batch < 0 || batch > 65535 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31))
+    return SIMSD_ERR_SHAPE;
   *bytes = accept_workspace_bytes(batch, B, vocab);
   return SIMSD_OK;
 }
@@ -251,7 +242,9 @@ int simsd_accept_prefix(const float* p_target, const float* q_draft, const int32
                         int32_t batch, int32_t B, int32_t gamma, int64_t vocab, uint64_t seed, uint64_t offset,
                         int32_t* n_accepted, int32_t* next_token, int32_t* status, void* workspace,
                         size_t workspace_bytes_in, void* stream) {
-  if (batch < 0 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31)) return SIMSD_ERR_SHAPE;
+  // one grid row per sequence
+  if (batch < 0 || batch > 65535 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31))
+    return SIMSD_ERR_SHAPE;
   if (gamma < 0 || gamma > B) return SIMSD_ERR_GAMMA;
   if (batch == 0) return SIMSD_OK;
   if (!n_accepted || (B > 0 && (!p_target || !q_draft || !draft_tok || !tau))) return SIMSD_ERR_NULL;
@@ -259,7 +252,9 @@ int simsd_accept_prefix(const float* p_target, const float* q_draft, const int32
       (p_target && !aligned(p_target, 4)) || (q_draft && !aligned(q_draft, 4)) ||
       (draft_tok && !aligned(draft_tok, 4)) || (tau && !aligned(tau, 4)))
     return SIMSD_ERR_ALIGN;
-  const size_t need = next_token ? accept_workspace_bytes(batch, B, vocab) : 0;
+  // only a call that can draw a replacement streams rows (B == 0 or
+  // gamma == 0 walks nothing and needs no workspace)
+  const size_t need = (next_token && B > 0 && gamma > 0) ? accept_workspace_bytes(batch, B, vocab) : 0;
   if (need > 0) {
     if (!workspace || workspace_bytes_in < need) return SIMSD_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SIMSD_ERR_ALIGN;

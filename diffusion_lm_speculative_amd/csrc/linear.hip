@@ -208,13 +208,8 @@ template <int BM, int BN>
 hipError_t launch_tile(const LinearArgs& a, hipStream_t s) {
   constexpr size_t lds = lin_lds_bytes(BM, BN);
   static_assert(lds <= kLinLdsPerCu, "LDS");
-  static int attr_set = 0;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(linear_kernel<BM, BN>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_set = 1;
-  }
+  const hipError_t e = allow_dynamic_lds<linear_kernel<BM, BN>>(static_cast<int>(lds));
+  if (e != hipSuccess) return e;
   const dim3 grid(static_cast<unsigned>((a.N + BN - 1) / BN), static_cast<unsigned>((a.M + BM - 1) / BM));
   hipLaunchKernelGGL((linear_kernel<BM, BN>), grid, dim3(kLinThreads), lds, s, a);
   return hipGetLastError();

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "simsd.h"
 
 namespace simsd {
@@ -197,6 +199,27 @@ __device__ __forceinline__ int valid_splits(int plen, int chunk, int nsplit) {
   return n < nsplit ? n : nsplit;
 }
 
+// Let kernel `Kern` use up to `bytes` of dynamic LDS on the current device.
+// The attribute is set once per (kernel, device), under std::call_once, so
+// first launches from several host threads at once do not race; `bytes` must
+// be the same on every call for one kernel (each caller passes its largest).
+template <auto Kern>
+hipError_t allow_dynamic_lds(int bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static hipError_t err[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices)
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  std::call_once(once[dev], [&] {
+    err[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   bytes);
+  });
+  return err[dev];
+}
+
 // Host-side launchers (one per translation unit).
 hipError_t launch_verify_valu(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s);
@@ -218,6 +241,7 @@ hipError_t launch_linear(const uint16_t* x, const uint16_t* w, int64_t M, int N,
                          uint16_t* out0, int ld0, uint16_t* out1, int ld1, uint16_t* out2, int ld2, hipStream_t s);
 hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 void accept_plan(int NB, int64_t V, int& nch, int& cpw, int& ngrp);
+size_t accept_workspace_bytes(int NB, int B, int64_t V);
 int coupled_chunks(int64_t V);
 size_t coupled_workspace_bytes(int NB, int B, int64_t V);
 hipError_t launch_accept_coupled(const float* p, const float* e, const int32_t* draft, const int32_t* tau, int NB,

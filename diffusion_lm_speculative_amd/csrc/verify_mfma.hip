@@ -43,6 +43,7 @@ namespace simsd {
 namespace {
 
 constexpr int KT = 64;  // keys per tile
+constexpr int kLdsMax = 163840;  // LDS bytes of one CU, the most a workgroup may use
 
 template <int HD>
 struct Layout {
@@ -766,13 +767,10 @@ template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT>
 hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
   auto kern = verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT>;
   const size_t lds = mfma_lds_bytes(HD, NSTAGE, pl.tab_rows, RW * ROWT * 16, QSEP);
-  static int attr_set = 0;  // largest dynamic LDS size already allowed for this instantiation
-  if (static_cast<int>(lds) > attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_set = static_cast<int>(lds);
-  }
+  // the table and staged-row sizes vary per call: allow the whole LDS once
+  const hipError_t e = allow_dynamic_lds<verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT>>(kLdsMax);
+  if (e != hipSuccess) return e;
+  if (lds > static_cast<size_t>(kLdsMax)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(pl.Hkv), static_cast<unsigned>(pl.NB) * static_cast<unsigned>(pl.nrg),
                   static_cast<unsigned>(pl.nsplit));
   hipLaunchKernelGGL(kern, grid, dim3(RW * KSPLIT * 64), lds, s, pl, a);

@@ -39,9 +39,11 @@
  *   - The library allocates nothing.  Scratch memory is a caller-provided
  *     workspace sized by the matching *_workspace query.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the legacy
- *     default stream) and never synchronise.  The library holds no state,
- *     so concurrent calls on different streams with disjoint buffers are
- *     safe.
+ *     default stream) and never synchronise.  The library keeps no state
+ *     between calls beyond a kernel attribute (the dynamic LDS limit) that
+ *     is set once per kernel and device under std::call_once, so concurrent
+ *     calls from several host threads, on different streams with disjoint
+ *     buffers and workspaces, are safe.
  *   - A negative return code means the host rejected the arguments before
  *     any HIP call: nothing was launched.  SIMSD_ERR_HIP means a launch was
  *     attempted and HIP reported an error.
@@ -158,13 +160,16 @@ int simsd_verify_attn(const simsd_verify_desc* desc,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes that simsd_accept_prefix needs when next_token is not NULL
- * (host only, no HIP call): fp64 partial sums of the rejected rows and a
- * record of each sequence's walk.  The workspace needs no initialisation; two
- * calls that overlap in time must not share one. */
+ * and B, gamma > 0 (host only, no HIP call): fp64 partial sums of the
+ * rejected rows and a record of each sequence's walk (0 when B == 0).  The
+ * workspace needs no initialisation; two calls that overlap in time must not
+ * share one. */
 int simsd_accept_prefix_workspace(int32_t batch, int32_t B, int64_t vocab, size_t* bytes);
 
 /* Acceptance walk in tau order (section 4 above, read as textbook rejection
- * sampling with residual resampling).
+ * sampling with residual resampling).  Two kernel launches when a
+ * replacement can be drawn (chunk sums of the rejected rows, then the draw),
+ * one otherwise.
  *
  *  p_target [NB][B][V] fp32  target probabilities read at the D~_k slot,
  *                            row k = response position k.
@@ -191,10 +196,12 @@ int simsd_accept_prefix_workspace(int32_t batch, int32_t B, int64_t vocab, size_
  *                            SIMSD_ST_TOKEN_RANGE; a faulted sequence gets
  *                            n_accepted = next_token = -1.
  *  workspace / workspace_bytes: at least simsd_accept_prefix_workspace bytes,
- *                            256-byte aligned, when next_token is not NULL.
+ *                            256-byte aligned, when next_token is not NULL and
+ *                            B, gamma > 0 (otherwise it is never touched and
+ *                            may be NULL).
  *
- * Errors: SIMSD_ERR_NULL, _SHAPE (negative sizes, B > 64, vocab < 1 or
- * >= 2^31), _GAMMA, _WORKSPACE, _ALIGN, _HIP. */
+ * Errors: SIMSD_ERR_NULL, _SHAPE (negative sizes, batch > 65535, B > 64,
+ * vocab < 1 or >= 2^31), _GAMMA, _WORKSPACE, _ALIGN, _HIP. */
 int simsd_accept_prefix(const float* p_target, const float* q_draft,
                         const int32_t* draft_tok, const int32_t* tau,
                         int32_t batch, int32_t B, int32_t gamma, int64_t vocab,

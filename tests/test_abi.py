@@ -146,6 +146,10 @@ def test_workspace_query_sizes(lib):
     # 32-byte walk record per sequence, each part 256-byte aligned
     assert lib.simsd_accept_prefix_workspace(4, 8, 151936, ctypes.byref(n)) == 0
     assert n.value == ru(4 * 149 * 2 * 8) + ru(4 * 32)
+    assert lib.simsd_accept_prefix_workspace(70, 8, 1000, ctypes.byref(n)) == 0
+    assert n.value == ru(70 * 1 * 2 * 8) + ru(70 * 32)
+    # one grid row per sequence
+    assert lib.simsd_accept_prefix_workspace(65536, 8, 1000, ctypes.byref(n)) == L.ERR_SHAPE
     assert lib.simsd_accept_prefix_workspace(4, 0, 151936, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.simsd_accept_prefix_workspace(4, 65, 151936, ctypes.byref(n)) == L.ERR_SHAPE
     assert lib.simsd_accept_prefix_workspace(4, 8, 0, ctypes.byref(n)) == L.ERR_SHAPE
@@ -192,9 +196,9 @@ def test_verify_empty_is_noop(lib):
 
 @no_gpu_only
 def test_accept_rejects_on_host(lib):
-    def call(p=A, q=A, x=A, tau=A, NB=4, B=8, gamma=8, V=1000, n=A, nx=None, st=None):
-        return lib.simsd_accept_prefix(p, q, x, tau, NB, B, gamma, V, 1, 0, n, nx, st, None,
-                                       ctypes.c_size_t(0), None)
+    def call(p=A, q=A, x=A, tau=A, NB=4, B=8, gamma=8, V=1000, n=A, nx=None, st=None, ws=None, wsb=0):
+        return lib.simsd_accept_prefix(p, q, x, tau, NB, B, gamma, V, 1, 0, n, nx, st, ws,
+                                       ctypes.c_size_t(wsb), None)
     assert call(gamma=9) == L.ERR_GAMMA
     assert call(gamma=-1) == L.ERR_GAMMA
     assert call(B=65, gamma=1) == L.ERR_SHAPE
@@ -206,8 +210,11 @@ def test_accept_rejects_on_host(lib):
         assert call(**{k: None}) == L.ERR_NULL, k
     for k in ("p", "q", "x", "tau", "n", "nx", "st"):
         assert call(**{k: A + 2}) == L.ERR_ALIGN, k
-    # the residual draw (next_token != NULL) needs the workspace
+    assert call(NB=65536) == L.ERR_SHAPE
+    # the residual draw (next_token != NULL, B and gamma > 0) needs the workspace
     assert call(nx=A) == L.ERR_WORKSPACE
+    assert call(nx=A, ws=A, wsb=64) == L.ERR_WORKSPACE
+    assert call(nx=A, ws=A + 16, wsb=1 << 20) == L.ERR_ALIGN
 
 
 @no_gpu_only

@@ -138,6 +138,25 @@ def test_workspace_reused_across_calls_needs_no_clearing():
         _check(inp, gamma, seed=31 + i, offset=i, workspace=ws)
 
 
+def test_without_stages_next_token_is_minus_one_and_no_workspace_is_needed():
+    # B == 0 (nothing to walk) and gamma == 0 (no stage walked): n = 0 and
+    # next_token = -1 for every sequence, with a NULL workspace.
+    for NB, B, V, gamma in ((5, 0, 1000, 0), (6, 4, 1000, 0), (2, 0, 151936, 0)):
+        inp = synth.make_accept_inputs(NB, max(B, 1), V, seed=NB + B)
+        p, q = inp["p"][:, :B].contiguous(), inp["q"][:, :B].contiguous()
+        x, tau = inp["draft_tok"][:, :B].contiguous(), inp["tau"][:, :B].contiguous()
+        if B:
+            tau = torch.stack([torch.randperm(B) + 1 for _ in range(NB)]).to(torch.int32)
+        print(f"accept without stages NB={NB} B={B} V={V} gamma={gamma}", flush=True)
+        nx = torch.full((NB,), -7, dtype=torch.int32, device=dev())
+        n, nx, st = sd.accept_prefix(p.to(dev()), q.to(dev()), x.to(dev()), tau.to(dev()), gamma, 3, 0,
+                                     next_token=nx, workspace=None)
+        torch.cuda.synchronize()
+        assert n.cpu().tolist() == [0] * NB
+        assert nx.cpu().tolist() == [-1] * NB
+        assert st.cpu().tolist() == [0] * NB
+
+
 def test_empty_residual_draws_from_target():
     # p = q / 2 (not normalised): a stage rejects when u >= 1/2, and the
     # residual max(0, p - q) is then zero everywhere, so the draw uses p.

@@ -325,14 +325,24 @@ FULL = [
     ("sdar8b_p1024_b4", None),
     ("sdar8b_p4096_b8", [0, 17, 31]),
     ("sdar8b_p8192_b32", [0, 5]),
-    ("sdar8b_var16k_b16_accept", [0, 33, 63]),
+    ("sdar8b_var16k_b16_accept", "by_length"),
 ]
+
+
+def _by_length(prompt_len):
+    """The sequences with the shortest, the median and the longest prompt
+    (the extremes of the ragged last splits), plus sequence 0."""
+    order = torch.argsort(prompt_len.cpu(), stable=True).tolist()
+    return sorted({0, order[0], order[len(order) // 2], order[-1]})
 
 
 @pytest.mark.parametrize("name,b_idx", FULL, ids=[f[0] for f in FULL])
 def test_full_size_workload(name, b_idx):
     w = W[name]
     t = gpu_inputs(w, 1000 + list(W).index(name), on_device=True)
+    if b_idx == "by_length":
+        b_idx = _by_length(t["prompt_len"])
+        print(f"prompt lengths of the checked sequences: {t['prompt_len'][b_idx].tolist()}", flush=True)
     _check(t, w, name, b_idx=b_idx)
     del t
     torch.cuda.empty_cache()
