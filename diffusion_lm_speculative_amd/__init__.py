@@ -13,7 +13,7 @@ from ._lib import (  # noqa: F401
     ST_POS_NEG, ST_PROMPT_LEN, ST_TAU_NOT_PERM, ST_TAU_RANGE, ST_TOKEN_RANGE,
 )
 from .api import (  # noqa: F401
-    accept_coupled, accept_coupled_workspace_bytes, accept_prefix, accept_workspace_bytes, append_kv, bind_accept,
+    accept_coupled, accept_coupled_workspace_bytes, accept_prefix, accept_prefix_noalloc, accept_workspace_bytes, append_kv, bind_accept,
     bind_append_kv, bind_commit, bind_next_round, next_round,
     bind_accept_coupled, bind_linear, bind_qkv_proj, bind_verify, commit, debug_mask, debug_rope, linear, make_desc,
     qkv_proj, verify_attn,

@@ -29,6 +29,7 @@ ERR_GAMMA = -5
 ERR_ALIGN = -6
 ERR_HIP = -7
 ERR_KV_CHUNK = -8
+ERR_SCRATCH = -9
 
 ST_TAU_RANGE = 1
 ST_TAU_NOT_PERM = 2
@@ -72,6 +73,8 @@ SIGNATURES = {
     "simsd_accept_prefix_workspace": (c_int32, [c_int32, c_int32, c_int64, ctypes.POINTER(c_size_t)]),
     "simsd_accept_prefix": (c_int32, [c_void_p] * 4 + [c_int32, c_int32, c_int32, c_int64, c_uint64, c_uint64]
                             + [c_void_p] * 4 + [c_size_t, c_void_p]),
+    "simsd_accept_prefix_noalloc": (c_int32, [c_void_p] * 4 + [c_int32, c_int32, c_int32, c_int64, c_uint64,
+                                                          c_uint64] + [c_void_p] * 4),
     "simsd_accept_coupled_workspace": (c_int32, [c_int32, c_int32, c_int64, ctypes.POINTER(c_size_t)]),
     "simsd_accept_coupled": (c_int32, [c_void_p] * 4 + [c_int32, c_int32, c_int32, c_int64]
                              + [c_void_p] * 4 + [c_size_t, c_void_p]),

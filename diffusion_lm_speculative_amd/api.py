@@ -189,6 +189,36 @@ def accept_prefix(p_target, q_draft, draft_tok, tau, gamma, seed, offset=0, *, n
     return n_accepted, next_token, status
 
 
+def accept_prefix_noalloc(p_target, q_draft, draft_tok, tau, gamma, seed, offset=0, *, n_accepted=None,
+                          next_token=None, status=None, stream=None, with_next=True, with_status=True):
+    """accept_prefix through the entry point that takes no workspace (its
+    scratch is the library's fixed device array); returns (n_accepted,
+    next_token, status)."""
+    lib = L.load()
+    NB, B, V = p_target.shape
+    dev = p_target.device
+    _need(p_target, "p_target", torch.float32)
+    _need(q_draft, "q_draft", torch.float32, (NB, B, V), dev)
+    _need(draft_tok, "draft_tok", torch.int32, (NB, B), dev)
+    _need(tau, "tau", torch.int32, (NB, B), dev)
+    if n_accepted is None:
+        n_accepted = torch.empty((NB,), dtype=torch.int32, device=dev)
+    _need(n_accepted, "n_accepted", torch.int32, (NB,), dev)
+    if next_token is None and with_next:
+        next_token = torch.empty((NB,), dtype=torch.int32, device=dev)
+    if next_token is not None:
+        _need(next_token, "next_token", torch.int32, (NB,), dev)
+    if status is None and with_status:
+        status = torch.empty((NB,), dtype=torch.int32, device=dev)
+    if status is not None:
+        _need(status, "status", torch.int32, (NB,), dev)
+    rc = lib.simsd_accept_prefix_noalloc(_ptr(p_target), _ptr(q_draft), _ptr(draft_tok), _ptr(tau), NB, B,
+                                         int(gamma), V, ctypes.c_uint64(int(seed)), ctypes.c_uint64(int(offset)),
+                                         _ptr(n_accepted), _ptr(next_token), _ptr(status), _stream_handle(stream))
+    L.check(rc, "simsd_accept_prefix_noalloc")
+    return n_accepted, next_token, status
+
+
 def linear(x, w, *, out=None, stream=None):
     """y = x w^T for bf16 x [M][K] and w [N][K] (fp32 accumulation); returns y [M][N] bf16."""
     lib = L.load()

@@ -33,9 +33,21 @@
 // numbers: as easy as 1, 2, 3", SC'11), key (seed, 0); stage t of sequence b
 // uses counter (b, t, 0, offset) and the top 24 bits of word 0; the
 // replacement draw uses counter (b, n+1, 1, offset) and the top 53 bits.
+#include <mutex>
+
 #include "simsd_common.hpp"
 
 namespace simsd {
+
+// Scratch of simsd_accept_prefix_noalloc: the chunk sums and walk records
+// that simsd_accept_prefix keeps in the caller's workspace, in a fixed device
+// array instead (one copy per GPU, held until the process ends).  Host code
+// never passes the array's name to a kernel: the name is a host-side
+// stand-in, and the device address comes from hipGetSymbolAddress, taken once
+// per device.
+constexpr size_t kNoAllocScratchBytes = size_t{4} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace {
 
 constexpr int kAccThreads = 512;
@@ -443,4 +455,47 @@ hipError_t launch_accept(const float* p, const float* q, const int32_t* draft, c
   return hipGetLastError();
 }
 
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+hipError_t scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
 }  // namespace simsd
+
+extern "C" int simsd_accept_prefix_noalloc(const float* p_target, const float* q_draft, const int32_t* draft_tok,
+                                           const int32_t* tau, int32_t batch, int32_t B, int32_t gamma,
+                                           int64_t vocab, uint64_t seed, uint64_t offset, int32_t* n_accepted,
+                                           int32_t* next_token, int32_t* status, void* stream) {
+  using namespace simsd;
+  size_t need = 0;
+  const int rc = accept_prefix_checks(p_target, q_draft, draft_tok, tau, batch, B, gamma, vocab, n_accepted,
+                                      next_token, status, &need);
+  if (rc != SIMSD_OK) return rc;
+  if (need > kNoAllocScratchBytes) return SIMSD_ERR_SCRATCH;
+  if (batch == 0) return SIMSD_OK;
+  void* ws = nullptr;
+  if (need > 0 && scratch_on_current_device(&ws) != hipSuccess) return SIMSD_ERR_HIP;
+  const hipError_t e = launch_accept(p_target, q_draft, draft_tok, tau, batch, B, gamma, vocab, seed, offset,
+                                     n_accepted, next_token, status, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
+}

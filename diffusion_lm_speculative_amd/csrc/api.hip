@@ -129,6 +129,31 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   return SIMSD_OK;
 }
 
+}  // namespace
+
+// Host validation of an accept_prefix call (no HIP call).  On success `need`
+// is the scratch it streams through: nonzero only when a replacement can be
+// drawn (next_token wanted, B and gamma > 0).
+int accept_prefix_checks(const float* p_target, const float* q_draft, const int32_t* draft_tok, const int32_t* tau,
+                         int32_t batch, int32_t B, int32_t gamma, int64_t vocab, const int32_t* n_accepted,
+                         const int32_t* next_token, const int32_t* status, size_t* need) {
+  *need = 0;
+  // one grid row per sequence
+  if (batch < 0 || batch > 65535 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31))
+    return SIMSD_ERR_SHAPE;
+  if (gamma < 0 || gamma > B) return SIMSD_ERR_GAMMA;
+  if (batch == 0) return SIMSD_OK;
+  if (!n_accepted || (B > 0 && (!p_target || !q_draft || !draft_tok || !tau))) return SIMSD_ERR_NULL;
+  if (!aligned(n_accepted, 4) || (next_token && !aligned(next_token, 4)) || (status && !aligned(status, 4)) ||
+      (p_target && !aligned(p_target, 4)) || (q_draft && !aligned(q_draft, 4)) ||
+      (draft_tok && !aligned(draft_tok, 4)) || (tau && !aligned(tau, 4)))
+    return SIMSD_ERR_ALIGN;
+  if (next_token && B > 0 && gamma > 0) *need = accept_workspace_bytes(batch, B, vocab);
+  return SIMSD_OK;
+}
+
+namespace {
+
 size_t workspace_bytes(const Plan& pl) {
   if (pl.nsplit <= 1 || pl.NB == 0 || pl.B == 0) return 0;
   return round_up(pl.part_o_floats * sizeof(float), 256) + round_up(pl.part_ml_floats * sizeof(float), 256);
@@ -154,7 +179,7 @@ int linear_checks(const void* x, const void* w, int64_t M, int64_t N, int64_t K)
 
 extern "C" {
 
-int simsd_abi_version(void) { return 3; }
+int simsd_abi_version(void) { return 4; }
 
 const char* simsd_strerror(int code) {
   switch (code) {
@@ -167,6 +192,7 @@ const char* simsd_strerror(int code) {
     case SIMSD_ERR_ALIGN: return "misaligned pointer";
     case SIMSD_ERR_HIP: return "HIP error at launch";
     case SIMSD_ERR_KV_CHUNK: return "kv_chunk must be a non-negative multiple of 64";
+    case SIMSD_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point's fixed buffer";
     default: return "unknown error code";
   }
 }
@@ -242,19 +268,11 @@ int simsd_accept_prefix(const float* p_target, const float* q_draft, const int32
                         int32_t batch, int32_t B, int32_t gamma, int64_t vocab, uint64_t seed, uint64_t offset,
                         int32_t* n_accepted, int32_t* next_token, int32_t* status, void* workspace,
                         size_t workspace_bytes_in, void* stream) {
-  // one grid row per sequence
-  if (batch < 0 || batch > 65535 || B < 0 || B > 64 || vocab < 1 || vocab >= (int64_t{1} << 31))
-    return SIMSD_ERR_SHAPE;
-  if (gamma < 0 || gamma > B) return SIMSD_ERR_GAMMA;
+  size_t need = 0;
+  const int rc = accept_prefix_checks(p_target, q_draft, draft_tok, tau, batch, B, gamma, vocab, n_accepted,
+                                      next_token, status, &need);
+  if (rc != SIMSD_OK) return rc;
   if (batch == 0) return SIMSD_OK;
-  if (!n_accepted || (B > 0 && (!p_target || !q_draft || !draft_tok || !tau))) return SIMSD_ERR_NULL;
-  if (!aligned(n_accepted, 4) || (next_token && !aligned(next_token, 4)) || (status && !aligned(status, 4)) ||
-      (p_target && !aligned(p_target, 4)) || (q_draft && !aligned(q_draft, 4)) ||
-      (draft_tok && !aligned(draft_tok, 4)) || (tau && !aligned(tau, 4)))
-    return SIMSD_ERR_ALIGN;
-  // only a call that can draw a replacement streams rows (B == 0 or
-  // gamma == 0 walks nothing and needs no workspace)
-  const size_t need = (next_token && B > 0 && gamma > 0) ? accept_workspace_bytes(batch, B, vocab) : 0;
   if (need > 0) {
     if (!workspace || workspace_bytes_in < need) return SIMSD_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SIMSD_ERR_ALIGN;

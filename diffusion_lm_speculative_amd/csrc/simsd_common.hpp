@@ -242,6 +242,9 @@ hipError_t launch_linear(const uint16_t* x, const uint16_t* w, int64_t M, int N,
 hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s);
 void accept_plan(int NB, int64_t V, int& nch, int& cpw, int& ngrp);
 size_t accept_workspace_bytes(int NB, int B, int64_t V);
+int accept_prefix_checks(const float* p_target, const float* q_draft, const int32_t* draft_tok, const int32_t* tau,
+                         int32_t batch, int32_t B, int32_t gamma, int64_t vocab, const int32_t* n_accepted,
+                         const int32_t* next_token, const int32_t* status, size_t* need);
 int coupled_chunks(int64_t V);
 size_t coupled_workspace_bytes(int NB, int B, int64_t V);
 hipError_t launch_accept_coupled(const float* p, const float* e, const int32_t* draft, const int32_t* tau, int NB,

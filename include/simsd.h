@@ -37,7 +37,8 @@
  *     for every call except simsd_append_kv, which appends committed blocks
  *     (buffers documented as in/out are updated in place).
  *   - The library allocates nothing.  Scratch memory is a caller-provided
- *     workspace sized by the matching *_workspace query.
+ *     workspace sized by the matching *_workspace query (except for
+ *     simsd_accept_prefix_noalloc, whose scratch is a fixed device array).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the legacy
  *     default stream) and never synchronise.  The library keeps no state
  *     between calls beyond a kernel attribute (the dynamic LDS limit) that
@@ -73,6 +74,8 @@ extern "C" {
 #define SIMSD_ERR_ALIGN       (-6) /* pointer not aligned as documented */
 #define SIMSD_ERR_HIP         (-7) /* HIP reported an error at launch */
 #define SIMSD_ERR_KV_CHUNK    (-8) /* kv_chunk not a non-negative multiple of 64 */
+#define SIMSD_ERR_SCRATCH     (-9) /* needs more than the no-allocation entry point's fixed
+                                       4 MiB scratch */
 
 /* ---- per-sequence device status flags (OR-ed together) --------------------------- */
 #define SIMSD_ST_TAU_RANGE     1   /* a stage label outside 0..B */
@@ -208,6 +211,28 @@ int simsd_accept_prefix(const float* p_target, const float* q_draft,
                         uint64_t seed, uint64_t offset,
                         int32_t* n_accepted, int32_t* next_token, int32_t* status,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* simsd_accept_prefix without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, outputs and errors as
+ * simsd_accept_prefix; the scratch that call keeps in the workspace (the
+ * chunk sums and walk records, simsd_accept_prefix_workspace bytes) lives in
+ * a fixed 4 MiB device array of the library instead, one per GPU, held until
+ * the process ends.  Nothing in it needs to start at zero (every entry is
+ * written before it is read).  A call that needs more than 4 MiB (about
+ * 1700 sequences at vocab 151936) returns SIMSD_ERR_SCRATCH before any HIP
+ * call.  The array of the current device is used: `stream` must belong to
+ * it.  All calls on one GPU share that array, so two calls that overlap in
+ * time on one GPU (different streams, or different host threads) race;
+ * calls in order on one stream do not.  The entry point itself allocates
+ * nothing: no hipMalloc, hipFree or allocating library routine (the first
+ * call on a device looks the array's address up once). */
+int simsd_accept_prefix_noalloc(const float* p_target, const float* q_draft,
+                                const int32_t* draft_tok, const int32_t* tau,
+                                int32_t batch, int32_t B, int32_t gamma, int64_t vocab,
+                                uint64_t seed, uint64_t offset,
+                                int32_t* n_accepted, int32_t* next_token, int32_t* status,
+                                void* stream);
 
 /* Workspace bytes that simsd_accept_coupled needs (host only, no HIP call):
  * one (p, E, index) winner per 8192-element chunk of every walked row.  It

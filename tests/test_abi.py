@@ -39,7 +39,7 @@ def _declared():
 def test_header_declarations_match_binding():
     decl = _declared()
     assert decl == set(L.SIGNATURES), decl ^ set(L.SIGNATURES)
-    assert len(decl) == 15
+    assert len(decl) == 16
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -51,8 +51,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.simsd_abi_version() == 3
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    assert lib.simsd_abi_version() == 4
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert lib.simsd_strerror(code)
     assert lib.simsd_strerror(-99) == b"unknown error code"
 
@@ -215,6 +215,28 @@ def test_accept_rejects_on_host(lib):
     assert call(nx=A) == L.ERR_WORKSPACE
     assert call(nx=A, ws=A, wsb=64) == L.ERR_WORKSPACE
     assert call(nx=A, ws=A + 16, wsb=1 << 20) == L.ERR_ALIGN
+
+
+@no_gpu_only
+def test_accept_noalloc_rejects_on_host(lib):
+    def call(p=A, q=A, x=A, tau=A, NB=4, B=8, gamma=8, V=1000, n=A, nx=A, st=None):
+        return lib.simsd_accept_prefix_noalloc(p, q, x, tau, NB, B, gamma, V, 1, 0, n, nx, st, None)
+    # the same checks as simsd_accept_prefix
+    assert call(gamma=9) == L.ERR_GAMMA
+    assert call(B=65, gamma=1) == L.ERR_SHAPE
+    assert call(NB=65536) == L.ERR_SHAPE
+    assert call(V=0) == L.ERR_SHAPE
+    for k in ("p", "q", "x", "tau", "n"):
+        assert call(**{k: None}) == L.ERR_NULL, k
+    for k in ("p", "q", "x", "tau", "n", "nx", "st"):
+        assert call(**{k: A + 2}) == L.ERR_ALIGN, k
+    assert call(NB=0, p=None, q=None, x=None, tau=None, n=None) == 0
+    # scratch needed above the fixed 4 MiB: rejected before any HIP call
+    n = ctypes.c_size_t(0)
+    assert lib.simsd_accept_prefix_workspace(1800, 16, 151936, ctypes.byref(n)) == 0 and n.value > 4 << 20
+    assert call(NB=1800, B=16, gamma=16, V=151936) == L.ERR_SCRATCH
+    assert call(NB=1, B=2, gamma=2, V=(1 << 31) - 1) == L.ERR_SCRATCH
+    assert lib.simsd_strerror(L.ERR_SCRATCH) != b"unknown error code"
 
 
 @no_gpu_only
