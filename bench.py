@@ -91,6 +91,41 @@ def cpu_baseline(t_host, a_host, w, budget_s=12.0):
                       f"acceptance walk with its residual draw), {dt:.1f} s"}
 
 
+def call_event_times(torch, sets, stream, n=40):
+    """Verify calls timed with events recorded on the stream around each call
+    (ms, sorted): the kernel time plus the marker packets' overhead."""
+    res = []
+    for i in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sets[i % 2]["call"]()
+        e1.record(stream)
+        e1.synchronize()
+        res.append(e0.elapsed_time(e1))
+    return sorted(res)
+
+
+def stream_probe_measure(torch, sd, t, dev, stream, kv_bytes, n=30, warmup=5):
+    """The attention kernel's load path alone over the same prompt cache
+    (kernel-bound events): the streaming ceiling of that path on this GPU."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    for _ in range(warmup):
+        sd.stream_probe(t["k_cache"], t["v_cache"], sink, stream=stream)
+    for a, b in evs:
+        sd.stream_probe(t["k_cache"], t["v_cache"], sink, a, b, stream=stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    mean = sum(us) / len(us)
+    gbs = kv_bytes / (mean * 1e-6) / 1e9
+    return {"what": "the attention kernel's K/V load path alone (same ring, grid and cache), no attention",
+            "us": {"mean": mean, "median": us[len(us) // 2], "min": us[0]}, "bytes": kv_bytes,
+            "achieved_gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+
 def copy_calibration(torch, dev, mib, steps, warmup):
     """A plain copy of known size: each launch reads and writes mib MiB once."""
     n = (mib << 20) // 4
@@ -286,11 +321,15 @@ def main():
     ap.add_argument("--kernel-only", default=None,
                     help="only repeat one kernel --steps times (a verification workload name, or "
                          "'projection'), for hardware-counter runs; prints no bench line")
-    ap.add_argument("--event-stride", type=int, default=4,
-                    help="record the HIP events around verify and accept on every N-th timed step (each event "
-                         "packet adds a few microseconds to its step)")
+    ap.add_argument("--event-stride", type=int, default=5,
+                    help="time verify and accept on every N-th timed step (each event packet adds a few "
+                         "microseconds to its step); N odd, so that the two alternating input sets are sampled "
+                         "equally")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the host oracle timing")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only run the streaming probe over the bench workload's prompt cache --steps times "
+                         "(for kernel-trace runs); prints its JSON")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the bench, time a plain device-to-device copy of MIB MiB (the known-size "
                          "reference that HBM byte counters are scaled by)")
@@ -318,6 +357,11 @@ def main():
     w = synth.WORKLOADS[WORKLOAD]
     gamma = w.B
     stream = torch.cuda.current_stream()
+    if args.stream_probe:
+        t = synth.make_verify_inputs(w, 1002, device=dev)
+        print(json.dumps({"stream_probe": stream_probe_measure(torch, sd, t, dev, stream, w.kv_bytes(),
+                                                               n=args.steps)}), flush=True)
+        return
 
     # Two input sets (each ~537 MB of K/V, together > the 256 MB last-level cache).
     sets = []
@@ -348,13 +392,17 @@ def main():
                          nxt=nxt, ast=ast, aws=aws))
     torch.cuda.synchronize()
 
+    # On the event steps the verify call takes its two events bound to its own
+    # kernel (start and end of the attention kernel, hipExtLaunchKernel):
+    # events recorded around the call add marker packets whose few
+    # microseconds are not the kernel's.  The acceptance is timed from the
+    # end of that kernel to an event recorded after the acceptance call.
     def step(i, ev=None):
         s = sets[i % 2]
         if ev is not None:
-            ev[0].record(stream)
-        s["call"]()
-        if ev is not None:
-            ev[1].record(stream)
+            s["call"].timed(ev[0], ev[1])
+        else:
+            s["call"]()
         s["accept"]()
         if ev is not None:
             ev[2].record(stream)
@@ -371,7 +419,12 @@ def main():
         step(i)
 
     stride = max(1, args.event_stride)
+    if stride % 2 == 0:
+        stride += 1  # an even stride would time only one of the two alternating input sets
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(0, args.steps, stride)]
+    for e in evs:  # HIP creates an event at its first record; the kernel-bound ones then re-record it
+        e[0].record(stream)
+        e[1].record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -389,6 +442,8 @@ def main():
     desc = sd.make_desc(sets[0]["t"]["q_blk"], sets[0]["t"]["k_blk"], sets[0]["t"]["k_cache"], rope_base=w.rope_base)
     traffic = measured_traffic()
 
+    call_ms = call_event_times(torch, sets, stream)
+    probe = stream_probe_measure(torch, sd, sets[0]["t"], dev, stream, kv_bytes)
     coupled = coupled_measure(torch, sd, synth, dev, stream, args.steps, args.warmup)
     projections = projection_measure(torch, sd, synth, dev, stream, args.steps, args.warmup)
     commit_times = commit_measure(torch, sd, w, sets, dev, stream, args.steps)
@@ -421,7 +476,10 @@ def main():
         "kv_tb_per_s": achieved_gbs / 1e3,
         "verify_us": {"mean": v_avg * 1e3, "median": verify_ms[len(verify_ms) // 2] * 1e3,
                       "p90": verify_ms[int(len(verify_ms) * 0.9)] * 1e3, "samples": len(verify_ms),
-                      "event_stride": stride},
+                      "event_stride": stride, "events": "bound to the attention kernel's own dispatch"},
+        "verify_call_us": {"mean": sum(call_ms) / len(call_ms) * 1e3, "median": call_ms[len(call_ms) // 2] * 1e3,
+                           "samples": len(call_ms), "events": "recorded on the stream around each call"},
+        "stream_probe": probe,
         "accept_us": {"mean": a_avg * 1e3, "median": accept_ms[len(accept_ms) // 2] * 1e3},
         "workspace_bytes": sd.verify_workspace_bytes(desc),
         "cpu_baseline": cpu,

@@ -70,6 +70,8 @@ class VerifyDesc(ctypes.Structure):
 SIGNATURES = {
     "simsd_verify_attn_workspace": (c_int32, [ctypes.POINTER(VerifyDesc), ctypes.POINTER(c_size_t)]),
     "simsd_verify_attn": (c_int32, [ctypes.POINTER(VerifyDesc)] + [c_void_p] * 12 + [c_size_t, c_void_p]),
+    "simsd_verify_attn_timed": (c_int32, [ctypes.POINTER(VerifyDesc)] + [c_void_p] * 12 + [c_size_t, c_void_p,
+                                                                                         c_void_p, c_void_p]),
     "simsd_accept_prefix_workspace": (c_int32, [c_int32, c_int32, c_int64, ctypes.POINTER(c_size_t)]),
     "simsd_accept_prefix": (c_int32, [c_void_p] * 4 + [c_int32, c_int32, c_int32, c_int64, c_uint64, c_uint64]
                             + [c_void_p] * 4 + [c_size_t, c_void_p]),
@@ -80,6 +82,8 @@ SIGNATURES = {
                              + [c_void_p] * 4 + [c_size_t, c_void_p]),
     "simsd_debug_mask": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "simsd_debug_rope": (c_int32, [ctypes.POINTER(VerifyDesc)] + [c_void_p] * 7),
+    "simsd_stream_probe": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                     c_void_p, c_void_p]),
     "simsd_strerror": (ctypes.c_char_p, [c_int32]),
     "simsd_abi_version": (c_int32, []),
     "simsd_commit": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,

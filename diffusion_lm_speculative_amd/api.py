@@ -133,6 +133,15 @@ class VerifyCall:
         if rc:
             L.check(rc, "simsd_verify_attn")
 
+    def timed(self, start, stop):
+        """The same call with `start` / `stop` (torch.cuda.Event with timing,
+        each recorded once before so that it exists) bound to the pass's own
+        kernels: start of the attention kernel, end of the last kernel."""
+        rc = L.load().simsd_verify_attn_timed(ctypes.byref(self.desc), *self.args,
+                                              ctypes.c_void_p(start.cuda_event), ctypes.c_void_p(stop.cuda_event))
+        if rc:
+            L.check(rc, "simsd_verify_attn_timed")
+
 
 def bind_verify(q_blk, k_blk, v_blk, k_cache, v_cache, tau, prompt_len=None, pos_d=None, *, out, lse=None,
                 status=None, workspace=None, stream=None, **desc_kw) -> VerifyCall:
@@ -507,6 +516,20 @@ def bind_accept_coupled(p_target, noise_exp, draft_tok, tau, gamma, *, n_accepte
     args = (_ptr(p_target), _ptr(noise_exp), _ptr(draft_tok), _ptr(tau), NB, B, int(gamma), V, _ptr(n_accepted),
             _ptr(next_token), _ptr(status), _ptr(workspace), ctypes.c_size_t(ws_len), _stream_handle(stream))
     return CoupledCall(args, (p_target, noise_exp, draft_tok, tau, n_accepted, next_token, status, workspace))
+
+
+def stream_probe(k_cache, v_cache, sink, start=None, stop=None, stream=None):
+    """The attention kernel's load path alone over a prompt cache [NB][Hkv][P][d]
+    (bf16): the streaming ceiling it is compared with.  `start` / `stop`
+    (torch.cuda.Event, each recorded once before) take the kernel's own start
+    and end."""
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(v_cache, "v_cache", torch.bfloat16, tuple(k_cache.shape), k_cache.device)
+    _need(sink, "sink", torch.int32, None, k_cache.device)
+    NB, Hkv, P, d = k_cache.shape
+    ev = [ctypes.c_void_p(0 if e is None else e.cuda_event) for e in (start, stop)]
+    L.check(L.load().simsd_stream_probe(_ptr(k_cache), _ptr(v_cache), Hkv, NB, P, d, _ptr(sink),
+                                        _stream_handle(stream), *ev), "simsd_stream_probe")
 
 
 def debug_mask(tau, mask_mode=L.MASK_TEMPORAL, stream=None):

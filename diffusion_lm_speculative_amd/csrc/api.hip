@@ -206,10 +206,11 @@ int simsd_verify_attn_workspace(const simsd_verify_desc* desc, size_t* bytes) {
   return SIMSD_OK;
 }
 
-int simsd_verify_attn(const simsd_verify_desc* desc, const void* q_blk, const void* k_blk, const void* v_blk,
-                      const void* k_cache, const void* v_cache, const int32_t* prompt_len, const int32_t* tau,
-                      const int32_t* pos_d, void* out, float* lse, int32_t* status, void* workspace,
-                      size_t workspace_bytes_in, void* stream) {
+namespace {
+int verify_attn_impl(const simsd_verify_desc* desc, const void* q_blk, const void* k_blk, const void* v_blk,
+                     const void* k_cache, const void* v_cache, const int32_t* prompt_len, const int32_t* tau,
+                     const int32_t* pos_d, void* out, float* lse, int32_t* status, void* workspace,
+                     size_t workspace_bytes_in, void* stream, PassEvents ev) {
   if (!desc) return SIMSD_ERR_NULL;
   Plan pl;
   const int rc = make_plan(*desc, pl);
@@ -247,13 +248,34 @@ int simsd_verify_attn(const simsd_verify_desc* desc, const void* q_blk, const vo
                                          round_up(pl.part_o_floats * sizeof(float), 256));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = pl.impl == SIMSD_IMPL_MFMA ? launch_verify_mfma(pl, a, s) : launch_verify_valu(pl, a, s);
+  // the start event goes with the attention kernel, the stop event with the
+  // last kernel of the pass (the merge when the prompt is split)
+  const PassEvents first{ev.start, pl.nsplit > 1 ? nullptr : ev.stop};
+  hipError_t e = pl.impl == SIMSD_IMPL_MFMA ? launch_verify_mfma(pl, a, s, first) : launch_verify_valu(pl, a, s, first);
   if (e != hipSuccess) return SIMSD_ERR_HIP;
   if (pl.nsplit > 1) {
-    e = launch_merge(pl, a, s);
+    e = launch_merge(pl, a, s, PassEvents{nullptr, ev.stop});
     if (e != hipSuccess) return SIMSD_ERR_HIP;
   }
   return SIMSD_OK;
+}
+}  // namespace
+
+int simsd_verify_attn(const simsd_verify_desc* desc, const void* q_blk, const void* k_blk, const void* v_blk,
+                      const void* k_cache, const void* v_cache, const int32_t* prompt_len, const int32_t* tau,
+                      const int32_t* pos_d, void* out, float* lse, int32_t* status, void* workspace,
+                      size_t workspace_bytes_in, void* stream) {
+  return verify_attn_impl(desc, q_blk, k_blk, v_blk, k_cache, v_cache, prompt_len, tau, pos_d, out, lse, status,
+                          workspace, workspace_bytes_in, stream, PassEvents{});
+}
+
+int simsd_verify_attn_timed(const simsd_verify_desc* desc, const void* q_blk, const void* k_blk, const void* v_blk,
+                            const void* k_cache, const void* v_cache, const int32_t* prompt_len, const int32_t* tau,
+                            const int32_t* pos_d, void* out, float* lse, int32_t* status, void* workspace,
+                            size_t workspace_bytes_in, void* stream, void* start_event, void* stop_event) {
+  return verify_attn_impl(desc, q_blk, k_blk, v_blk, k_cache, v_cache, prompt_len, tau, pos_d, out, lse, status,
+                          workspace, workspace_bytes_in, stream,
+                          PassEvents{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)});
 }
 
 int simsd_accept_prefix_workspace(int32_t batch, int32_t B, int64_t vocab, size_t* bytes) {

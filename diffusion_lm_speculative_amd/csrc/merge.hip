@@ -65,20 +65,19 @@ __global__ __launch_bounds__(256) void merge_kernel(Plan pl, VerifyArgs a) {
 }
 
 template <typename T, int HD>
-hipError_t launch_typed(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
+hipError_t launch_typed(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
   const size_t nrows = static_cast<size_t>(pl.NB) * pl.Hkv * pl.M;
   const unsigned grid = static_cast<unsigned>((nrows + 3) / 4);
-  hipLaunchKernelGGL((merge_kernel<T, HD>), dim3(grid), dim3(256), 0, s, pl, a);
-  return hipGetLastError();
+  return launch_with_events(merge_kernel<T, HD>, dim3(grid), dim3(256), 0, s, ev.start, ev.stop, pl, a);
 }
 
 }  // namespace
 
-hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
+hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
   if (pl.dtype == SIMSD_F32) {
-    return pl.d == 64 ? launch_typed<float, 64>(pl, a, s) : launch_typed<float, 128>(pl, a, s);
+    return pl.d == 64 ? launch_typed<float, 64>(pl, a, s, ev) : launch_typed<float, 128>(pl, a, s, ev);
   }
-  return pl.d == 64 ? launch_typed<uint16_t, 64>(pl, a, s) : launch_typed<uint16_t, 128>(pl, a, s);
+  return pl.d == 64 ? launch_typed<uint16_t, 64>(pl, a, s, ev) : launch_typed<uint16_t, 128>(pl, a, s, ev);
 }
 
 }  // namespace simsd

@@ -4,6 +4,7 @@
 // Speculative Decoding in Diffusion Language Models" (sections 1-3).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -220,9 +221,28 @@ hipError_t allow_dynamic_lds(int bytes) {
   return err[dev];
 }
 
+// Events a caller binds to a pass: `start` takes the start time of its first
+// kernel and `stop` the end time of its last, from the dispatches themselves.
+struct PassEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// Launch `kern` on `s`; when an event is given, through hipExtLaunchKernelGGL,
+// which records `start` / `stop` at the kernel's own start and end.
+template <typename... KArgs, typename... Args>
+hipError_t launch_with_events(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                              hipEvent_t start, hipEvent_t stop, Args... args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kern, grid, block, static_cast<uint32_t>(lds), s, start, stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kern, grid, block, lds, s, args...);
+  return hipGetLastError();
+}
+
 // Host-side launchers (one per translation unit).
-hipError_t launch_verify_valu(const Plan& pl, const VerifyArgs& a, hipStream_t s);
-hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s);
+hipError_t launch_verify_valu(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev);
+hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev);
 size_t mfma_lds_bytes(int hd, int nstage, int tab_rows, int rows_wg, bool qsep);
 
 // y = x W^T (bf16, fp32 accumulation); output channels [0, cut1) go to
@@ -239,7 +259,7 @@ hipError_t launch_append_kv(const Plan& pl, const void* k_blk, const void* v_blk
                             int32_t* status, hipStream_t s);
 hipError_t launch_linear(const uint16_t* x, const uint16_t* w, int64_t M, int N, int K, int cut1, int cut2,
                          uint16_t* out0, int ld0, uint16_t* out1, int ld1, uint16_t* out2, int ld2, hipStream_t s);
-hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s);
+hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev);
 void accept_plan(int NB, int64_t V, int& nch, int& cpw, int& ngrp);
 size_t accept_workspace_bytes(int NB, int B, int64_t V);
 int accept_prefix_checks(const float* p_target, const float* q_draft, const int32_t* draft_tok, const int32_t* tau,

@@ -1,0 +1,108 @@
+// Measurement kernel: the streaming ceiling of the attention kernel's load
+// path, with the attention taken out.  It reads a K and a V region laid out
+// like the prompt cache ([stream][len][head_dim] bf16 each, one stream per
+// (sequence, KV head)) through the same machinery as verify_mfma_kernel: one
+// workgroup of 8 waves per stream on a (KV head, sequence) grid (so
+// consecutive workgroups land on consecutive XCDs the same way), 64-key tiles
+// through a 4-stage LDS ring filled by direct-to-LDS loads of 1 KiB per wave
+// instruction, the same split of K and V rows over the waves, one barrier per
+// tile.  Each step only touches one LDS word of the tile.  The time of a
+// launch over the bench's cache is the most that workload's bytes can stream
+// at through this path, which the attention kernel's time is compared with.
+#include "mfma_common.hpp"
+
+namespace simsd {
+namespace {
+
+constexpr int kProbeKeys = 64;  // keys per tile
+constexpr int kProbeStages = 4;
+constexpr int kProbeWaves = 8;
+
+template <int HD>
+__global__ __launch_bounds__(kProbeWaves * 64) void stream_probe_kernel(const uint16_t* __restrict__ kc,
+                                                                         const uint16_t* __restrict__ vc, int len,
+                                                                         uint32_t* __restrict__ sink) {
+  constexpr int ROWB = HD * 2;                      // bytes per row
+  constexpr int TILEB = kProbeKeys * ROWB;          // one K or V tile
+  constexpr int RPI = 1024 / ROWB;                  // rows per 1 KiB load instruction
+  constexpr int IPT = kProbeKeys / RPI;             // load instructions per tensor per tile
+  constexpr int LPW = 2 * IPT / kProbeWaves;        // loads per wave per tile
+  constexpr int VREG = kProbeStages * TILEB;
+  static_assert(LPW * kProbeWaves == 2 * IPT, "tile loads split evenly over the waves");
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const size_t stream = static_cast<size_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+  const uint16_t* kt0 = kc + stream * static_cast<size_t>(len) * HD;
+  const uint16_t* vt0 = vc + stream * static_cast<size_t>(len) * HD;
+  const uint32_t sbase = lds_addr(smem);
+  const int T = len / kProbeKeys;
+  uint32_t goff[LPW];
+#pragma unroll
+  for (int mm = 0; mm < LPW; ++mm) {
+    const int ii = (wave * LPW + mm) % IPT;
+    goff[mm] = (ii * RPI + lane / (ROWB / 16)) * ROWB + (lane % (ROWB / 16)) * 16;
+  }
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int st = t % kProbeStages;
+#pragma unroll
+    for (int mm = 0; mm < LPW; ++mm) {
+      const int ins = wave * LPW + mm;
+      const bool isv = ins >= IPT;
+      const int ii = isv ? ins - IPT : ins;
+      const uint16_t* base = (isv ? vt0 : kt0) + static_cast<size_t>(t) * kProbeKeys * HD;
+      dma16s(base, goff[mm], sbase + (isv ? VREG : 0) + st * TILEB + ii * 1024);
+    }
+  };
+  for (int t = 0; t < kProbeStages && t < T; ++t) issue(t);
+  uint32_t acc = 0;
+  for (int t = 0; t < T; ++t) {
+    // tile t landed; the tiles issued after it may still be in flight
+    const int later = min(t == 0 ? kProbeStages - 1 : kProbeStages - 2, T - 1 - t);
+    if (later >= 3)
+      lds_barrier<3 * LPW>();
+    else if (later == 2)
+      lds_barrier<2 * LPW>();
+    else if (later == 1)
+      lds_barrier<LPW>();
+    else
+      lds_barrier<0>();
+    if (t > 0 && t + kProbeStages - 1 < T) issue(t + kProbeStages - 1);  // into the stage tile t-1 left
+    acc ^= *reinterpret_cast<const uint32_t*>(smem + (t % kProbeStages) * TILEB + (tid * 64) % TILEB);
+  }
+  wait_counts<0, 15>();
+  if (acc == 0x5eed5eedu && tid == 0) sink[0] = acc;  // keeps the reads; not expected to happen
+}
+
+template <int HD>
+hipError_t launch_probe(const void* k, const void* v, int sx, int sy, int len, void* sink, hipStream_t s,
+                        PassEvents ev) {
+  auto kern = stream_probe_kernel<HD>;
+  const int lds = 2 * kProbeStages * kProbeKeys * HD * 2;
+  const hipError_t e = allow_dynamic_lds<stream_probe_kernel<HD>>(lds);
+  if (e != hipSuccess) return e;
+  return launch_with_events(kern, dim3(sx, sy), dim3(kProbeWaves * 64), lds, s, ev.start, ev.stop,
+                            static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), len,
+                            static_cast<uint32_t*>(sink));
+}
+
+}  // namespace
+}  // namespace simsd
+
+extern "C" int simsd_stream_probe(const void* k, const void* v, int32_t streams_x, int32_t streams_y, int32_t len,
+                                  int32_t head_dim, void* sink, void* stream, void* start_event, void* stop_event) {
+  using namespace simsd;
+  if (streams_x < 1 || streams_y < 1 || streams_y > 65535 || len < 0 || len % kProbeKeys != 0 ||
+      (head_dim != 64 && head_dim != 128))
+    return SIMSD_ERR_SHAPE;
+  if (len == 0) return SIMSD_OK;
+  if (!k || !v || !sink) return SIMSD_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(k) % 16 || reinterpret_cast<uintptr_t>(v) % 16 ||
+      reinterpret_cast<uintptr_t>(sink) % 4)
+    return SIMSD_ERR_ALIGN;
+  const PassEvents ev{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = head_dim == 128 ? launch_probe<128>(k, v, streams_x, streams_y, len, sink, s, ev)
+                                       : launch_probe<64>(k, v, streams_x, streams_y, len, sink, s, ev);
+  return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
+}

@@ -33,10 +33,10 @@
 // loop (unrolled by NSTAGE) addresses every operand as a loop-invariant
 // per-lane register plus an immediate stage offset.
 //
-// Software pipeline.  Step t waits for tile t+1, refills the stage tile t-1
-// left, reads V of tile t, computes the scores of tile t+1 (MFMA) and, while
-// those run, the softmax of tile t (VALU), then accumulates P V of tile t.
-// One barrier per tile; each wave waits only for its own loads.
+// Pipeline.  Step t waits for tile t, refills the stage tile t-1 left (so
+// three tiles are in flight behind the one in use), reads K and V of tile t,
+// computes its scores (MFMA), softmax (VALU) and P V (MFMA).  One barrier per
+// tile; each wave waits only for its own loads.
 #include "mfma_common.hpp"
 
 namespace simsd {
@@ -495,11 +495,6 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       for (int rt = 0; rt < ROWT; ++rt) sacc[rt][i] = sa[rt];
     }
   };
-  auto scores = [&](int st, f32x4 (&sacc)[ROWT][NSUB]) __attribute__((always_inline)) {
-    bf16x8 kop[NSUB][KSTEPS];
-    kread(st, kop);
-    kmma(kop, sacc);
-  };
 
   // V^T operands of the tile in stage ST (the reads complete during the softmax).
   auto vread = [&](int st, bf16x8 (&vop)[DTILES][NU]) __attribute__((always_inline)) {
@@ -618,11 +613,9 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
         for (int rt = 0; rt < ROWT; ++rt) acc[rt][dt] = mfma(vop[dt][uu], pop[rt][uu], acc[rt][dt]);
   };
 
-  // ---- the T = ntiles + nbt tiles, software-pipelined over the ring.
-  //      Before step t: tiles 0 .. min(t + NSTAGE - 2, T - 1) are issued
-  //      (0 .. min(NSTAGE, T) - 1 for t = 0), in tile order.
-  // Scores of the next tile: the softmax of tile t reads them before the
-  // score MFMAs of tile t+1 overwrite them, so one buffer serves.
+  // ---- the T = ntiles + nbt tiles over the ring.  Before step t: tiles
+  //      0 .. min(t + NSTAGE - 2, T - 1) are issued (0 .. min(NSTAGE, T) - 1
+  //      for t = 0), in tile order.
   f32x4 sb[ROWT][NSUB];
   const int nfull = (c1 - c0) / KT;  // whole prompt tiles: nbt .. nbt + nfull - 1
   if (T >= NSTAGE)
@@ -630,34 +623,30 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   else
     lds_barrier<0>();
   if (nbt > 0) rotate_block(0, 0);
-  scores(0, sb);
+  // Step t waits for tile t only (the barrier also frees the stage of tile
+  // t-1, refilled at once), then reads K and V of tile t and runs its score
+  // MFMAs, softmax and PV MFMAs, so three tiles stay in flight behind the one
+  // in use.  (Keeping tile t+1 resident too, to run its score MFMAs under the
+  // softmax of tile t, leaves two in flight and measured 0.3-2% slower on
+  // every workload.)
   auto step = [&](auto mode_c, int t) __attribute__((always_inline)) {
-    const int K = t % NSTAGE;                // stage of tile t
-    const int K1 = K + 1 == NSTAGE ? 0 : K + 1;
-    if (t + 1 < T) {
-      // tile t+1 must have landed: only the loads of later tiles may still be
-      // in flight; for t >= 1 the barrier also frees the stage of tile t-1
-      if (t == 0) {
-        if (T >= NSTAGE)
-          lds_barrier<(NSTAGE - 2) * LPW>();
-        else
-          lds_barrier<0>();
-      } else {
-        if (t + NSTAGE - 2 < T)
-          lds_barrier<(NSTAGE - 3) * LPW>();
-        else
-          lds_barrier<0>();
-        if (t + NSTAGE - 1 < T) issue(K == 0 ? NSTAGE - 1 : K - 1, t + NSTAGE - 1, c1);
-      }
-      if (t + 1 < nbt) rotate_block(K1, t + 1);
+    const int K = t % NSTAGE;
+    if (t > 0) {
+      const int later = T - 1 - t;  // tiles after t that may still be in flight (at most NSTAGE - 2)
+      if (later >= NSTAGE - 2)
+        lds_barrier<(NSTAGE - 2) * LPW>();
+      else if (later == 1)
+        lds_barrier<LPW>();
+      else
+        lds_barrier<0>();
+      if (t + NSTAGE - 1 < T) issue(K == 0 ? NSTAGE - 1 : K - 1, t + NSTAGE - 1, c1);
+      if (t < nbt) rotate_block(K, t);
     }
-    // One row tile: the K reads of tile t+1 go out first and land behind
-    // the softmax.  Two row tiles: the registers for both do not fit beside
-    // the softmax, so they go out after it and land behind the PV MFMAs.
     bf16x8 kop[NSUB][KSTEPS];
-    if (ROWT == 1 && t + 1 < T) kread(K1, kop);
+    kread(K, kop);
     bf16x8 vop[DTILES][NU];
     vread(K, vop);
+    kmma(kop, sb);
     if (decltype(mode_c)::value == 0) {
       const uint64_t cm[ROWT] = {};
       finish(IC<0>{}, sb, vop, cm);
@@ -669,8 +658,6 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       for (int rt = 0; rt < ROWT; ++rt) cm[rt] = t < nbt ? block_vis(rt, t) : tail;
       finish(IC<1>{}, sb, vop, cm);
     }
-    if (ROWT > 1 && t + 1 < T) kread(K1, kop);
-    if (t + 1 < T) kmma(kop, sb);
   };
   // block tiles, then whole prompt tiles, then the rest through the masked
   // path
@@ -764,7 +751,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
 }
 
 template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT>
-hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
+hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
   auto kern = verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT>;
   const size_t lds = mfma_lds_bytes(HD, NSTAGE, pl.tab_rows, RW * ROWT * 16, QSEP);
   // the table and staged-row sizes vary per call: allow the whole LDS once
@@ -773,8 +760,7 @@ hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
   if (lds > static_cast<size_t>(kLdsMax)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(pl.Hkv), static_cast<unsigned>(pl.NB) * static_cast<unsigned>(pl.nrg),
                   static_cast<unsigned>(pl.nsplit));
-  hipLaunchKernelGGL(kern, grid, dim3(RW * KSPLIT * 64), lds, s, pl, a);
-  return hipGetLastError();
+  return launch_with_events(kern, grid, dim3(RW * KSPLIT * 64), lds, s, ev.start, ev.stop, pl, a);
 }
 
 // Rows per workgroup -> (row waves, key splits, row tiles per wave): up to 64
@@ -782,12 +768,12 @@ hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
 // rows four row waves of two row tiles each, keys split over 2 waves, so
 // every K and V operand read from LDS feeds two MFMAs.
 template <int HD, int NSTAGE, bool QSEP>
-hipError_t launch_stages(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
+hipError_t launch_stages(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
   switch (pl.rows_wg / 16) {
-    case 1: return launch_cfg<HD, 1, 4, NSTAGE, QSEP, 1>(pl, a, s);
-    case 2: return launch_cfg<HD, 2, 4, NSTAGE, QSEP, 1>(pl, a, s);
-    case 4: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 1>(pl, a, s);
-    case 8: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 2>(pl, a, s);
+    case 1: return launch_cfg<HD, 1, 4, NSTAGE, QSEP, 1>(pl, a, s, ev);
+    case 2: return launch_cfg<HD, 2, 4, NSTAGE, QSEP, 1>(pl, a, s, ev);
+    case 4: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 1>(pl, a, s, ev);
+    case 8: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 2>(pl, a, s, ev);
     default: return hipErrorInvalidConfiguration;
   }
 }
@@ -802,10 +788,10 @@ size_t mfma_lds_bytes(int hd, int nstage, int tab_rows, int rows_wg, bool qsep) 
          static_cast<size_t>(tab_rows) * (hd / 2) * sizeof(float2);
 }
 
-hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s) {
-  if (pl.d == 64) return launch_stages<64, 4, true>(pl, a, s);
-  if (pl.qsep) return launch_stages<128, 4, true>(pl, a, s);
-  return pl.nstage == 4 ? launch_stages<128, 4, false>(pl, a, s) : launch_stages<128, 3, false>(pl, a, s);
+hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
+  if (pl.d == 64) return launch_stages<64, 4, true>(pl, a, s, ev);
+  if (pl.qsep) return launch_stages<128, 4, true>(pl, a, s, ev);
+  return pl.nstage == 4 ? launch_stages<128, 4, false>(pl, a, s, ev) : launch_stages<128, 3, false>(pl, a, s, ev);
 }
 
 }  // namespace simsd

@@ -162,6 +162,22 @@ int simsd_verify_attn(const simsd_verify_desc* desc,
                       void* out, float* lse, int32_t* status,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* simsd_verify_attn with the caller's HIP events (hipEvent_t, created with
+ * timing enabled, or NULL) bound to the pass's own kernels: `start_event`
+ * takes the start time of the attention kernel and `stop_event` the end time
+ * of the last kernel of the pass (the split merge when the prompt is split),
+ * both recorded from the dispatches themselves (hipExtLaunchKernel), so their
+ * elapsed time is the pass's kernel time, without the marker packets that
+ * hipEventRecord puts on the stream before and after.  For timing only; the
+ * arguments, results and errors are those of simsd_verify_attn. */
+int simsd_verify_attn_timed(const simsd_verify_desc* desc,
+                            const void* q_blk, const void* k_blk, const void* v_blk,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* prompt_len, const int32_t* tau, const int32_t* pos_d,
+                            void* out, float* lse, int32_t* status,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* start_event, void* stop_event);
+
 /* Workspace bytes that simsd_accept_prefix needs when next_token is not NULL
  * and B, gamma > 0 (host only, no HIP call): fp64 partial sums of the
  * rejected rows and a record of each sequence's walk (0 when B == 0).  The
@@ -373,6 +389,18 @@ int simsd_next_round(const uint64_t* committed, const int32_t* block_tok, const 
 int simsd_append_kv(const simsd_verify_desc* desc, const void* k_blk, const void* v_blk, const int32_t* pos_d,
                     const uint64_t* committed, int32_t* prompt_len, void* k_cache, void* v_cache, int32_t* status,
                     void* stream);
+
+/* Measurement only: the streaming ceiling of simsd_verify_attn's load path.
+ * Streams k and v ([streams_y][streams_x][len][head_dim] bf16 each, the
+ * prompt-cache layout with streams_x = KV heads and streams_y = sequences;
+ * len a multiple of 64, head_dim 64 or 128) through the attention kernel's
+ * 4-stage ring of direct-to-LDS loads, one 8-wave workgroup per stream, and
+ * computes nothing.  `sink` (4 bytes, device) is written only on a condition
+ * that is not expected to happen.  The events are bound to the kernel as in
+ * simsd_verify_attn_timed (NULL for none).  Errors: SIMSD_ERR_SHAPE
+ * (streams_y > 65535 included), _NULL, _ALIGN, _HIP. */
+int simsd_stream_probe(const void* k, const void* v, int32_t streams_x, int32_t streams_y, int32_t len,
+                       int32_t head_dim, void* sink, void* stream, void* start_event, void* stop_event);
 
 /* Human-readable text for a return code (static storage). */
 const char* simsd_strerror(int code);

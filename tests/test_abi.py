@@ -39,7 +39,7 @@ def _declared():
 def test_header_declarations_match_binding():
     decl = _declared()
     assert decl == set(L.SIGNATURES), decl ^ set(L.SIGNATURES)
-    assert len(decl) == 16
+    assert len(decl) == 18
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -237,6 +237,18 @@ def test_accept_noalloc_rejects_on_host(lib):
     assert call(NB=1800, B=16, gamma=16, V=151936) == L.ERR_SCRATCH
     assert call(NB=1, B=2, gamma=2, V=(1 << 31) - 1) == L.ERR_SCRATCH
     assert lib.simsd_strerror(L.ERR_SCRATCH) != b"unknown error code"
+
+
+@no_gpu_only
+def test_stream_probe_rejects_on_host(lib):
+    def call(k=A, v=A, sx=8, sy=32, n=4096, d=128, sink=A):
+        return lib.simsd_stream_probe(k, v, sx, sy, n, d, sink, None, None, None)
+    assert call(n=100) == L.ERR_SHAPE and call(d=96) == L.ERR_SHAPE and call(sy=65536) == L.ERR_SHAPE
+    assert call(sx=0) == L.ERR_SHAPE and call(n=-64) == L.ERR_SHAPE
+    assert call(n=0, k=None, v=None, sink=None) == 0
+    for name in ("k", "v", "sink"):
+        assert call(**{name: None}) == L.ERR_NULL, name
+    assert call(k=A + 8) == L.ERR_ALIGN and call(sink=A + 2) == L.ERR_ALIGN
 
 
 @no_gpu_only
