@@ -107,12 +107,16 @@ class SimsdError(RuntimeError):
         super().__init__(f"{where}: {strerror(code)} (code {code})")
 
 
-def load(path: str = LIB_PATH):
-    """Load libsimsd.so once and attach the C signatures."""
+def load(path: str = None):
+    """Load libsimsd.so once and attach the C signatures.  The path defaults
+    to the in-tree build, or SIMSD_LIBRARY when set (another build of the same
+    sources, e.g. one with host sanitizers)."""
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
+        if path is None:
+            path = os.environ.get("SIMSD_LIBRARY") or LIB_PATH
         if not os.path.exists(path):
             raise RuntimeError(
                 f"{path} is not built; run diffusion_lm_speculative_amd.build.build() "

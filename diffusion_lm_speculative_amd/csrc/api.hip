@@ -12,6 +12,7 @@ constexpr int kKeyTile = 64;        // prompt keys per tile (both kernels iterat
 constexpr int kNumCUs = 256;        // MI355X compute units
 constexpr size_t kLdsPerCu = 163840;  // bytes of LDS per CU (and per workgroup at most)
 constexpr int kMaxChunk = 8192;     // default split length cap (tail of ragged prompts)
+constexpr int kMaxQHeads = 65536;   // query heads per layer accepted by the planner
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -20,6 +21,10 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int make_plan(const simsd_verify_desc& d, Plan& pl) {
   if (d.batch < 0 || d.n_q_heads < 1 || d.n_kv_heads < 1 || d.n_q_heads % d.n_kv_heads != 0 ||
       (d.head_dim != 64 && d.head_dim != 128) || d.B < 0 || d.B > 64 || d.p_max < 0)
+    return SIMSD_ERR_SHAPE;
+  // bounds under which every count and size below fits its type: rows per KV
+  // head G*2B <= 2^23, batch x KV heads <= 2^31
+  if (d.n_q_heads > kMaxQHeads || static_cast<int64_t>(d.batch) * d.n_kv_heads > (int64_t{1} << 31))
     return SIMSD_ERR_SHAPE;
   if (!(d.rope_base > 0.0) || !std::isfinite(d.rope_base) || !(d.softmax_scale >= 0.0f) ||
       !std::isfinite(d.softmax_scale))
@@ -122,6 +127,8 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   // the MFMA kernel's grid is (Hkv, NB * nrg, nsplit): y and z stay below 2^16
   if (pl.impl == SIMSD_IMPL_MFMA && (pl.nsplit > 65535 || static_cast<int64_t>(pl.NB) * pl.nrg > 65535))
     return SIMSD_ERR_SHAPE;
+  // the merge runs one wave per output row, four rows per workgroup
+  if (pl.nsplit > 1 && static_cast<int64_t>(pl.NB) * pl.twoB * pl.Hq > 4 * 0x7fffffffLL) return SIMSD_ERR_SHAPE;
   if (pl.nsplit > 1) {
     pl.part_o_floats = static_cast<size_t>(pl.NB) * pl.Hkv * pl.nsplit * pl.M * pl.d;
     pl.part_ml_floats = static_cast<size_t>(pl.NB) * pl.Hkv * pl.nsplit * pl.M * 2;
@@ -431,6 +438,7 @@ int simsd_debug_rope(const simsd_verify_desc* desc, const void* q_blk, const voi
   const int rc = make_plan(*desc, pl);
   if (rc) return rc;
   if (pl.NB == 0 || pl.B == 0) return SIMSD_OK;
+  if (static_cast<int64_t>(pl.NB) * pl.twoB > 0x7fffffffLL) return SIMSD_ERR_SHAPE;  // one workgroup per block row
   if (!q_blk || !k_blk || !q_rot || !k_rot) return SIMSD_ERR_NULL;
   if (!aligned(q_blk, 16) || !aligned(k_blk, 16) || !aligned(q_rot, 16) || !aligned(k_rot, 16) ||
       (prompt_len && !aligned(prompt_len, 4)) || (pos_d && !aligned(pos_d, 4)))

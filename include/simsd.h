@@ -65,7 +65,8 @@ extern "C" {
 /* ---- return codes ---------------------------------------------------------------- */
 #define SIMSD_OK               0
 #define SIMSD_ERR_NULL        (-1) /* a required pointer is NULL */
-#define SIMSD_ERR_SHAPE       (-2) /* negative size, Hq % Hkv != 0, head_dim not 64/128, B > 64;
+#define SIMSD_ERR_SHAPE       (-2) /* negative size, Hq % Hkv != 0, Hq > 65536, head_dim not 64/128,
+                                       B > 64, batch x Hkv > 2^31;
                                        bf16: prompt splits or batch x ceil(Hq/Hkv*2B/128)
                                        above 65535 */
 #define SIMSD_ERR_DTYPE       (-3) /* unknown dtype, mask mode, RoPE mode or implementation */
@@ -107,8 +108,8 @@ typedef enum { SIMSD_IMPL_AUTO = 0, SIMSD_IMPL_VALU = 1, SIMSD_IMPL_MFMA = 2 } s
 typedef enum { SIMSD_ROPE_COPY = 0, SIMSD_ROPE_SEQUENTIAL = 1 } simsd_rope_mode;
 
 typedef struct {
-  int32_t batch;        /* NB >= 0 */
-  int32_t n_q_heads;    /* Hq >= 1 */
+  int32_t batch;        /* NB >= 0, NB * Hkv <= 2^31 */
+  int32_t n_q_heads;    /* Hq in 1..65536 */
   int32_t n_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0 */
   int32_t head_dim;     /* d: 64 or 128 */
   int32_t B;            /* section length 0..64; B == 0 is a valid no-op */

@@ -107,8 +107,28 @@ def test_mfma_grid_limits(lib):
     # splits of 64 keys: 65535 of them fit, one more does not
     assert _ws(lib, batch=1, p_max=64 * 65535, kv_chunk=64, impl=L.IMPL_MFMA)[0] == 0
     assert _ws(lib, batch=1, p_max=64 * 65536, kv_chunk=64, impl=L.IMPL_MFMA)[0] == L.ERR_SHAPE
-    # many KV heads are fine (x has no such limit)
-    assert _ws(lib, batch=1, n_q_heads=70000, n_kv_heads=70000, p_max=64)[0] == 0
+    # many KV heads are fine (x has no such limit), up to the planner's 65536 query heads
+    assert _ws(lib, batch=1, n_q_heads=65536, n_kv_heads=65536, p_max=64)[0] == 0
+    assert _ws(lib, batch=1, n_q_heads=65537, n_kv_heads=65537, p_max=64)[0] == L.ERR_SHAPE
+
+
+def test_extreme_shapes_are_rejected_or_sized_without_overflow(lib):
+    # sizes whose products overflow 32 or 64 bits must come back as an error
+    # (never a wrapped-around size); the host-sanitizer run of this file
+    # checks the arithmetic itself
+    big = 2 ** 31 - 1
+    for kw in (dict(n_q_heads=2 ** 30, n_kv_heads=1, B=64), dict(n_q_heads=big, n_kv_heads=1, B=64),
+               dict(batch=big, n_q_heads=big, n_kv_heads=big, p_max=big), dict(batch=big, p_max=big, kv_chunk=64),
+               dict(batch=big, n_q_heads=64, n_kv_heads=1, B=64, p_max=big),
+               dict(batch=65535, n_q_heads=big, n_kv_heads=big, B=64, p_max=big, kv_chunk=64, impl=L.IMPL_VALU)):
+        rc, n = _ws(lib, **kw)
+        assert rc == L.ERR_SHAPE or (rc == 0 and 0 <= n < 2 ** 62), (kw, rc, n)
+    n = ctypes.c_size_t(0)
+    for NB, B, V in ((65535, 64, big), (1, 64, big), (65535, 1, 1)):
+        assert lib.simsd_accept_prefix_workspace(NB, B, V, ctypes.byref(n)) == 0 and n.value < 2 ** 62
+        assert lib.simsd_accept_coupled_workspace(NB, B, V, ctypes.byref(n)) in (0, L.ERR_SHAPE)
+    for M, N, K in ((2 ** 62, 16, 64), (big, big - (big % 16), 64), (1, 16, 2 ** 31 - 64)):
+        assert lib.simsd_linear(None, None, M, min(N, big), min(K, big), None, None) in (L.ERR_SHAPE, L.ERR_NULL)
 
 
 def test_descriptor_layout():
