@@ -17,5 +17,6 @@ from .api import (  # noqa: F401
     bind_append_kv, bind_commit, bind_next_round, next_round,
     bind_accept_coupled, bind_linear, bind_qkv_proj, bind_verify, commit, debug_mask, debug_rope, linear, make_desc,
     qkv_proj, stream_probe, verify_attn,
+    verify_plan,
     verify_workspace_bytes,
 )

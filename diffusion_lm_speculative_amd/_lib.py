@@ -66,9 +66,15 @@ class VerifyDesc(ctypes.Structure):
     ]
 
 
+class VerifyPlan(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in ("impl", "threads", "rows_wg", "row_groups", "ksplit", "row_tiles", "nstage",
+                                       "qsep", "blk_rows", "nsplit", "chunk", "lds_bytes")]
+
+
 # name -> (restype, argtypes); every function declared in include/simsd.h.
 SIGNATURES = {
     "simsd_verify_attn_workspace": (c_int32, [ctypes.POINTER(VerifyDesc), ctypes.POINTER(c_size_t)]),
+    "simsd_verify_plan_info": (c_int32, [ctypes.POINTER(VerifyDesc), ctypes.POINTER(VerifyPlan)]),
     "simsd_verify_attn": (c_int32, [ctypes.POINTER(VerifyDesc)] + [c_void_p] * 12 + [c_size_t, c_void_p]),
     "simsd_verify_attn_timed": (c_int32, [ctypes.POINTER(VerifyDesc)] + [c_void_p] * 12 + [c_size_t, c_void_p,
                                                                                          c_void_p, c_void_p]),

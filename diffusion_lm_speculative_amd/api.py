@@ -65,6 +65,14 @@ def verify_workspace_bytes(desc) -> int:
     return int(n.value)
 
 
+def verify_plan(desc) -> dict:
+    """How simsd_verify_attn would run `desc` (a VerifyDesc): the fields of
+    simsd_verify_plan as a dict.  Host only."""
+    p = L.VerifyPlan()
+    L.check(L.load().simsd_verify_plan_info(ctypes.byref(desc), ctypes.byref(p)), "simsd_verify_plan_info")
+    return {name: int(getattr(p, name)) for name, _ in L.VerifyPlan._fields_}
+
+
 def verify_attn(q_blk, k_blk, v_blk, k_cache, v_cache, tau, prompt_len=None, pos_d=None, *,
                 rope_base=10000.0, softmax_scale=0.0, mask_mode=L.MASK_TEMPORAL, impl=L.IMPL_AUTO,
                 kv_chunk=0, rope_mode=L.ROPE_COPY, out=None, lse=None, status=None, workspace=None,

@@ -57,7 +57,7 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   pl.rope_seq = d.rope_mode == SIMSD_ROPE_SEQUENTIAL;
   pl.tab_rows = pl.rope_seq ? 2 * d.B : d.B;  // distinct block positions
   if (pl.impl == SIMSD_IMPL_MFMA && d.head_dim == 128 &&
-      mfma_lds_bytes(128, 3, pl.tab_rows, 128, false) + 1024 > kLdsPerCu) {
+      mfma_lds_bytes(128, 3, pl.tab_rows, 128, false, 0) + 1024 > kLdsPerCu) {
     // the RoPE table does not fit beside a 3-stage ring
     if (d.impl == SIMSD_IMPL_MFMA) return SIMSD_ERR_SHAPE;
     pl.impl = SIMSD_IMPL_VALU;
@@ -79,12 +79,23 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
     // Four ring stages with the query rows staged in their own LDS region
     // when that fits; else the query rows borrow the last stage during the
     // prologue; else three stages.
-    if (mfma_lds_bytes(pl.d, 4, pl.tab_rows, pl.rows_wg, true) + 1024 <= kLdsPerCu) {
+    if (mfma_lds_bytes(pl.d, 4, pl.tab_rows, pl.rows_wg, true, 0) + 1024 <= kLdsPerCu) {
       pl.nstage = 4;
       pl.qsep = 1;
     } else {
-      pl.nstage = mfma_lds_bytes(pl.d, 4, pl.tab_rows, pl.rows_wg, false) + 1024 <= kLdsPerCu ? 4 : 3;
+      pl.nstage = mfma_lds_bytes(pl.d, 4, pl.tab_rows, pl.rows_wg, false, 0) + 1024 <= kLdsPerCu ? 4 : 3;
       pl.qsep = 0;
+    }
+    // The 2B block K/V rows take a region of their own (16-row multiples)
+    // when it fits beside the ring without costing a workgroup per CU; the
+    // ring then streams prompt tiles only, and the block keys are done while
+    // the first of those are in flight.  Only beside a 4-stage ring: where
+    // three stages are all that fit, such a region does not fit either.
+    if (pl.nstage == 4 && pl.twoB > 0 && pl.twoB <= kKeyTile) {
+      const int rows = (pl.twoB + 15) / 16 * 16;
+      const size_t base = mfma_lds_bytes(pl.d, pl.nstage, pl.tab_rows, pl.rows_wg, pl.qsep != 0, 0) + 1024;
+      const size_t with = mfma_lds_bytes(pl.d, pl.nstage, pl.tab_rows, pl.rows_wg, pl.qsep != 0, rows) + 1024;
+      if (with <= kLdsPerCu && kLdsPerCu / with == kLdsPerCu / base) pl.blk_rows = rows;
     }
   } else {
     pl.rowt = 1;
@@ -100,7 +111,7 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   // sequence, so longer splits (fewer partials to merge) cost little tail.
   int64_t target = 2 * kNumCUs;
   if (pl.impl == SIMSD_IMPL_MFMA) {
-    const size_t per_wg = mfma_lds_bytes(pl.d, pl.nstage, pl.tab_rows, pl.rows_wg, pl.qsep != 0) + 1024;
+    const size_t per_wg = mfma_lds_bytes(pl.d, pl.nstage, pl.tab_rows, pl.rows_wg, pl.qsep != 0, pl.blk_rows) + 1024;
     target = kNumCUs * static_cast<int64_t>(kLdsPerCu / per_wg);
   }
   const int64_t tiles_max = (static_cast<int64_t>(pl.p_max) + kKeyTile - 1) / kKeyTile;
@@ -186,7 +197,7 @@ int linear_checks(const void* x, const void* w, int64_t M, int64_t N, int64_t K)
 
 extern "C" {
 
-int simsd_abi_version(void) { return 4; }
+int simsd_abi_version(void) { return 5; }
 
 const char* simsd_strerror(int code) {
   switch (code) {
@@ -210,6 +221,31 @@ int simsd_verify_attn_workspace(const simsd_verify_desc* desc, size_t* bytes) {
   const int rc = make_plan(*desc, pl);
   if (rc) return rc;
   *bytes = workspace_bytes(pl);
+  return SIMSD_OK;
+}
+
+int simsd_verify_plan_info(const simsd_verify_desc* desc, simsd_verify_plan* plan) {
+  if (!desc || !plan) return SIMSD_ERR_NULL;
+  Plan pl;
+  const int rc = make_plan(*desc, pl);
+  if (rc) return rc;
+  const bool mfma = pl.impl == SIMSD_IMPL_MFMA;
+  simsd_verify_plan o{};
+  o.impl = pl.impl;
+  o.threads = pl.threads;
+  o.rows_wg = pl.rows_wg;
+  o.row_groups = pl.nrg;
+  o.ksplit = mfma ? pl.ksplit : 0;
+  o.row_tiles = pl.rowt;
+  o.nstage = mfma ? pl.nstage : 0;
+  o.qsep = mfma ? pl.qsep : 0;
+  o.blk_rows = mfma ? pl.blk_rows : 0;
+  o.nsplit = pl.nsplit;
+  o.chunk = pl.chunk;
+  o.lds_bytes =
+      mfma ? static_cast<int32_t>(mfma_lds_bytes(pl.d, pl.nstage, pl.tab_rows, pl.rows_wg, pl.qsep != 0, pl.blk_rows))
+           : 0;
+  *plan = o;
   return SIMSD_OK;
 }
 

@@ -170,6 +170,7 @@ struct Plan {
   double rope_base;
   double log2_base;                   // log2(rope_base)
   int qsep;                           // MFMA: query rows staged in their own LDS region
+  int blk_rows;                       // MFMA: block K/V rows in their own LDS region (0: through the ring)
   int rope_seq;                       // D~_k at pos(D_k) + B instead of pos(D_k)
   int tab_rows;                       // distinct block positions: B, or 2B with rope_seq
   float scale_log2;                   // softmax scale * log2(e)
@@ -243,7 +244,7 @@ hipError_t launch_with_events(void (*kern)(KArgs...), dim3 grid, dim3 block, siz
 // Host-side launchers (one per translation unit).
 hipError_t launch_verify_valu(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev);
 hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev);
-size_t mfma_lds_bytes(int hd, int nstage, int tab_rows, int rows_wg, bool qsep);
+size_t mfma_lds_bytes(int hd, int nstage, int tab_rows, int rows_wg, bool qsep, int blk_rows);
 
 // y = x W^T (bf16, fp32 accumulation); output channels [0, cut1) go to
 // out0, [cut1, cut2) to out1, [cut2, N) to out2, row-major with row lengths

@@ -122,14 +122,17 @@ __device__ __forceinline__ void rotate8(const uint32_t (&wx)[4], const uint32_t 
 
 // LDS layout of one workgroup (bytes): NSTAGE K tiles, NSTAGE V tiles, the
 // stage labels and positions (2 x 256), the query rows when they have their
-// own region, then the RoPE table of the B block positions.
+// own region, the block K and V rows when they have their own region
+// (Plan::blk_rows each, a run-time size), then the RoPE table of the block
+// positions.
 template <int HD, int NSTAGE, bool QSEP>
 struct Smem {
   static constexpr int KREG = 0;
   static constexpr int VREG = NSTAGE * Layout<HD>::TILEB;
   static constexpr int TPREG = 2 * NSTAGE * Layout<HD>::TILEB;
   static constexpr int QREG = TPREG + 512;
-  static constexpr int tab(int rows_wg) { return QREG + (QSEP ? rows_wg * Layout<HD>::ROWB : 0); }
+  // start of the block rows' region (the table follows it)
+  static constexpr int blk(int rows_wg) { return QREG + (QSEP ? rows_wg * Layout<HD>::ROWB : 0); }
   // Byte offset of query row lr (0 <= lr < rows per workgroup) of the staging area.
   static constexpr int qrow(int lr) {
     return QSEP ? QREG + lr * Layout<HD>::ROWB
@@ -138,7 +141,7 @@ struct Smem {
   }
 };
 
-template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT>
+template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT, bool BSEP>
 __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, VerifyArgs a) {
   using L = Layout<HD>;
   using S = Smem<HD, NSTAGE, QSEP>;
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   constexpr int LPW = 2 * L::IPT / NW;           // direct-to-LDS loads per wave per tile
   constexpr int KREG = S::KREG;
   constexpr int VREG = S::VREG;
-  constexpr int TABREG = S::tab(ROWS);
+  constexpr int BKREG = S::blk(ROWS);
   constexpr int NPRO = QSEP ? NSTAGE : NSTAGE - 1;  // ring tiles issued before the query rows are read
   constexpr int QI = ROWS / L::RPI;              // 1 KiB loads of the workgroup's query rows
   constexpr int XSTR = HD + 4;                   // floats per row of the key-split exchange buffer
@@ -211,7 +214,15 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   };
   const int c0 = s * pl.chunk;
   const bool has_block = (s == 0);
-  const int nbt = has_block ? (twoB + KT - 1) / KT : 0;  // block tiles, streamed after the prompt tiles
+  // The block keys either sit in their own LDS region (BSEP: R = blk_rows
+  // rows of K, then of V; rows past 2B re-read row 2B-1), loaded with the
+  // query rows and processed before the first prompt tile lands, or stream
+  // through the ring as its first nbt tiles.  (One kernel holding both paths
+  // needs about 35 more VGPRs.)
+  const int R = BSEP ? pl.blk_rows : 0;
+  const bool blk = BSEP && has_block;
+  const int nbt = !BSEP && has_block ? (twoB + KT - 1) / KT : 0;
+  const int BVREG = BKREG + R * L::ROWB;
   const int plen = a.prompt_len ? a.prompt_len[b] : pl.p_max;  // scalar load
   const uint32_t sbase = lds_addr(smem);
 
@@ -219,7 +230,8 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   //      complete in issue order, so waiting for all but the ring loads
   //      waits for exactly these): stage labels and positions, then this
   //      workgroup's query rows (granules swizzled like the ring tiles;
-  //      rows past M re-read row M-1).
+  //      rows past M re-read row M-1), then the block rows if they have
+  //      their own region.
   if (wave == 0) {
     const int lc = min(lane, B - 1);
     dma4(tau_b + lc, sbase + S::TPREG);
@@ -310,12 +322,23 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   // of the ring is issued once they are in.
   constexpr int kSpecTiles = NPRO < 2 ? NPRO : 2;
   const int nspec = min(kSpecTiles, nbt + nts);
+  if (blk) {
+    // R K rows then R V rows, RPI rows per 1 KiB load, swizzled like ring rows
+    for (int ins = wave; ins < 2 * R / L::RPI; ins += NW) {
+      const int row = ins * L::RPI + lane / L::GR;
+      const bool isv = row >= R;
+      const int lr = isv ? row - R : row;
+      const int sw = isv ? vsw<HD>(lr) : (lr & (L::GR - 1));
+      const size_t c = static_cast<size_t>(min(lr, twoB - 1));
+      dma16((isv ? vblk_b : kblk_b) + c * blk_row + ((lane % L::GR) ^ sw) * 8, sbase + BKREG + ins * 1024);
+    }
+  }
   issue_range(0, nspec, c1s);
 
   // ---- RoPE table of the distinct block positions (B with the RoPE copy,
   //      2B without it), while the loads are in flight: positions come by
   //      scalar loads (a wave's 64 entries need at most two)
-  float2* cs_tab = reinterpret_cast<float2*>(smem + TABREG);
+  float2* cs_tab = reinterpret_cast<float2*>(smem + BKREG + 2 * R * L::ROWB);
   const int nent = pl.tab_rows;  // block row r uses entry r % nent
   {
     const double lane_inv_freq = rope_inv_freq(tid % HALF, HD, pl.log2_base);
@@ -360,7 +383,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const int c1 = min(c0 + pl.chunk, plen);
   const int ntiles = c1 > c0 ? (c1 - c0 + KT - 1) / KT : 0;
   const int T = nbt + ntiles;
-  if (st || T == 0) {
+  if (st || (T == 0 && !blk)) {
     wait_counts<0, 15>();  // drain the ring loads before the workgroup's LDS is released
     if (status_writer) a.status[b] = st;
     if (st && pl.nsplit == 1 && ks == 0) {
@@ -516,16 +539,15 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       }
   };
 
-  // Rotate block tile bt (its K rows in stage st) in place.
-  auto rotate_block = [&](int st, int bt) __attribute__((always_inline)) {
-    unsigned char* Kb = smem + KREG + st * L::TILEB;
-    const int nvalid = min(KT, twoB - bt * KT);
+  // Rotate block K rows row0 .. row0 + nvalid - 1, held from Kb on (K
+  // swizzle), in place.
+  auto rotate_rows = [&](unsigned char* Kb, int nvalid, int row0) __attribute__((always_inline)) {
     for (int i = tid; i < nvalid * (L::GR / 2); i += NT) {
       const int row = i / (L::GR / 2), j = i % (L::GR / 2);
       uint4* px = reinterpret_cast<uint4*>(Kb + swz<HD>(row, j));
       uint4* py = reinterpret_cast<uint4*>(Kb + swz<HD>(row, j + L::GR / 2));
       const uint4 x4 = *px, y4 = *py;
-      const float4* csr = reinterpret_cast<const float4*>(cs_tab + ((bt * KT + row) % nent) * HALF + 8 * j);
+      const float4* csr = reinterpret_cast<const float4*>(cs_tab + ((row0 + row) % nent) * HALF + 8 * j);
       float4 c4[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) c4[q4] = csr[q4];
@@ -536,6 +558,10 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       *px = make_uint4(ox[0], ox[1], ox[2], ox[3]);
       *py = make_uint4(oy[0], oy[1], oy[2], oy[3]);
     }
+  };
+  // Rotate block tile bt (its K rows in stage st) in place.
+  auto rotate_block = [&](int st, int bt) __attribute__((always_inline)) {
+    rotate_rows(smem + KREG + st * L::TILEB, min(KT, twoB - bt * KT), bt * KT);
     lds_barrier<63>();
   };
 
@@ -617,6 +643,45 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   //      0 .. min(t + NSTAGE - 2, T - 1) are issued (0 .. min(NSTAGE, T) - 1
   //      for t = 0), in tile order.
   f32x4 sb[ROWT][NSUB];
+  // ---- the block keys from their own region, before the first prompt tile
+  //      (the block work costs about the same at any step: done first, the
+  //      result matches the ring path's bit for bit).  Only waves whose key
+  //      range starts below 2B take part.  Their operand reads of key row k
+  //      use block row k mod R, so the keys past 2B hold finite values; the
+  //      mask drops them.
+  if (blk) {
+    rotate_rows(smem + BKREG, twoB, 0);
+    lds_barrier<63>();
+  }
+  if (blk && 16 * ks * NSUB < twoB) {
+    bf16x8 kop[NSUB][KSTEPS];
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) {
+      const int ro = BKREG + ((16 * (ks * NSUB + i)) % R) * L::ROWB;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        kop[i][kk] = *reinterpret_cast<const bf16x8*>(smem + ro + swz<HD>(n, 4 * kk + g));
+    }
+    bf16x8 vop[DTILES][NU];
+    const int vr = 4 * g + ((lane & 15) >> 2);
+    const int vc4 = lane & 3;
+#pragma unroll
+    for (int uu = 0; uu < NU; ++uu) {
+      const int u = (ks * NSUB) / 2 + uu;
+      const uint32_t rlo = sbase + BVREG + ((32 * u) % R) * L::ROWB;
+      const uint32_t rhi = sbase + BVREG + ((32 * u + 16) % R) * L::ROWB;
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) {
+        const uint32_t co = swz_v<HD>(vr, 2 * dt + (vc4 >> 1)) + (vc4 & 1) * 8;
+        vop[dt][uu] = __builtin_shufflevector(tr_read<0>(rlo + co), tr_read<0>(rhi + co), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+    kmma(kop, sb);
+    uint64_t cm[ROWT];
+#pragma unroll
+    for (int rt = 0; rt < ROWT; ++rt) cm[rt] = block_vis(rt, 0);
+    finish(IC<1>{}, sb, vop, cm);
+  }
   const int nfull = (c1 - c0) / KT;  // whole prompt tiles: nbt .. nbt + nfull - 1
   if (T >= NSTAGE)
     lds_barrier<(NSTAGE - 1) * LPW>();  // tile 0 landed
@@ -750,12 +815,12 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   }
 }
 
-template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT>
+template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT, bool BSEP>
 hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
-  auto kern = verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT>;
-  const size_t lds = mfma_lds_bytes(HD, NSTAGE, pl.tab_rows, RW * ROWT * 16, QSEP);
+  auto kern = verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT, BSEP>;
+  const size_t lds = mfma_lds_bytes(HD, NSTAGE, pl.tab_rows, RW * ROWT * 16, QSEP, pl.blk_rows);
   // the table and staged-row sizes vary per call: allow the whole LDS once
-  const hipError_t e = allow_dynamic_lds<verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT>>(kLdsMax);
+  const hipError_t e = allow_dynamic_lds<verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT, BSEP>>(kLdsMax);
   if (e != hipSuccess) return e;
   if (lds > static_cast<size_t>(kLdsMax)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(pl.Hkv), static_cast<unsigned>(pl.NB) * static_cast<unsigned>(pl.nrg),
@@ -767,31 +832,41 @@ hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEv
 // rows one 16-row tile per wave with the keys split over 4 or 2 waves; 128
 // rows four row waves of two row tiles each, keys split over 2 waves, so
 // every K and V operand read from LDS feeds two MFMAs.
-template <int HD, int NSTAGE, bool QSEP>
-hipError_t launch_stages(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
+template <int HD, int NSTAGE, bool QSEP, bool BSEP>
+hipError_t launch_rows(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
   switch (pl.rows_wg / 16) {
-    case 1: return launch_cfg<HD, 1, 4, NSTAGE, QSEP, 1>(pl, a, s, ev);
-    case 2: return launch_cfg<HD, 2, 4, NSTAGE, QSEP, 1>(pl, a, s, ev);
-    case 4: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 1>(pl, a, s, ev);
-    case 8: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 2>(pl, a, s, ev);
+    case 1: return launch_cfg<HD, 1, 4, NSTAGE, QSEP, 1, BSEP>(pl, a, s, ev);
+    case 2: return launch_cfg<HD, 2, 4, NSTAGE, QSEP, 1, BSEP>(pl, a, s, ev);
+    case 4: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 1, BSEP>(pl, a, s, ev);
+    case 8: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 2, BSEP>(pl, a, s, ev);
     default: return hipErrorInvalidConfiguration;
   }
+}
+
+template <int HD, int NSTAGE, bool QSEP>
+hipError_t launch_stages(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
+  return pl.blk_rows > 0 ? launch_rows<HD, NSTAGE, QSEP, true>(pl, a, s, ev)
+                         : launch_rows<HD, NSTAGE, QSEP, false>(pl, a, s, ev);
 }
 
 }  // namespace
 
 // Dynamic LDS of one workgroup: the tile ring, stage labels and positions,
-// the staged query rows when they have their own region, the RoPE table.
-size_t mfma_lds_bytes(int hd, int nstage, int tab_rows, int rows_wg, bool qsep) {
+// the staged query rows when they have their own region, blk_rows block K
+// rows and as many V rows, the RoPE table.
+size_t mfma_lds_bytes(int hd, int nstage, int tab_rows, int rows_wg, bool qsep, int blk_rows) {
   const size_t ring = static_cast<size_t>(nstage) * 2 * KT * hd * 2;
   return ring + 512 + (qsep ? static_cast<size_t>(rows_wg) * hd * 2 : 0) +
-         static_cast<size_t>(tab_rows) * (hd / 2) * sizeof(float2);
+         2 * static_cast<size_t>(blk_rows) * hd * 2 + static_cast<size_t>(tab_rows) * (hd / 2) * sizeof(float2);
 }
 
 hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
   if (pl.d == 64) return launch_stages<64, 4, true>(pl, a, s, ev);
   if (pl.qsep) return launch_stages<128, 4, true>(pl, a, s, ev);
-  return pl.nstage == 4 ? launch_stages<128, 4, false>(pl, a, s, ev) : launch_stages<128, 3, false>(pl, a, s, ev);
+  if (pl.nstage == 4) return launch_stages<128, 4, false>(pl, a, s, ev);
+  // the planner gives the block rows a region of their own only beside a 4-stage ring
+  if (pl.blk_rows > 0) return hipErrorInvalidConfiguration;
+  return launch_rows<128, 3, false, false>(pl, a, s, ev);
 }
 
 }  // namespace simsd

@@ -127,6 +127,29 @@ typedef struct {
  * Host only; no HIP call.  Returns SIMSD_OK or a negative code. */
 int simsd_verify_attn_workspace(const simsd_verify_desc* desc, size_t* bytes);
 
+/* How simsd_verify_attn would run `desc`: the kernel, the workgroup shape,
+ * the LDS layout choices and the prompt split.  Host only; no HIP call.
+ * Filled on SIMSD_OK; a descriptor that simsd_verify_attn would reject
+ * returns the same negative code and leaves *plan unchanged. */
+typedef struct {
+  int32_t impl;       /* SIMSD_IMPL_VALU or SIMSD_IMPL_MFMA, after AUTO is resolved */
+  int32_t threads;    /* threads per workgroup */
+  int32_t rows_wg;    /* query rows per workgroup (16-row multiples) */
+  int32_t row_groups; /* workgroups sharing one (sequence, KV head, split) */
+  int32_t ksplit;     /* MFMA: waves that share the keys of a tile (else 0) */
+  int32_t row_tiles;  /* 16-row tiles per wave */
+  int32_t nstage;     /* MFMA: LDS ring stages (else 0) */
+  int32_t qsep;       /* MFMA: 1 = query rows staged in their own LDS region */
+  int32_t blk_rows;   /* MFMA: rows of the LDS region holding the 2B block K
+                         rows (and as many V rows), 0 = block keys streamed
+                         through the ring */
+  int32_t nsplit;     /* prompt splits per (sequence, KV head) */
+  int32_t chunk;      /* prompt keys per split */
+  int32_t lds_bytes;  /* MFMA: dynamic LDS per workgroup (else 0) */
+} simsd_verify_plan;
+
+int simsd_verify_plan_info(const simsd_verify_desc* desc, simsd_verify_plan* plan);
+
 /* The verification attention of the SimSD pass (sections 1-3 above).
  *
  *  q_blk   [NB][2B][Hq][d]   rows 0..B-1 are D_0..D_{B-1}, rows B..2B-1 are
@@ -406,7 +429,7 @@ int simsd_stream_probe(const void* k, const void* v, int32_t streams_x, int32_t 
 /* Human-readable text for a return code (static storage). */
 const char* simsd_strerror(int code);
 
-/* ABI version of this header: 3. */
+/* ABI version of this header: 5. */
 int simsd_abi_version(void);
 
 #ifdef __cplusplus

@@ -39,7 +39,7 @@ def _declared():
 def test_header_declarations_match_binding():
     decl = _declared()
     assert decl == set(L.SIGNATURES), decl ^ set(L.SIGNATURES)
-    assert len(decl) == 18
+    assert len(decl) == 19
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.simsd_abi_version() == 4
+    assert lib.simsd_abi_version() == 5
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert lib.simsd_strerror(code)
     assert lib.simsd_strerror(-99) == b"unknown error code"

@@ -1,0 +1,110 @@
+"""Host checks of the launch plan (simsd_verify_plan_info, no GPU needed).
+
+The MFMA kernel has two ways of handling the 2B block keys: in an LDS region
+of their own, loaded with the query rows and done before the first prompt
+tile, or streamed through the tile ring ahead of the prompt tiles.  These
+tests pin which one the benchmark workloads take, check that the GPU parity
+cases reach both, and check the planner's invariants over a sweep of shapes:
+every plan fits the LDS, and the block region never costs a workgroup per CU.
+"""
+import ctypes
+import dataclasses
+import itertools
+
+import pytest
+
+import diffusion_lm_speculative_amd as sd
+from diffusion_lm_speculative_amd import _lib as L
+from diffusion_lm_speculative_amd import synth
+from tests.test_gpu_verify import LONG, SMALL
+
+LDS_PER_CU = 163840
+LDS_RESERVE = 1024  # per workgroup, kept free by the planner
+
+
+def _desc(NB, Hq, Hkv, d, B, p_max, dtype=L.BF16, impl=L.IMPL_AUTO, rope_mode=L.ROPE_COPY, kv_chunk=0):
+    return L.VerifyDesc(NB, Hq, Hkv, d, B, p_max, dtype, L.MASK_TEMPORAL, impl, kv_chunk, 1e6, 0.0, rope_mode)
+
+
+def _plan_of(w, **kw):
+    dt = L.F32 if "float32" in str(w.dtype) else L.BF16
+    return sd.verify_plan(_desc(w.NB, w.Hq, w.Hkv, w.d, w.B, w.P, dtype=dt, **kw))
+
+
+def _lds_without_block_region(p, d):
+    return p["lds_bytes"] - 2 * p["blk_rows"] * d * 2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_loaded():
+    L.load()
+
+
+@pytest.mark.parametrize("name,expect", [
+    # workload: (rows per workgroup, row groups, key split, row tiles, stages, qsep, block rows, splits)
+    # (1024-key prompts of 16 sequences x 8 KV heads: two 512-key splits fill the 256 CUs; the 16k
+    # prompts are split at the 8192-key cap)
+    ("sdar8b_p1024_b4", (32, 1, 4, 1, 4, 1, 16, 2)),
+    ("sdar8b_p4096_b8", (64, 1, 2, 1, 4, 1, 16, 1)),
+    ("sdar8b_p8192_b32", (128, 2, 2, 2, 4, 0, 0, 2)),
+    ("sdar8b_var16k_b16_accept", (128, 1, 2, 2, 4, 0, 32, 2)),
+])
+def test_benchmark_workload_plans(name, expect):
+    p = _plan_of(synth.WORKLOADS[name])
+    got = (p["rows_wg"], p["row_groups"], p["ksplit"], p["row_tiles"], p["nstage"], p["qsep"], p["blk_rows"],
+           p["nsplit"])
+    assert p["impl"] == L.IMPL_MFMA and got == expect, p
+    assert p["lds_bytes"] + LDS_RESERVE <= LDS_PER_CU
+
+
+def test_headline_plan_lds_layout():
+    # 4-stage ring of 64-key K and V tiles, stage labels and positions, 64
+    # staged query rows, 16 block K rows + 16 block V rows, RoPE table of B=8
+    # positions (d/2 cos/sin pairs each)
+    p = _plan_of(synth.WORKLOADS["sdar8b_p4096_b8"])
+    d = 128
+    assert p["lds_bytes"] == 4 * 2 * 64 * d * 2 + 512 + 64 * d * 2 + 2 * 16 * d * 2 + 8 * (d // 2) * 8
+
+
+def test_parity_cases_reach_both_block_paths():
+    base = synth.WORKLOADS["sdar8b_p1024_b4"]
+    kinds = {}
+    for label, ov in SMALL + [(f"long_{l}", dict(NB=2, P=1000, p_lo=300, **o)) for l, o in LONG]:
+        w = dataclasses.replace(base, **ov)
+        p = _plan_of(w, impl=L.IMPL_MFMA)
+        kinds.setdefault(p["blk_rows"] > 0, []).append(label)
+    assert kinds.get(True) and kinds.get(False), kinds
+    assert "block_only" in kinds[True]  # P = 0: only the block keys, from their own region
+    assert "b64_g4" in kinds[False] and "long_rows256" in kinds[False]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rope_mode", [L.ROPE_COPY, L.ROPE_SEQUENTIAL])
+def test_plan_invariants_over_shapes(d, rope_mode):
+    seen = set()
+    for B, G, p_max in itertools.product(range(1, 65), (1, 2, 4, 8), (0, 64, 4096)):
+        try:
+            p = sd.verify_plan(_desc(4, 8 * G, 8, d, B, p_max, rope_mode=rope_mode))
+        except L.SimsdError:
+            continue  # a table too large for the MFMA kernel with an explicit request only
+        if p["impl"] != L.IMPL_MFMA:
+            continue
+        assert p["lds_bytes"] + LDS_RESERVE <= LDS_PER_CU, (B, G, p)
+        r = p["blk_rows"]
+        if r:
+            assert r % 16 == 0 and 2 * B <= r < 2 * B + 16 and 2 * B <= 64 and p["nstage"] == 4, (B, G, p)
+            without = _lds_without_block_region(p, d) + LDS_RESERVE
+            assert LDS_PER_CU // (p["lds_bytes"] + LDS_RESERVE) == LDS_PER_CU // without, (B, G, p)
+        seen.add(r > 0)
+    assert seen == {True, False}
+
+
+def test_plan_rejects_like_the_call():
+    bad = _desc(1, 3, 2, 128, 4, 64)  # Hq not a multiple of Hkv
+    with pytest.raises(L.SimsdError):
+        sd.verify_plan(bad)
+    p = L.VerifyPlan()
+    p.impl = 77
+    assert L.load().simsd_verify_plan_info(ctypes.byref(bad), ctypes.byref(p)) == L.ERR_SHAPE
+    assert p.impl == 77  # left unchanged
+    assert L.load().simsd_verify_plan_info(None, ctypes.byref(p)) == L.ERR_NULL
