@@ -107,23 +107,32 @@ def call_event_times(torch, sets, stream, n=40):
 
 def stream_probe_measure(torch, sd, t, dev, stream, kv_bytes, n=30, warmup=5):
     """The attention kernel's load path alone over the same prompt cache
-    (kernel-bound events): the streaming ceiling of that path on this GPU."""
+    (kernel-bound events): the streaming ceiling of that path on this GPU;
+    and, beside it, a plain vector-load read of the same bytes."""
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for a, b in evs:
-        a.record(stream)
-        b.record(stream)
-    for _ in range(warmup):
-        sd.stream_probe(t["k_cache"], t["v_cache"], sink, stream=stream)
-    for a, b in evs:
-        sd.stream_probe(t["k_cache"], t["v_cache"], sink, a, b, stream=stream)
-    torch.cuda.synchronize()
-    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-    mean = sum(us) / len(us)
-    gbs = kv_bytes / (mean * 1e-6) / 1e9
-    return {"what": "the attention kernel's K/V load path alone (same ring, grid and cache), no attention",
-            "us": {"mean": mean, "median": us[len(us) // 2], "min": us[0]}, "bytes": kv_bytes,
-            "achieved_gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+    def timed(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            b.record(stream)
+        for _ in range(warmup):
+            fn(t["k_cache"], t["v_cache"], sink, stream=stream)
+        for a, b in evs:
+            fn(t["k_cache"], t["v_cache"], sink, a, b, stream=stream)
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        mean = sum(us) / len(us)
+        gbs = kv_bytes / (mean * 1e-6) / 1e9
+        return {"us": {"mean": mean, "median": us[len(us) // 2], "min": us[0]}, "bytes": kv_bytes,
+                "achieved_gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+    rec = {"what": "the attention kernel's K/V load path alone (same ring, grid and cache), no attention"}
+    rec.update(timed(sd.stream_probe))
+    rec["read_probe"] = {"what": "plain 16-byte vector loads of the same K and V bytes into registers "
+                                 "(256 workgroups x 512 threads, grid-stride), no LDS"}
+    rec["read_probe"].update(timed(sd.read_probe))
+    return rec
 
 
 def copy_calibration(torch, dev, mib, steps, warmup):

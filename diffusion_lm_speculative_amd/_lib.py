@@ -90,6 +90,7 @@ SIGNATURES = {
     "simsd_debug_rope": (c_int32, [ctypes.POINTER(VerifyDesc)] + [c_void_p] * 7),
     "simsd_stream_probe": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                      c_void_p, c_void_p]),
+    "simsd_read_probe": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_void_p]),
     "simsd_strerror": (ctypes.c_char_p, [c_int32]),
     "simsd_abi_version": (c_int32, []),
     "simsd_commit": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,

@@ -540,6 +540,17 @@ def stream_probe(k_cache, v_cache, sink, start=None, stop=None, stream=None):
                                         _stream_handle(stream), *ev), "simsd_stream_probe")
 
 
+def read_probe(k_cache, v_cache, sink, start=None, stop=None, stream=None):
+    """Plain vector-load read of the same two regions (no LDS), for
+    comparison with stream_probe.  Events as for stream_probe."""
+    _need(k_cache, "k_cache", torch.bfloat16)
+    _need(v_cache, "v_cache", torch.bfloat16, tuple(k_cache.shape), k_cache.device)
+    _need(sink, "sink", torch.int32, None, k_cache.device)
+    ev = [ctypes.c_void_p(0 if e is None else e.cuda_event) for e in (start, stop)]
+    L.check(L.load().simsd_read_probe(_ptr(k_cache), _ptr(v_cache), k_cache.numel() * 2, _ptr(sink),
+                                      _stream_handle(stream), *ev), "simsd_read_probe")
+
+
 def debug_mask(tau, mask_mode=L.MASK_TEMPORAL, stream=None):
     """Block visibility words [NB][2B][2] (int64 view of the uint64 bits)."""
     lib = L.load()

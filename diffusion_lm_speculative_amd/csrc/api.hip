@@ -197,7 +197,7 @@ int linear_checks(const void* x, const void* w, int64_t M, int64_t N, int64_t K)
 
 extern "C" {
 
-int simsd_abi_version(void) { return 5; }
+int simsd_abi_version(void) { return 6; }
 
 const char* simsd_strerror(int code) {
   switch (code) {

@@ -6,7 +6,8 @@
 // consecutive workgroups land on consecutive XCDs the same way), 64-key tiles
 // through a 4-stage LDS ring filled by direct-to-LDS loads of 1 KiB per wave
 // instruction, the same split of K and V rows over the waves, one barrier per
-// tile.  Each step only touches one LDS word of the tile.  The time of a
+// tile, the same staggered tile order (stream i starts at tile i mod T and
+// wraps around).  Each step only touches one LDS word of the tile.  The time of a
 // launch over the bench's cache is the most that workload's bytes can stream
 // at through this path, which the attention kernel's time is compared with.
 #include "mfma_common.hpp"
@@ -43,14 +44,16 @@ __global__ __launch_bounds__(kProbeWaves * 64) void stream_probe_kernel(const ui
     const int ii = (wave * LPW + mm) % IPT;
     goff[mm] = (ii * RPI + lane / (ROWB / 16)) * ROWB + (lane % (ROWB / 16)) * 16;
   }
+  const int rot = T > 0 ? static_cast<int>(stream % static_cast<size_t>(T)) : 0;
   auto issue = [&](int t) __attribute__((always_inline)) {
     const int st = t % kProbeStages;
+    const int tr = t + rot < T ? t + rot : t + rot - T;
 #pragma unroll
     for (int mm = 0; mm < LPW; ++mm) {
       const int ins = wave * LPW + mm;
       const bool isv = ins >= IPT;
       const int ii = isv ? ins - IPT : ins;
-      const uint16_t* base = (isv ? vt0 : kt0) + static_cast<size_t>(t) * kProbeKeys * HD;
+      const uint16_t* base = (isv ? vt0 : kt0) + static_cast<size_t>(tr) * kProbeKeys * HD;
       dma16s(base, goff[mm], sbase + (isv ? VREG : 0) + st * TILEB + ii * 1024);
     }
   };
@@ -86,8 +89,55 @@ hipError_t launch_probe(const void* k, const void* v, int sx, int sy, int len, v
                             static_cast<uint32_t*>(sink));
 }
 
+// Plain read of the same K and V regions, for comparison: vector loads of 16
+// bytes into registers (no LDS), four in flight per thread, a grid-stride
+// loop over each region with one 512-thread workgroup per CU.  Its time is
+// how fast this memory streams these bytes without the direct-to-LDS path.
+constexpr int kReadThreads = 512;
+constexpr int kReadGroups = 256;
+constexpr int kReadUnroll = 4;
+
+__global__ __launch_bounds__(kReadThreads) void read_probe_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
+                                                                  size_t n16, uint32_t* __restrict__ sink) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  uint32_t acc = 0;
+  for (int region = 0; region < 2; ++region) {
+    const uint4* src = region == 0 ? k : v;
+    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+      uint4 w[kReadUnroll];
+#pragma unroll
+      for (int u = 0; u < kReadUnroll; ++u) w[u] = src[i + u * stride];
+#pragma unroll
+      for (int u = 0; u < kReadUnroll; ++u) acc ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
+    }
+    for (; i < n16; i += stride) {
+      const uint4 w = src[i];
+      acc ^= w.x ^ w.y ^ w.z ^ w.w;
+    }
+  }
+  if (acc == 0x5eed5eedu && threadIdx.x == 0) sink[0] = acc;  // keeps the reads; not expected to happen
+}
+
 }  // namespace
 }  // namespace simsd
+
+extern "C" int simsd_read_probe(const void* k, const void* v, int64_t bytes, void* sink, void* stream,
+                                void* start_event, void* stop_event) {
+  using namespace simsd;
+  if (bytes < 0 || bytes % 16 != 0) return SIMSD_ERR_SHAPE;
+  if (bytes == 0) return SIMSD_OK;
+  if (!k || !v || !sink) return SIMSD_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(k) % 16 || reinterpret_cast<uintptr_t>(v) % 16 ||
+      reinterpret_cast<uintptr_t>(sink) % 4)
+    return SIMSD_ERR_ALIGN;
+  const hipError_t e = launch_with_events(read_probe_kernel, dim3(kReadGroups), dim3(kReadThreads), 0,
+                                          static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+                                          static_cast<hipEvent_t>(stop_event), static_cast<const uint4*>(k),
+                                          static_cast<const uint4*>(v), static_cast<size_t>(bytes / 16),
+                                          static_cast<uint32_t*>(sink));
+  return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
+}
 
 extern "C" int simsd_stream_probe(const void* k, const void* v, int32_t streams_x, int32_t streams_y, int32_t len,
                                   int32_t head_dim, void* sink, void* stream, void* start_event, void* stop_event) {

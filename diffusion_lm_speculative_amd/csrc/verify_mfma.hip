@@ -275,9 +275,24 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   const size_t blk_row = static_cast<size_t>(pl.Hkv) * HD;  // elements between block rows
   const uint16_t* kblk_b = kblk + (static_cast<size_t>(b) * twoB * pl.Hkv + kvh) * HD;
   const uint16_t* vblk_b = vblk + (static_cast<size_t>(b) * twoB * pl.Hkv + kvh) * HD;
+  // Staggered tile order: the whole prompt tiles of stream (b, kvh) start at
+  // tile (b * Hkv + kvh) mod nfull and wrap around, the ragged last tile
+  // stays last.  Streams that all started at tile 0 would read addresses a
+  // power of two apart at every step; staggered, they spread over the memory
+  // channels (a streaming probe of this ring: 3.5% faster).  The row groups
+  // of one stream keep the same order, so they still share each tile in L2.
+  // map_nfull / map_rot hold the order the loads are issued in: first for a
+  // prompt filling the cache, then for the real prompt length.
+  const int rot_key = b * pl.Hkv + kvh;
+  int map_nfull = 0, map_rot = 0;
   auto issue = [&](int ST, int t, int lim) __attribute__((always_inline)) {
     if (t >= nbt) {
-      const int kb = c0 + (t - nbt) * KT;
+      int u = t - nbt;
+      if (u < map_nfull) {
+        u += map_rot;
+        if (u >= map_nfull) u -= map_nfull;
+      }
+      const int kb = c0 + u * KT;
       const bool full = kb + KT <= lim;
       const uint16_t* ktile = kc + static_cast<size_t>(kb) * HD;
       const uint16_t* vtile = vc + static_cast<size_t>(kb) * HD;
@@ -315,6 +330,8 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   // assuming the whole cache capacity (always in bounds).
   const int c1s = min(c0 + pl.chunk, pl.p_max);
   const int nts = c1s > c0 ? (c1s - c0 + KT - 1) / KT : 0;
+  map_nfull = c1s > c0 ? (c1s - c0) / KT : 0;
+  map_rot = map_nfull > 0 ? rot_key % map_nfull : 0;
   // Only the first two go out before the query rows and stage labels have
   // landed: behind a whole ring of tile loads from every workgroup those small
   // scattered loads land about with its last tile, and the work that needs
@@ -401,13 +418,17 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   }
   // A speculative prompt tile that reaches past the prompt may hold cache
   // rows beyond P_b (any bits, NaN included, which a zero probability would
-  // not cancel in P V): drop them and issue again.  Then fill the remaining
-  // prologue stages.
+  // not cancel in P V), and a prompt shorter than the cache changes the
+  // staggered order: then drop the speculative tiles and issue again.  Then
+  // fill the remaining prologue stages.
   int issued = nspec;
-  if (nspec > nbt && c0 + (nspec - nbt) * KT > c1) {
+  const int nfull_p = c1 > c0 ? (c1 - c0) / KT : 0;
+  if (nspec > nbt && (c0 + (nspec - nbt) * KT > c1 || nfull_p != map_nfull)) {
     wait_counts<0, 15>();
     issued = nbt;
   }
+  map_nfull = nfull_p;
+  map_rot = nfull_p > 0 ? rot_key % nfull_p : 0;
   issue_range(issued, min(NPRO, T), c1);
 
   // ---- Q operands of this lane's rows, rotated in registers: k-steps i and

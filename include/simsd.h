@@ -426,10 +426,19 @@ int simsd_append_kv(const simsd_verify_desc* desc, const void* k_blk, const void
 int simsd_stream_probe(const void* k, const void* v, int32_t streams_x, int32_t streams_y, int32_t len,
                        int32_t head_dim, void* sink, void* stream, void* start_event, void* stop_event);
 
+/* Measurement only: the plain read rate of the same bytes, to compare with
+ * simsd_stream_probe.  Reads `bytes` (a multiple of 16) from k and then from
+ * v with 16-byte vector loads into registers (no LDS), 256 workgroups of 512
+ * threads in a grid-stride loop, and computes nothing.  `sink`, the events
+ * and the errors are as for simsd_stream_probe (SIMSD_ERR_SHAPE for a
+ * negative or unaligned size; 0 bytes launches nothing). */
+int simsd_read_probe(const void* k, const void* v, int64_t bytes, void* sink, void* stream, void* start_event,
+                     void* stop_event);
+
 /* Human-readable text for a return code (static storage). */
 const char* simsd_strerror(int code);
 
-/* ABI version of this header: 5. */
+/* ABI version of this header: 6. */
 int simsd_abi_version(void);
 
 #ifdef __cplusplus

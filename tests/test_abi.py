@@ -39,7 +39,7 @@ def _declared():
 def test_header_declarations_match_binding():
     decl = _declared()
     assert decl == set(L.SIGNATURES), decl ^ set(L.SIGNATURES)
-    assert len(decl) == 19
+    assert len(decl) == 20
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.simsd_abi_version() == 5
+    assert lib.simsd_abi_version() == 6
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert lib.simsd_strerror(code)
     assert lib.simsd_strerror(-99) == b"unknown error code"
@@ -269,6 +269,17 @@ def test_stream_probe_rejects_on_host(lib):
     for name in ("k", "v", "sink"):
         assert call(**{name: None}) == L.ERR_NULL, name
     assert call(k=A + 8) == L.ERR_ALIGN and call(sink=A + 2) == L.ERR_ALIGN
+
+
+@no_gpu_only
+def test_read_probe_rejects_on_host(lib):
+    def call(k=A, v=A, n=1 << 20, sink=A):
+        return lib.simsd_read_probe(k, v, n, sink, None, None, None)
+    assert call(n=100) == L.ERR_SHAPE and call(n=-16) == L.ERR_SHAPE
+    assert call(n=0, k=None, v=None, sink=None) == 0
+    for name in ("k", "v", "sink"):
+        assert call(**{name: None}) == L.ERR_NULL, name
+    assert call(v=A + 8) == L.ERR_ALIGN and call(sink=A + 2) == L.ERR_ALIGN
 
 
 @no_gpu_only
