@@ -593,10 +593,19 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
                     const uint64_t (&cmask)[ROWT]) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_c)::value;
     bf16x8 pop[ROWT][NU];
+    // The probabilities are taken against the current reference right away,
+    // alongside the maximum, for every row tile: the exponentials then do not
+    // wait for the vote.  A row's first visible key sets its reference and a
+    // score more than kRaise above it raises it; in that (rare) case the
+    // accumulators are rescaled and the tile's probabilities taken again
+    // against the new reference, so the result is the same as deciding
+    // first.  One vote covers the wave's row tiles.  The four lanes of a row
+    // reduce the same maximum, so they take the same decision.
+    float sv[ROWT][NSUB][4], pv[ROWT][NSUB][4], tmax[ROWT], lsum[ROWT];
+    bool need_any = false;
 #pragma unroll
     for (int rt = 0; rt < ROWT; ++rt) {
-      float sv[NSUB][4];
-      float tmax = -INFINITY;
+      tmax[rt] = -INFINITY;
       // this lane's keys are 16*(ks*NSUB + i) + 4g + j: one variable shift, then constant bit tests
       const uint64_t cm = MODE == 0 ? 0ull : cmask[rt] >> (16 * ks * NSUB + 4 * g);
 #pragma unroll
@@ -605,16 +614,25 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
         for (int j = 0; j < 4; ++j) {
           const bool vis = MODE == 0 || ((cm >> (16 * i + j)) & 1ull);
           const float x = vis ? sacc[rt][i][j] : -INFINITY;  // raw score; the scale is applied below
-          sv[i][j] = x;
-          tmax = fmaxf(tmax, x);
+          sv[rt][i][j] = x;
+          tmax[rt] = fmaxf(tmax[rt], x);
         }
       }
-      // a row's first visible key sets its reference; a score more than
-      // kRaise above it raises it.  The four lanes of a row reduce the same
-      // maximum, so they take the same decision.
-      const bool need = mref[rt] == -INFINITY ? tmax != -INFINITY : tmax * scale > mref[rt] + kRaise;
-      if (__any(need)) {
-        float rmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      const float muse = (mref[rt] == -INFINITY) ? 0.0f : mref[rt];
+      lsum[rt] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pv[rt][i][j] = __builtin_amdgcn_exp2f(fmaf(sv[rt][i][j], scale, -muse));
+          lsum[rt] += pv[rt][i][j];
+        }
+      need_any |= mref[rt] == -INFINITY ? tmax[rt] != -INFINITY : tmax[rt] * scale > mref[rt] + kRaise;
+    }
+    if (__any(need_any)) {
+#pragma unroll
+      for (int rt = 0; rt < ROWT; ++rt) {
+        float rmax = fmaxf(tmax[rt], __shfl_xor(tmax[rt], 16));
         rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
         const float nref = rmax * scale;
         if (mref[rt] == -INFINITY ? nref != -INFINITY : nref > mref[rt] + kRaise) {
@@ -623,19 +641,20 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
 #pragma unroll
           for (int dt = 0; dt < DTILES; ++dt) acc[rt][dt] = acc[rt][dt] * f;
           mref[rt] = nref;
+          lsum[rt] = 0.0f;
+#pragma unroll
+          for (int i = 0; i < NSUB; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              pv[rt][i][j] = __builtin_amdgcn_exp2f(fmaf(sv[rt][i][j], scale, -nref));
+              lsum[rt] += pv[rt][i][j];
+            }
         }
       }
-      const float muse = (mref[rt] == -INFINITY) ? 0.0f : mref[rt];
-      float pv[NSUB][4];
-      float lsum = 0.0f;
+    }
 #pragma unroll
-      for (int i = 0; i < NSUB; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pv[i][j] = __builtin_amdgcn_exp2f(fmaf(sv[i][j], scale, -muse));
-          lsum += pv[i][j];
-        }
-      lpart[rt] += lsum;
+    for (int rt = 0; rt < ROWT; ++rt) {
+      lpart[rt] += lsum[rt];
       // P^T operand of k-step u: keys 4g..4g+3 of subtile 2u, then of 2u+1;
       // subtiles of other waves contribute zeros.
 #pragma unroll
@@ -647,7 +666,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
           const int i = 2 * u + h2 - ks * NSUB;
           const int ic = i < 0 ? 0 : (i >= NSUB ? NSUB - 1 : i);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pb[4 * h2 + j] = static_cast<__bf16>((i >= 0 && i < NSUB) ? pv[ic][j] : 0.0f);
+          for (int j = 0; j < 4; ++j) pb[4 * h2 + j] = static_cast<__bf16>((i >= 0 && i < NSUB) ? pv[rt][ic][j] : 0.0f);
         }
         pop[rt][uu] = bf16x8{pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
       }
