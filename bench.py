@@ -11,8 +11,9 @@ cache alternate so no step reads K/V that a previous step left in cache.
 
 Prints ONE JSON line.  `value` is verified candidates per second
 (batch * gamma per step).  `roofline` prices the verification call against
-the HBM peak using the algorithmic K/V bytes and its HIP-event duration on
-the launch stream, the events taken inside the timed loop on every
+the HBM peak using its algorithmic bytes (the K/V stream, each key and value
+once, plus the block rows' Q, K and V and the outputs; `kv_frac` gives the
+K/V stream alone) and its HIP-event duration on the launch stream, the events taken inside the timed loop on every
 --event-stride-th step (an event packet adds a few microseconds to the
 step it sits in, so recording them on every step would understate the
 throughput); `cpu_baseline` times the fp64 oracle on a bounded sample of the
@@ -447,7 +448,15 @@ def main():
     a_avg = sum(accept_ms) / len(accept_ms)
     ms_per_step = wall * 1e3 / args.steps
     kv_bytes = w.kv_bytes()
-    achieved_gbs = kv_bytes / (v_avg * 1e-3) / 1e9
+    # bytes the call must move besides the K/V stream: the block rows' Q, K
+    # and V, the output rows and lse
+    esz = 2
+    q_bytes = w.NB * 2 * w.B * w.Hq * w.d * esz
+    alg_parts = {"kv_cache": kv_bytes, "q_blk": q_bytes, "kv_blk": 2 * w.NB * 2 * w.B * w.Hkv * w.d * esz,
+                 "out": q_bytes, "lse": w.NB * 2 * w.B * w.Hq * 4}
+    alg_bytes = sum(alg_parts.values())
+    achieved_gbs = alg_bytes / (v_avg * 1e-3) / 1e9
+    kv_gbs = kv_bytes / (v_avg * 1e-3) / 1e9
     desc = sd.make_desc(sets[0]["t"]["q_blk"], sets[0]["t"]["k_blk"], sets[0]["t"]["k_cache"], rope_base=w.rope_base)
     traffic = measured_traffic()
 
@@ -481,8 +490,9 @@ def main():
                    "prompt_len": w.P, "B": w.B, "gamma": gamma, "vocab": VOCAB, "kv_chunk": 0},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "verify_mfma_kernel (+ lse merge when split)", "algorithmic_bytes": kv_bytes},
-        "kv_tb_per_s": achieved_gbs / 1e3,
+                     "kernel": "verify_mfma_kernel (+ lse merge when split)", "algorithmic_bytes": alg_bytes,
+                     "algorithmic_parts": alg_parts, "kv_frac": kv_gbs / HBM_PEAK_GBS},
+        "kv_tb_per_s": kv_gbs / 1e3,
         "verify_us": {"mean": v_avg * 1e3, "median": verify_ms[len(verify_ms) // 2] * 1e3,
                       "p90": verify_ms[int(len(verify_ms) * 0.9)] * 1e3, "samples": len(verify_ms),
                       "event_stride": stride, "events": "bound to the attention kernel's own dispatch"},
