@@ -293,20 +293,29 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
         if (u >= map_nfull) u -= map_nfull;
       }
       const int kb = c0 + u * KT;
-      const bool full = kb + KT <= lim;
       const uint16_t* ktile = kc + static_cast<size_t>(kb) * HD;
       const uint16_t* vtile = vc + static_cast<size_t>(kb) * HD;
+      // A whole tile (the wave-uniform common case) takes the per-lane
+      // offsets as they are; kept apart from the clamped form so the
+      // compiler branches instead of computing both and selecting.
+      if (__builtin_expect(kb + KT <= lim, 1)) {
 #pragma unroll
-      for (int mm = 0; mm < LPW; ++mm) {
-        const int ins = wave * LPW + mm;
-        const bool isv = ins >= L::IPT;
-        const int ii = isv ? ins - L::IPT : ins;
-        uint32_t off = goff[mm];
-        if (!full) {
-          const int row = static_cast<int>(off / L::ROWB);
-          off = (min(kb + row, lim - 1) - kb) * L::ROWB + off % L::ROWB;
+        for (int mm = 0; mm < LPW; ++mm) {
+          const int ins = wave * LPW + mm;
+          const bool isv = ins >= L::IPT;
+          const int ii = isv ? ins - L::IPT : ins;
+          dma16s(isv ? vtile : ktile, goff[mm], sbase + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024);
         }
-        dma16s(isv ? vtile : ktile, off, sbase + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024);
+      } else {
+#pragma unroll
+        for (int mm = 0; mm < LPW; ++mm) {
+          const int ins = wave * LPW + mm;
+          const bool isv = ins >= L::IPT;
+          const int ii = isv ? ins - L::IPT : ins;
+          const int row = static_cast<int>(goff[mm] / L::ROWB);
+          const uint32_t off = (min(kb + row, lim - 1) - kb) * L::ROWB + goff[mm] % L::ROWB;
+          dma16s(isv ? vtile : ktile, off, sbase + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024);
+        }
       }
     } else {
 #pragma unroll
@@ -516,13 +525,19 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
 
   // K operands of this wave's keys of the tile in stage ST, all read at once
   // (their latency is then paid once, behind the softmax of the previous tile).
-  auto kread = [&](int st, bf16x8 (&kop)[NSUB][KSTEPS]) __attribute__((always_inline)) {
-    const int sto = st * L::TILEB;
+  // With the stage known at compile time (SC >= 0) its offset is part of the
+  // instructions' immediate offset; otherwise it is added at run time.
+  auto kread = [&](auto stage_c, int st, bf16x8 (&kop)[NSUB][KSTEPS]) __attribute__((always_inline)) {
+    constexpr int SC = decltype(stage_c)::value;
 #pragma unroll
     for (int i = 0; i < NSUB; ++i)
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-        kop[i][kk] = *reinterpret_cast<const bf16x8*>(smem + (kofs[kk] + sto) + i * 16 * L::ROWB);
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        if constexpr (SC >= 0)
+          kop[i][kk] = *reinterpret_cast<const bf16x8*>(smem + kofs[kk] + (SC * L::TILEB + i * 16 * L::ROWB));
+        else
+          kop[i][kk] = *reinterpret_cast<const bf16x8*>(smem + (kofs[kk] + st * L::TILEB) + i * 16 * L::ROWB);
+      }
   };
   // S^T of those keys for every row tile (each K operand feeds ROWT MFMAs).
   auto kmma = [&](const bf16x8 (&kop)[NSUB][KSTEPS], f32x4 (&sacc)[ROWT][NSUB]) __attribute__((always_inline)) {
@@ -541,20 +556,21 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   };
 
   // V^T operands of the tile in stage ST (the reads complete during the softmax).
-  auto vread = [&](int st, bf16x8 (&vop)[DTILES][NU]) __attribute__((always_inline)) {
-    const uint32_t sto = st * L::TILEB;
+  auto vread = [&](auto stage_c, int st, bf16x8 (&vop)[DTILES][NU]) __attribute__((always_inline)) {
+    constexpr int SC = decltype(stage_c)::value;
+    constexpr int SO = SC >= 0 ? SC * L::TILEB : 0;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt)
 #pragma unroll
       for (int uu = 0; uu < NU; ++uu) {
-        const uint32_t va = vadr[dt] + sto;
+        const uint32_t va = SC >= 0 ? vadr[dt] : vadr[dt] + st * L::TILEB;
         bf16x4 lo, hi;
         if (uu == 0) {
-          lo = tr_read<0>(va);
-          hi = tr_read<16 * L::ROWB>(va);
+          lo = tr_read<SO>(va);
+          hi = tr_read<SO + 16 * L::ROWB>(va);
         } else {
-          lo = tr_read<32 * L::ROWB>(va);
-          hi = tr_read<48 * L::ROWB>(va);
+          lo = tr_read<SO + 32 * L::ROWB>(va);
+          hi = tr_read<SO + 48 * L::ROWB>(va);
         }
         vop[dt][uu] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
@@ -734,8 +750,11 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   // in use.  (Keeping tile t+1 resident too, to run its score MFMAs under the
   // softmax of tile t, leaves two in flight and measured 0.3-2% slower on
   // every workload.)
-  auto step = [&](auto mode_c, int t) __attribute__((always_inline)) {
-    const int K = t % NSTAGE;
+  // Step t.  stage_c: the ring stage of tile t when the caller knows it at
+  // compile time (IC<-1>: taken from t at run time).
+  auto step = [&](auto mode_c, auto stage_c, int t) __attribute__((always_inline)) {
+    constexpr int SC = decltype(stage_c)::value;
+    const int K = SC >= 0 ? SC : t % NSTAGE;
     if (t > 0) {
       const int later = T - 1 - t;  // tiles after t that may still be in flight (at most NSTAGE - 2)
       if (later >= NSTAGE - 2)
@@ -748,9 +767,9 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       if (t < nbt) rotate_block(K, t);
     }
     bf16x8 kop[NSUB][KSTEPS];
-    kread(K, kop);
+    kread(stage_c, K, kop);
     bf16x8 vop[DTILES][NU];
-    vread(K, vop);
+    vread(stage_c, K, vop);
     kmma(kop, sb);
     if (decltype(mode_c)::value == 0) {
       const uint64_t cm[ROWT] = {};
@@ -767,14 +786,26 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   // block tiles, then whole prompt tiles, then the rest through the masked
   // path
   if (nbt == 1) {
-    step(IC<1>{}, 0);
+    step(IC<1>{}, IC<-1>{}, 0);
   } else if (nbt == 2) {
-    step(IC<1>{}, 0);
-    step(IC<1>{}, 1);
+    step(IC<1>{}, IC<-1>{}, 0);
+    step(IC<1>{}, IC<-1>{}, 1);
   }
+  // whole prompt tiles in groups of NSTAGE whose ring stages are known at
+  // compile time (the stage of tile t is t mod NSTAGE), then the rest of them
+  // and the ragged last tile with the stage taken at run time
   int t0 = nbt;
-  for (; t0 < nbt + nfull; ++t0) step(IC<0>{}, t0);
-  for (; t0 < T; ++t0) step(IC<1>{}, t0);
+  const int tw = nbt + nfull;
+  if (t0 % NSTAGE == 0) {
+    for (; t0 + NSTAGE <= tw; t0 += NSTAGE) {
+      step(IC<0>{}, IC<0>{}, t0);
+      step(IC<0>{}, IC<1>{}, t0 + 1);
+      step(IC<0>{}, IC<2>{}, t0 + 2);
+      if constexpr (NSTAGE > 3) step(IC<0>{}, IC<NSTAGE - 1>{}, t0 + 3);
+    }
+  }
+  for (; t0 < tw; ++t0) step(IC<0>{}, IC<-1>{}, t0);
+  for (; t0 < T; ++t0) step(IC<1>{}, IC<-1>{}, t0);
 
   // ---- combine the key splits of each row (through the drained ring)
   wait_counts<0, 15>();  // no ring load may land after the workgroup ends
