@@ -42,9 +42,9 @@ def _lib_loaded():
 
 @pytest.mark.parametrize("name,expect", [
     # workload: (rows per workgroup, row groups, key split, row tiles, stages, qsep, block rows, splits)
-    # (1024-key prompts of 16 sequences x 8 KV heads: two 512-key splits fill the 256 CUs; the 16k
-    # prompts are split at the 8192-key cap)
-    ("sdar8b_p1024_b4", (32, 1, 4, 1, 4, 1, 16, 2)),
+    # (1024-key prompts: one split, as splits of fewer than 16 tiles cost more in the merge than
+    # they save; the 16k prompts are split at the 8192-key cap)
+    ("sdar8b_p1024_b4", (32, 1, 4, 1, 4, 1, 16, 1)),
     ("sdar8b_p4096_b8", (64, 1, 2, 1, 4, 1, 16, 1)),
     ("sdar8b_p8192_b32", (128, 2, 2, 2, 4, 0, 0, 2)),
     ("sdar8b_var16k_b16_accept", (128, 1, 2, 2, 4, 0, 32, 2)),
@@ -97,6 +97,16 @@ def test_plan_invariants_over_shapes(d, rope_mode):
             assert LDS_PER_CU // (p["lds_bytes"] + LDS_RESERVE) == LDS_PER_CU // without, (B, G, p)
         seen.add(r > 0)
     assert seen == {True, False}
+
+
+def test_default_splits_keep_at_least_16_tiles():
+    for NB, Hkv, p_max in ((16, 8, 1024), (8, 8, 1024), (16, 8, 2048), (1, 2, 8192), (1, 8, 65536), (32, 8, 4096)):
+        p = sd.verify_plan(_desc(NB, 4 * Hkv, Hkv, 128, 8, p_max))
+        assert p["nsplit"] == 1 or p["chunk"] // 64 >= 16, (NB, Hkv, p_max, p)
+        assert p["nsplit"] * p["chunk"] >= p_max
+    # an explicit kv_chunk is taken as given
+    p = sd.verify_plan(_desc(16, 32, 8, 128, 4, 1024, kv_chunk=256))
+    assert p["nsplit"] == 4 and p["chunk"] == 256
 
 
 def test_plan_rejects_like_the_call():
