@@ -82,5 +82,12 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t
                : "memory");
 }
 
+// dma16s with the non-temporal cache-policy bit, for data a call reads once.
+__device__ __forceinline__ void dma16s_nt(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
 }  // namespace
 }  // namespace simsd

@@ -7,7 +7,9 @@
 // through a 4-stage LDS ring filled by direct-to-LDS loads of 1 KiB per wave
 // instruction, the same split of K and V rows over the waves, one barrier per
 // tile, the same staggered tile order (stream i starts at tile i mod T and
-// wraps around).  Each step only touches one LDS word of the tile.  The time of a
+// wraps around), the same cache policy (non-temporal loads once K and V
+// together reach the last-level cache's size).  Each step only touches one
+// LDS word of the tile.  The time of a
 // launch over the bench's cache is the most that workload's bytes can stream
 // at through this path, which the attention kernel's time is compared with.
 #include "mfma_common.hpp"
@@ -18,8 +20,9 @@ namespace {
 constexpr int kProbeKeys = 64;  // keys per tile
 constexpr int kProbeStages = 4;
 constexpr int kProbeWaves = 8;
+constexpr long long kProbeLastLevelCache = 256ll << 20;  // MI355X Infinity Cache bytes
 
-template <int HD>
+template <int HD, bool NTL>
 __global__ __launch_bounds__(kProbeWaves * 64) void stream_probe_kernel(const uint16_t* __restrict__ kc,
                                                                          const uint16_t* __restrict__ vc, int len,
                                                                          uint32_t* __restrict__ sink) {
@@ -54,7 +57,10 @@ __global__ __launch_bounds__(kProbeWaves * 64) void stream_probe_kernel(const ui
       const bool isv = ins >= IPT;
       const int ii = isv ? ins - IPT : ins;
       const uint16_t* base = (isv ? vt0 : kt0) + static_cast<size_t>(tr) * kProbeKeys * HD;
-      dma16s(base, goff[mm], sbase + (isv ? VREG : 0) + st * TILEB + ii * 1024);
+      if constexpr (NTL)
+        dma16s_nt(base, goff[mm], sbase + (isv ? VREG : 0) + st * TILEB + ii * 1024);
+      else
+        dma16s(base, goff[mm], sbase + (isv ? VREG : 0) + st * TILEB + ii * 1024);
     }
   };
   for (int t = 0; t < kProbeStages && t < T; ++t) issue(t);
@@ -77,12 +83,12 @@ __global__ __launch_bounds__(kProbeWaves * 64) void stream_probe_kernel(const ui
   if (acc == 0x5eed5eedu && tid == 0) sink[0] = acc;  // keeps the reads; not expected to happen
 }
 
-template <int HD>
+template <int HD, bool NTL>
 hipError_t launch_probe(const void* k, const void* v, int sx, int sy, int len, void* sink, hipStream_t s,
                         PassEvents ev) {
-  auto kern = stream_probe_kernel<HD>;
+  auto kern = stream_probe_kernel<HD, NTL>;
   const int lds = 2 * kProbeStages * kProbeKeys * HD * 2;
-  const hipError_t e = allow_dynamic_lds<stream_probe_kernel<HD>>(lds);
+  const hipError_t e = allow_dynamic_lds<stream_probe_kernel<HD, NTL>>(lds);
   if (e != hipSuccess) return e;
   return launch_with_events(kern, dim3(sx, sy), dim3(kProbeWaves * 64), lds, s, ev.start, ev.stop,
                             static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), len,
@@ -91,14 +97,25 @@ hipError_t launch_probe(const void* k, const void* v, int sx, int sy, int len, v
 
 // Plain read of the same K and V regions, for comparison: vector loads of 16
 // bytes into registers (no LDS), four in flight per thread, a grid-stride
-// loop over each region with one 512-thread workgroup per CU.  Its time is
-// how fast this memory streams these bytes without the direct-to-LDS path.
+// loop over each region with one 512-thread workgroup per CU, non-temporal
+// by the same rule as the attention kernel's tiles.  Its time is how fast
+// this memory streams these bytes without the direct-to-LDS path.
 constexpr int kReadThreads = 512;
 constexpr int kReadGroups = 256;
 constexpr int kReadUnroll = 4;
 
+template <bool NTL>
 __global__ __launch_bounds__(kReadThreads) void read_probe_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                                                   size_t n16, uint32_t* __restrict__ sink) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  auto ld = [](const uint4* p) -> uint4 {
+    if constexpr (NTL) {
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+      return make_uint4(w.x, w.y, w.z, w.w);
+    } else {
+      return *p;
+    }
+  };
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
   uint32_t acc = 0;
   for (int region = 0; region < 2; ++region) {
@@ -107,12 +124,12 @@ __global__ __launch_bounds__(kReadThreads) void read_probe_kernel(const uint4* _
     for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
       uint4 w[kReadUnroll];
 #pragma unroll
-      for (int u = 0; u < kReadUnroll; ++u) w[u] = src[i + u * stride];
+      for (int u = 0; u < kReadUnroll; ++u) w[u] = ld(src + i + u * stride);
 #pragma unroll
       for (int u = 0; u < kReadUnroll; ++u) acc ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
     }
     for (; i < n16; i += stride) {
-      const uint4 w = src[i];
+      const uint4 w = ld(src + i);
       acc ^= w.x ^ w.y ^ w.z ^ w.w;
     }
   }
@@ -131,7 +148,9 @@ extern "C" int simsd_read_probe(const void* k, const void* v, int64_t bytes, voi
   if (reinterpret_cast<uintptr_t>(k) % 16 || reinterpret_cast<uintptr_t>(v) % 16 ||
       reinterpret_cast<uintptr_t>(sink) % 4)
     return SIMSD_ERR_ALIGN;
-  const hipError_t e = launch_with_events(read_probe_kernel, dim3(kReadGroups), dim3(kReadThreads), 0,
+  // non-temporal loads by the attention kernel's rule (K and V together at least the last-level cache)
+  const hipError_t e = launch_with_events(2 * bytes >= kProbeLastLevelCache ? read_probe_kernel<true> : read_probe_kernel<false>,
+                                          dim3(kReadGroups), dim3(kReadThreads), 0,
                                           static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
                                           static_cast<hipEvent_t>(stop_event), static_cast<const uint4*>(k),
                                           static_cast<const uint4*>(v), static_cast<size_t>(bytes / 16),
@@ -152,7 +171,14 @@ extern "C" int simsd_stream_probe(const void* k, const void* v, int32_t streams_
     return SIMSD_ERR_ALIGN;
   const PassEvents ev{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = head_dim == 128 ? launch_probe<128>(k, v, streams_x, streams_y, len, sink, s, ev)
-                                       : launch_probe<64>(k, v, streams_x, streams_y, len, sink, s, ev);
+  // the attention kernel's rule: non-temporal tile loads when K and V reach the last-level cache's size
+  const bool nt = 4ll * streams_x * streams_y * len * head_dim >= kProbeLastLevelCache;
+  hipError_t e;
+  if (head_dim == 128)
+    e = nt ? launch_probe<128, true>(k, v, streams_x, streams_y, len, sink, s, ev)
+           : launch_probe<128, false>(k, v, streams_x, streams_y, len, sink, s, ev);
+  else
+    e = nt ? launch_probe<64, true>(k, v, streams_x, streams_y, len, sink, s, ev)
+           : launch_probe<64, false>(k, v, streams_x, streams_y, len, sink, s, ev);
   return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
 }

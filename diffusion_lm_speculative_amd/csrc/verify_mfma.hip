@@ -141,7 +141,7 @@ struct Smem {
   }
 };
 
-template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT, bool BSEP>
+template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT, bool BSEP, bool KVNT>
 __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, VerifyArgs a) {
   using L = Layout<HD>;
   using S = Smem<HD, NSTAGE, QSEP>;
@@ -298,13 +298,19 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       // A whole tile (the wave-uniform common case) takes the per-lane
       // offsets as they are; kept apart from the clamped form so the
       // compiler branches instead of computing both and selecting.
+      // (KVNT: the non-temporal form, for a call whose K/V region is at
+      // least the size of the last-level cache)
       if (__builtin_expect(kb + KT <= lim, 1)) {
 #pragma unroll
         for (int mm = 0; mm < LPW; ++mm) {
           const int ins = wave * LPW + mm;
           const bool isv = ins >= L::IPT;
           const int ii = isv ? ins - L::IPT : ins;
-          dma16s(isv ? vtile : ktile, goff[mm], sbase + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024);
+          const uint32_t dst = sbase + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024;
+          if constexpr (KVNT)
+            dma16s_nt(isv ? vtile : ktile, goff[mm], dst);
+          else
+            dma16s(isv ? vtile : ktile, goff[mm], dst);
         }
       } else {
 #pragma unroll
@@ -314,7 +320,11 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
           const int ii = isv ? ins - L::IPT : ins;
           const int row = static_cast<int>(goff[mm] / L::ROWB);
           const uint32_t off = (min(kb + row, lim - 1) - kb) * L::ROWB + goff[mm] % L::ROWB;
-          dma16s(isv ? vtile : ktile, off, sbase + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024);
+          const uint32_t dst = sbase + (isv ? VREG : KREG) + ST * L::TILEB + ii * 1024;
+          if constexpr (KVNT)
+            dma16s_nt(isv ? vtile : ktile, off, dst);
+          else
+            dma16s(isv ? vtile : ktile, off, dst);
         }
       }
     } else {
@@ -886,12 +896,12 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   }
 }
 
-template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT, bool BSEP>
+template <int HD, int RW, int KSPLIT, int NSTAGE, bool QSEP, int ROWT, bool BSEP, bool KVNT>
 hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
-  auto kern = verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT, BSEP>;
+  auto kern = verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT, BSEP, KVNT>;
   const size_t lds = mfma_lds_bytes(HD, NSTAGE, pl.tab_rows, RW * ROWT * 16, QSEP, pl.blk_rows);
   // the table and staged-row sizes vary per call: allow the whole LDS once
-  const hipError_t e = allow_dynamic_lds<verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT, BSEP>>(kLdsMax);
+  const hipError_t e = allow_dynamic_lds<verify_mfma_kernel<HD, RW, KSPLIT, NSTAGE, QSEP, ROWT, BSEP, KVNT>>(kLdsMax);
   if (e != hipSuccess) return e;
   if (lds > static_cast<size_t>(kLdsMax)) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(pl.Hkv), static_cast<unsigned>(pl.NB) * static_cast<unsigned>(pl.nrg),
@@ -903,21 +913,21 @@ hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEv
 // rows one 16-row tile per wave with the keys split over 4 or 2 waves; 128
 // rows four row waves of two row tiles each, keys split over 2 waves, so
 // every K and V operand read from LDS feeds two MFMAs.
-template <int HD, int NSTAGE, bool QSEP, bool BSEP>
+template <int HD, int NSTAGE, bool QSEP, bool BSEP, bool KVNT>
 hipError_t launch_rows(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
   switch (pl.rows_wg / 16) {
-    case 1: return launch_cfg<HD, 1, 4, NSTAGE, QSEP, 1, BSEP>(pl, a, s, ev);
-    case 2: return launch_cfg<HD, 2, 4, NSTAGE, QSEP, 1, BSEP>(pl, a, s, ev);
-    case 4: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 1, BSEP>(pl, a, s, ev);
-    case 8: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 2, BSEP>(pl, a, s, ev);
+    case 1: return launch_cfg<HD, 1, 4, NSTAGE, QSEP, 1, BSEP, KVNT>(pl, a, s, ev);
+    case 2: return launch_cfg<HD, 2, 4, NSTAGE, QSEP, 1, BSEP, KVNT>(pl, a, s, ev);
+    case 4: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 1, BSEP, KVNT>(pl, a, s, ev);
+    case 8: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 2, BSEP, KVNT>(pl, a, s, ev);
     default: return hipErrorInvalidConfiguration;
   }
 }
 
-template <int HD, int NSTAGE, bool QSEP>
+template <int HD, int NSTAGE, bool QSEP, bool KVNT>
 hipError_t launch_stages(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
-  return pl.blk_rows > 0 ? launch_rows<HD, NSTAGE, QSEP, true>(pl, a, s, ev)
-                         : launch_rows<HD, NSTAGE, QSEP, false>(pl, a, s, ev);
+  return pl.blk_rows > 0 ? launch_rows<HD, NSTAGE, QSEP, true, KVNT>(pl, a, s, ev)
+                         : launch_rows<HD, NSTAGE, QSEP, false, KVNT>(pl, a, s, ev);
 }
 
 }  // namespace
@@ -931,13 +941,24 @@ size_t mfma_lds_bytes(int hd, int nstage, int tab_rows, int rows_wg, bool qsep, 
          2 * static_cast<size_t>(blk_rows) * hd * 2 + static_cast<size_t>(tab_rows) * (hd / 2) * sizeof(float2);
 }
 
-hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
-  if (pl.d == 64) return launch_stages<64, 4, true>(pl, a, s, ev);
-  if (pl.qsep) return launch_stages<128, 4, true>(pl, a, s, ev);
-  if (pl.nstage == 4) return launch_stages<128, 4, false>(pl, a, s, ev);
+namespace {
+
+template <bool KVNT>
+hipError_t launch_policy(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
+  if (pl.d == 64) return launch_stages<64, 4, true, KVNT>(pl, a, s, ev);
+  if (pl.qsep) return launch_stages<128, 4, true, KVNT>(pl, a, s, ev);
+  if (pl.nstage == 4) return launch_stages<128, 4, false, KVNT>(pl, a, s, ev);
   // the planner gives the block rows a region of their own only beside a 4-stage ring
   if (pl.blk_rows > 0) return hipErrorInvalidConfiguration;
-  return launch_rows<128, 3, false, false>(pl, a, s, ev);
+  return launch_rows<128, 3, false, false, KVNT>(pl, a, s, ev);
+}
+
+}  // namespace
+
+hipError_t launch_verify_mfma(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
+  // the tiles' cache policy is a template parameter: a run-time choice
+  // inside the issue loop changed the code of the whole ring schedule
+  return pl.kv_stream ? launch_policy<true>(pl, a, s, ev) : launch_policy<false>(pl, a, s, ev);
 }
 
 }  // namespace simsd

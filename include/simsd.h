@@ -146,6 +146,9 @@ typedef struct {
   int32_t nsplit;     /* prompt splits per (sequence, KV head) */
   int32_t chunk;      /* prompt keys per split */
   int32_t lds_bytes;  /* MFMA: dynamic LDS per workgroup (else 0) */
+  int32_t kv_stream;  /* MFMA: 1 = the prompt K/V tiles are loaded non-temporal,
+                         chosen when NB * Hkv * p_max * d * 2 * 2 bytes (K and V
+                         in bf16) reach 256 MiB, the last-level cache (else 0) */
 } simsd_verify_plan;
 
 int simsd_verify_plan_info(const simsd_verify_desc* desc, simsd_verify_plan* plan);
@@ -418,7 +421,8 @@ int simsd_append_kv(const simsd_verify_desc* desc, const void* k_blk, const void
  * Streams k and v ([streams_y][streams_x][len][head_dim] bf16 each, the
  * prompt-cache layout with streams_x = KV heads and streams_y = sequences;
  * len a multiple of 64, head_dim 64 or 128) through the attention kernel's
- * 4-stage ring of direct-to-LDS loads, one 8-wave workgroup per stream, and
+ * 4-stage ring of direct-to-LDS loads, one 8-wave workgroup per stream, with
+ * its cache policy (non-temporal when k and v together reach 256 MiB), and
  * computes nothing.  `sink` (4 bytes, device) is written only on a condition
  * that is not expected to happen.  The events are bound to the kernel as in
  * simsd_verify_attn_timed (NULL for none).  Errors: SIMSD_ERR_SHAPE
@@ -429,7 +433,8 @@ int simsd_stream_probe(const void* k, const void* v, int32_t streams_x, int32_t 
 /* Measurement only: the plain read rate of the same bytes, to compare with
  * simsd_stream_probe.  Reads `bytes` (a multiple of 16) from k and then from
  * v with 16-byte vector loads into registers (no LDS), 256 workgroups of 512
- * threads in a grid-stride loop, and computes nothing.  `sink`, the events
+ * threads in a grid-stride loop, non-temporal by the same rule, and computes
+ * nothing.  `sink`, the events
  * and the errors are as for simsd_stream_probe (SIMSD_ERR_SHAPE for a
  * negative or unaligned size; 0 bytes launches nothing). */
 int simsd_read_probe(const void* k, const void* v, int64_t bytes, void* sink, void* stream, void* start_event,
@@ -438,7 +443,7 @@ int simsd_read_probe(const void* k, const void* v, int64_t bytes, void* sink, vo
 /* Human-readable text for a return code (static storage). */
 const char* simsd_strerror(int code);
 
-/* ABI version of this header: 6. */
+/* ABI version of this header: 7. */
 int simsd_abi_version(void);
 
 #ifdef __cplusplus

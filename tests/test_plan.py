@@ -109,6 +109,27 @@ def test_default_splits_keep_at_least_16_tiles():
     assert p["nsplit"] == 4 and p["chunk"] == 256
 
 
+@pytest.mark.parametrize("name,expect", [
+    ("sdar8b_p1024_b4", 0),           # 67 MB of K/V: fits the last-level cache, kept there between calls
+    ("sdar8b_p4096_b8", 1),           # 537 MB
+    ("sdar8b_p8192_b32", 1),          # 256 MiB exactly
+    ("sdar8b_var16k_b16_accept", 1),  # 4.3 GB of capacity
+])
+def test_non_temporal_kv_loads_per_workload(name, expect):
+    assert _plan_of(synth.WORKLOADS[name])["kv_stream"] == expect
+
+
+def test_non_temporal_kv_loads_threshold():
+    # K and V in bf16: NB * Hkv * p_max * d * 4 bytes against 256 MiB
+    at = sd.verify_plan(_desc(8, 32, 8, 128, 8, 8192))      # 2^28 bytes
+    below = sd.verify_plan(_desc(8, 32, 8, 128, 8, 8128))   # one tile less per stream
+    assert at["kv_stream"] == 1 and below["kv_stream"] == 0
+    d64 = sd.verify_plan(_desc(8, 32, 8, 64, 8, 16384))     # the same bytes at head dim 64
+    assert d64["kv_stream"] == 1
+    valu = sd.verify_plan(_desc(8, 32, 8, 128, 8, 8192, impl=L.IMPL_VALU))
+    assert valu["kv_stream"] == 0  # only the MFMA kernel streams through the DMA ring
+
+
 def test_plan_rejects_like_the_call():
     bad = _desc(1, 3, 2, 128, 4, 64)  # Hq not a multiple of Hkv
     with pytest.raises(L.SimsdError):
