@@ -106,8 +106,9 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
     // with identical outputs.  A region that fits keeps the default policy,
     // under which the next call over the same cache still finds it there
     // (batch 16 x 1024 keys: 20.2 us against 21.4 us non-temporal).
-    const int64_t kv_bytes = static_cast<int64_t>(pl.NB) * pl.Hkv * pl.p_max * pl.d * 2 * 2;
-    pl.kv_stream = kv_bytes >= kLastLevelCache ? 1 : 0;
+    // (in double: the product of the descriptor's extremes overflows int64)
+    const double kv_bytes = static_cast<double>(pl.NB) * pl.Hkv * pl.p_max * pl.d * 2.0 * 2.0;
+    pl.kv_stream = kv_bytes >= static_cast<double>(kLastLevelCache) ? 1 : 0;
   } else {
     pl.rowt = 1;
     pl.threads = 256;
