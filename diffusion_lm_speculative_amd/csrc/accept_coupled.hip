@@ -16,7 +16,9 @@
 //   1. row argmax, grid (NB * gamma rows, chunks of a row): the workgroup of
 //      stage t of sequence b finds the position k with tau[k] = t, streams
 //      its chunk of p[b][k] and E[b][k] (16-byte loads; the rows are this
-//      call's bytes: 2 * V * 4 per walked stage) and reduces its best
+//      call's bytes: 2 * V * 4 per walked stage, read once, so when they add
+//      up to at least the last-level cache they are loaded with the
+//      non-temporal bit) and reduces its best
 //      (p, E, index) over lanes and waves with the exact comparison.
 //   2. walk, one workgroup per sequence: the reduction of every walked row's
 //      chunk winners (stages spread over the waves), then validation (labels
@@ -75,6 +77,22 @@ __device__ __forceinline__ int stage_position(const int32_t* tau_b, int B, int t
   return hit ? __builtin_ctzll(hit) : -1;
 }
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// One 16-byte load, non-temporal when NT.
+template <bool NT>
+__device__ __forceinline__ float4 load4(const float* ptr) {
+  if constexpr (NT) {
+    const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(ptr));
+    return make_float4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const float4*>(ptr);
+  }
+}
+
+// NT: the row loads carry the non-temporal bit (a template parameter, so the
+// issue loop's code is the same for both policies).
+template <bool NT>
 __global__ __launch_bounds__(kCoThreads) void coupled_argmax_kernel(const float* __restrict__ p,
                                                                      const float* __restrict__ e,
                                                                      const int32_t* __restrict__ tau, int B,
@@ -103,8 +121,8 @@ __global__ __launch_bounds__(kCoThreads) void coupled_argmax_kernel(const float*
       for (int u = 0; u < kU; ++u) {
         const int64_t v = v0 + 4 * (tid + u * kCoThreads);
         const int64_t vc = v < v1 ? v : v1 - 4;
-        p4[u] = *reinterpret_cast<const float4*>(pr + vc);
-        e4[u] = *reinterpret_cast<const float4*>(er + vc);
+        p4[u] = load4<NT>(pr + vc);
+        e4[u] = load4<NT>(er + vc);
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -228,8 +246,18 @@ hipError_t launch_accept_coupled(const float* p, const float* e, const int32_t* 
   const int nch = coupled_chunks(V);
   float4* part = static_cast<float4*>(workspace);
   if (gamma > 0) {
-    hipLaunchKernelGGL(coupled_argmax_kernel, dim3(NB * gamma, nch), dim3(kCoThreads), 0, s, p, e, tau, B, gamma,
-                       V, nch, part);
+    // Rows read once per call: at batch 64, gamma 16 (1.24 GB of p and E)
+    // the non-temporal bit took the argmax launch from 220 to 200 us (paired
+    // runs, identical outputs).  Rows that fit the last-level cache keep the
+    // default policy (a producer's writes may still be there).
+    const double bytes = static_cast<double>(NB) * gamma * static_cast<double>(V) * 8.0;
+    const bool nt = bytes >= static_cast<double>(kLastLevelCache);
+    if (nt)
+      hipLaunchKernelGGL(coupled_argmax_kernel<true>, dim3(NB * gamma, nch), dim3(kCoThreads), 0, s, p, e, tau, B,
+                         gamma, V, nch, part);
+    else
+      hipLaunchKernelGGL(coupled_argmax_kernel<false>, dim3(NB * gamma, nch), dim3(kCoThreads), 0, s, p, e, tau, B,
+                         gamma, V, nch, part);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

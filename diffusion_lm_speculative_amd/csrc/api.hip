@@ -13,7 +13,6 @@ constexpr int kNumCUs = 256;        // MI355X compute units
 constexpr size_t kLdsPerCu = 163840;  // bytes of LDS per CU (and per workgroup at most)
 constexpr int kMaxChunk = 8192;     // default split length cap (tail of ragged prompts)
 constexpr int kMinSplitTiles = 16;  // default splits of fewer tiles cost more in the merge than they save
-constexpr int64_t kLastLevelCache = int64_t{256} << 20;  // MI355X Infinity Cache bytes
 constexpr int kMaxQHeads = 65536;   // query heads per layer accepted by the planner
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }

@@ -263,6 +263,9 @@ hipError_t launch_linear(const uint16_t* x, const uint16_t* w, int64_t M, int N,
                          uint16_t* out0, int ld0, uint16_t* out1, int ld1, uint16_t* out2, int ld2, hipStream_t s);
 hipError_t launch_merge(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev);
 void accept_plan(int NB, int64_t V, int& nch, int& cpw, int& ngrp);
+// MI355X last-level (Infinity) cache: a call that reads at least this many
+// bytes once streams them with the non-temporal bit.
+constexpr int64_t kLastLevelCache = int64_t{256} << 20;
 size_t accept_workspace_bytes(int NB, int B, int64_t V);
 int accept_prefix_checks(const float* p_target, const float* q_draft, const int32_t* draft_tok, const int32_t* tau,
                          int32_t batch, int32_t B, int32_t gamma, int64_t vocab, const int32_t* n_accepted,
