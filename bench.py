@@ -136,6 +136,72 @@ def stream_probe_measure(torch, sd, t, dev, stream, kv_bytes, n=30, warmup=5):
     return rec
 
 
+def mfma_probe_measure(torch, sd, dev, stream, iters=2048, n=5):
+    """The bf16 matrix cores alone (simsd_mfma_probe: independent 32x32x16
+    MFMAs on registers, kernel-bound events) at 1, 2 and 4 waves per SIMD:
+    the compute-side ceiling the MFMA kernels are compared with."""
+    res = {"what": "independent v_mfma_f32_32x32x16_bf16 on registers, no memory traffic in the loop",
+           "iters": iters, "peak_tflops_published": MFMA_BF16_PEAK_TFLOPS}
+    best = 0.0
+    for waves_per_simd in (1, 2, 4):
+        wgs = 256 * waves_per_simd
+        sink = torch.zeros(wgs * sd.api.MFMA_PROBE_THREADS, dtype=torch.float32, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            b.record(stream)
+        sd.mfma_probe(wgs, 16, sink, stream=stream)
+        for a, b in evs:
+            sd.mfma_probe(wgs, iters, sink, a, b, stream=stream)
+        torch.cuda.synchronize()
+        us = min(a.elapsed_time(b) * 1e3 for a, b in evs)
+        flops = wgs * 4 * iters * sd.api.MFMA_PROBE_FLOPS_PER_ROUND
+        tflops = flops / (us * 1e-6) / 1e12
+        best = max(best, tflops)
+        res[f"waves_per_simd_{waves_per_simd}"] = {"us_min": us, "tflops": tflops}
+    res["tflops_best"] = best
+    res["frac_of_published_peak"] = best / MFMA_BF16_PEAK_TFLOPS
+    return res
+
+
+def ablation_measure(torch, sd, w, sets, dev, stream, n=20):
+    """The no-RoPE-copy ablation on the bench workload: the same verify call
+    with the mask slots at their own sequential positions (rope_mode =
+    SIMSD_ROPE_SEQUENTIAL) against the RoPE copy, kernel-bound events,
+    calls interleaved over both input sets."""
+    calls = {}
+    for mode_name, mode in (("rope_copy", sd.ROPE_COPY), ("rope_sequential", sd.ROPE_SEQUENTIAL)):
+        per_set = []
+        for s in sets:
+            t = s["t"]
+            out = torch.empty_like(t["q_blk"])
+            desc = sd.make_desc(t["q_blk"], t["k_blk"], t["k_cache"], rope_base=w.rope_base, rope_mode=mode)
+            ws = torch.empty(max(sd.verify_workspace_bytes(desc), 256), dtype=torch.uint8, device=dev)
+            per_set.append(sd.bind_verify(t["q_blk"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], t["tau"],
+                                          t["prompt_len"], None, out=out, workspace=ws, stream=stream,
+                                          rope_base=w.rope_base, rope_mode=mode))
+        calls[mode_name] = per_set
+    evs = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+           for k in calls}
+    for k in evs:
+        for a, b in evs[k]:
+            a.record(stream)
+            b.record(stream)
+    for i in range(4):
+        for k in calls:
+            calls[k][i % 2]()
+    for i in range(n):
+        for k in calls:
+            a, b = evs[k][i]
+            calls[k][i % 2].timed(a, b)
+    torch.cuda.synchronize()
+    res = {"what": "verify call with the mask slots at sequential positions (no RoPE copy) against the RoPE copy"}
+    for k in calls:
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs[k])
+        res[k] = {"us": {"mean": sum(us) / len(us), "median": us[len(us) // 2]}}
+    return res
+
+
 def copy_calibration(torch, dev, mib, steps, warmup):
     """A plain copy of known size: each launch reads and writes mib MiB once."""
     n = (mib << 20) // 4
@@ -244,19 +310,8 @@ def projection_measure(torch, sd, synth, dev, stream, steps, warmup):
     M, H, Hq, Hkv, d = 512, 4096, 32, 8, 128
     nsets = 8
     res = {}
-    for name, N, K in (("qkv_proj", (Hq + 2 * Hkv) * d, H), ("o_proj", H, Hq * d)):
-        calls = []
-        for i in range(nsets):
-            x, w = synth.make_linear_inputs(M, K, N, seed=4000 + 10 * i + (name == "o_proj"), device=dev)
-            if name == "qkv_proj":
-                q = torch.empty((32, 16, Hq, d), dtype=torch.bfloat16, device=dev)
-                k = torch.empty((32, 16, Hkv, d), dtype=torch.bfloat16, device=dev)
-                v = torch.empty_like(k)
-                calls.append(sd.bind_qkv_proj(x.view(32, 16, H), w, Hq, Hkv, d, q, k, v, stream=stream))
-            else:
-                out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-                calls.append(sd.bind_linear(x, w, out, stream=stream))
-        torch.cuda.synchronize()
+
+    def timed(calls):
         for i in range(max(warmup, nsets)):
             calls[i % nsets]()
         per_call = []
@@ -269,12 +324,35 @@ def projection_measure(torch, sd, synth, dev, stream, steps, warmup):
             e1.synchronize()
             per_call.append(e0.elapsed_time(e1) / nsets)
         per_call.sort()
-        us = sum(per_call) / len(per_call) * 1e3
+        return sum(per_call) / len(per_call) * 1e3, per_call[len(per_call) // 2] * 1e3
+
+    for name, N, K in (("qkv_proj", (Hq + 2 * Hkv) * d, H), ("o_proj", H, Hq * d)):
+        calls = []
+        lib_calls = []  # the vendor GEMM (hipBLASLt through torch.mm) on the same operands, for reference
+        for i in range(nsets):
+            x, w = synth.make_linear_inputs(M, K, N, seed=4000 + 10 * i + (name == "o_proj"), device=dev)
+            y_ref = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            lib_calls.append(lambda x=x, w=w, y=y_ref: torch.mm(x, w.t(), out=y))
+            if name == "qkv_proj":
+                q = torch.empty((32, 16, Hq, d), dtype=torch.bfloat16, device=dev)
+                k = torch.empty((32, 16, Hkv, d), dtype=torch.bfloat16, device=dev)
+                v = torch.empty_like(k)
+                calls.append(sd.bind_qkv_proj(x.view(32, 16, H), w, Hq, Hkv, d, q, k, v, stream=stream))
+            else:
+                out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                calls.append(sd.bind_linear(x, w, out, stream=stream))
+        torch.cuda.synchronize()
+        us, med = timed(calls)
+        lib_us, lib_med = timed(lib_calls)
         flops = 2.0 * M * N * K
         tflops = flops / (us * 1e-6) / 1e12
-        res[name] = {"M": M, "N": N, "K": K, "us": {"mean": us, "median": per_call[len(per_call) // 2] * 1e3},
+        res[name] = {"M": M, "N": N, "K": K, "us": {"mean": us, "median": med},
                      "tflops": tflops, "frac_mfma_bf16": tflops / MFMA_BF16_PEAK_TFLOPS,
-                     "weight_gbs": N * K * 2 / (us * 1e-6) / 1e9}
+                     "weight_gbs": N * K * 2 / (us * 1e-6) / 1e9,
+                     "library_reference": {"what": "torch.mm (hipBLASLt), y = x W^T on the same operands, "
+                                                   "same timing; context only, not on the path",
+                                           "us": {"mean": lib_us, "median": lib_med},
+                                           "tflops": flops / (lib_us * 1e-6) / 1e12}}
     return res
 
 
@@ -465,6 +543,8 @@ def main():
     coupled = coupled_measure(torch, sd, synth, dev, stream, args.steps, args.warmup)
     projections = projection_measure(torch, sd, synth, dev, stream, args.steps, args.warmup)
     commit_times = commit_measure(torch, sd, w, sets, dev, stream, args.steps)
+    mfma_ceiling = mfma_probe_measure(torch, sd, dev, stream)
+    ablation = ablation_measure(torch, sd, w, sets, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -505,6 +585,8 @@ def main():
         "accept_coupled": coupled,
         "projections": projections,
         "commit_step": commit_times,
+        "mfma_probe": mfma_ceiling,
+        "ablation_no_rope_copy": ablation,
     }
     print(json.dumps(rec), flush=True)
 

@@ -16,7 +16,7 @@ from .api import (  # noqa: F401
     accept_coupled, accept_coupled_workspace_bytes, accept_prefix, accept_prefix_noalloc, accept_workspace_bytes, append_kv, bind_accept,
     bind_append_kv, bind_commit, bind_next_round, next_round,
     bind_accept_coupled, bind_linear, bind_qkv_proj, bind_verify, commit, debug_mask, debug_rope, linear, make_desc,
-    qkv_proj, read_probe, stream_probe, verify_attn,
+    mfma_probe, qkv_proj, read_probe, stream_probe, verify_attn,
     verify_plan,
     verify_workspace_bytes,
 )

@@ -91,6 +91,7 @@ SIGNATURES = {
     "simsd_stream_probe": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
                                      c_void_p, c_void_p]),
     "simsd_read_probe": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "simsd_mfma_probe": (c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "simsd_strerror": (ctypes.c_char_p, [c_int32]),
     "simsd_abi_version": (c_int32, []),
     "simsd_commit": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,

@@ -551,6 +551,23 @@ def read_probe(k_cache, v_cache, sink, start=None, stop=None, stream=None):
                                       _stream_handle(stream), *ev), "simsd_read_probe")
 
 
+MFMA_PROBE_THREADS = 256
+MFMA_PROBE_FLOPS_PER_ROUND = 4 * 2 * 32 * 32 * 16  # per wave: four 32x32x16 MFMAs
+
+
+def mfma_probe(workgroups, iters, sink, start=None, stop=None, stream=None):
+    """The bf16 matrix cores alone: `workgroups` x 4 waves of independent
+    32x32x16 MFMAs on registers for `iters` rounds (MFMA_PROBE_FLOPS_PER_ROUND
+    flops per wave and round).  `sink`: float32, at least workgroups * 256.
+    Events as for stream_probe."""
+    _need(sink, "sink", torch.float32)
+    if sink.numel() < int(workgroups) * MFMA_PROBE_THREADS:
+        raise ValueError("sink needs workgroups * 256 floats")
+    ev = [ctypes.c_void_p(0 if e is None else e.cuda_event) for e in (start, stop)]
+    L.check(L.load().simsd_mfma_probe(int(workgroups), int(iters), _ptr(sink), _stream_handle(stream), *ev),
+            "simsd_mfma_probe")
+
+
 def debug_mask(tau, mask_mode=L.MASK_TEMPORAL, stream=None):
     """Block visibility words [NB][2B][2] (int64 view of the uint64 bits)."""
     lib = L.load()

@@ -213,7 +213,7 @@ int linear_checks(const void* x, const void* w, int64_t M, int64_t N, int64_t K)
 
 extern "C" {
 
-int simsd_abi_version(void) { return 7; }
+int simsd_abi_version(void) { return 8; }
 
 const char* simsd_strerror(int code) {
   switch (code) {

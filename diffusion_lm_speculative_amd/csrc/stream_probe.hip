@@ -136,8 +136,49 @@ __global__ __launch_bounds__(kReadThreads) void read_probe_kernel(const uint4* _
   if (acc == 0x5eed5eedu && threadIdx.x == 0) sink[0] = acc;  // keeps the reads; not expected to happen
 }
 
+// Measurement kernel: the sustained rate of the bf16 matrix cores.  Every
+// wave runs `iters` rounds of four independent 32x32x16 bf16 MFMAs on
+// register operands (no memory traffic in the loop), then each lane stores
+// one float of its accumulators.  4 waves per workgroup, one per SIMD.
+constexpr int kMfmaProbeThreads = 256;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(kMfmaProbeThreads) void mfma_probe_kernel(int iters, float* __restrict__ sink) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(1e-3f * static_cast<float>((threadIdx.x + i) & 15));
+    b[i] = static_cast<__bf16>(1e-3f * static_cast<float>(i + 1));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  const f32x16 c = c0 + c1 + c2 + c3;
+  float t = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) t += c[e];
+  sink[static_cast<size_t>(blockIdx.x) * kMfmaProbeThreads + threadIdx.x] = t;
+}
+
 }  // namespace
 }  // namespace simsd
+
+extern "C" int simsd_mfma_probe(int32_t workgroups, int32_t iters, float* sink, void* stream, void* start_event,
+                                void* stop_event) {
+  using namespace simsd;
+  if (workgroups < 1 || workgroups > 65536 || iters < 1) return SIMSD_ERR_SHAPE;
+  if (!sink) return SIMSD_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(sink) % 4) return SIMSD_ERR_ALIGN;
+  const hipError_t e = launch_with_events(mfma_probe_kernel, dim3(static_cast<unsigned>(workgroups)),
+                                          dim3(kMfmaProbeThreads), 0, static_cast<hipStream_t>(stream),
+                                          static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event),
+                                          static_cast<int>(iters), sink);
+  return e == hipSuccess ? SIMSD_OK : SIMSD_ERR_HIP;
+}
 
 extern "C" int simsd_read_probe(const void* k, const void* v, int64_t bytes, void* sink, void* stream,
                                 void* start_event, void* stop_event) {

@@ -440,10 +440,22 @@ int simsd_stream_probe(const void* k, const void* v, int32_t streams_x, int32_t 
 int simsd_read_probe(const void* k, const void* v, int64_t bytes, void* sink, void* stream, void* start_event,
                      void* stop_event);
 
+/* Measurement only: the sustained rate of the bf16 matrix cores, the
+ * compute-side ceiling the MFMA kernels are compared with.  Launches
+ * `workgroups` (1..65536) workgroups of 4 waves; every wave runs `iters`
+ * (>= 1) rounds of four independent v_mfma_f32_32x32x16_bf16 on register
+ * operands, 4 * 32768 flops a round, with no memory traffic in the loop, and
+ * each of its lanes then writes one float to sink[workgroup * 256 + lane of
+ * the workgroup] (`sink`: workgroups * 256 floats, device, 4-byte aligned).
+ * Events as for simsd_stream_probe.  Errors: SIMSD_ERR_SHAPE, _NULL, _ALIGN,
+ * _HIP. */
+int simsd_mfma_probe(int32_t workgroups, int32_t iters, float* sink, void* stream, void* start_event,
+                     void* stop_event);
+
 /* Human-readable text for a return code (static storage). */
 const char* simsd_strerror(int code);
 
-/* ABI version of this header: 7. */
+/* ABI version of this header: 8. */
 int simsd_abi_version(void);
 
 #ifdef __cplusplus

@@ -39,7 +39,7 @@ def _declared():
 def test_header_declarations_match_binding():
     decl = _declared()
     assert decl == set(L.SIGNATURES), decl ^ set(L.SIGNATURES)
-    assert len(decl) == 20
+    assert len(decl) == 21
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.simsd_abi_version() == 7
+    assert lib.simsd_abi_version() == 8
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert lib.simsd_strerror(code)
     assert lib.simsd_strerror(-99) == b"unknown error code"
@@ -269,6 +269,15 @@ def test_stream_probe_rejects_on_host(lib):
     for name in ("k", "v", "sink"):
         assert call(**{name: None}) == L.ERR_NULL, name
     assert call(k=A + 8) == L.ERR_ALIGN and call(sink=A + 2) == L.ERR_ALIGN
+
+
+@no_gpu_only
+def test_mfma_probe_rejects_on_host(lib):
+    def call(wgs=256, iters=16, sink=A):
+        return lib.simsd_mfma_probe(wgs, iters, sink, None, None, None)
+    assert call(wgs=0) == L.ERR_SHAPE and call(wgs=65537) == L.ERR_SHAPE and call(iters=0) == L.ERR_SHAPE
+    assert call(sink=None) == L.ERR_NULL
+    assert call(sink=A + 2) == L.ERR_ALIGN
 
 
 @no_gpu_only
