@@ -102,8 +102,8 @@ typedef enum { SIMSD_IMPL_AUTO = 0, SIMSD_IMPL_VALU = 1, SIMSD_IMPL_MFMA = 2 } s
  * consecutive indices in layout order: D~_k at pos(D_k) + B (by default
  * D_k at P_b + k and D~_k at P_b + B + k).  The MFMA kernel keeps a RoPE
  * table of one entry per distinct block position in LDS; at head_dim 128
- * and B > 32 the SEQUENTIAL table does not fit beside a 3-stage ring, and
- * AUTO then runs the VALU kernel (an explicit MFMA request is
+ * and B = 63 or 64 the SEQUENTIAL table does not fit beside a 3-stage ring,
+ * and AUTO then runs the VALU kernel (an explicit MFMA request is
  * SIMSD_ERR_SHAPE). */
 typedef enum { SIMSD_ROPE_COPY = 0, SIMSD_ROPE_SEQUENTIAL = 1 } simsd_rope_mode;
 

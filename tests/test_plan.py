@@ -139,3 +139,16 @@ def test_plan_rejects_like_the_call():
     assert L.load().simsd_verify_plan_info(ctypes.byref(bad), ctypes.byref(p)) == L.ERR_SHAPE
     assert p.impl == 77  # left unchanged
     assert L.load().simsd_verify_plan_info(None, ctypes.byref(p)) == L.ERR_NULL
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_sequential_positions_run_on_the_matrix_cores_up_to_b62_at_head_dim_128(G):
+    # Without the RoPE copy the table holds 2B positions (2B x 64 pairs x 8 bytes at head dim
+    # 128).  Beside a 3-stage ring of 32 KiB tiles and the 512 bytes of labels it fits up to
+    # B = 62; B = 63 and 64 go to the VALU kernel under AUTO.
+    for B in range(1, 65):
+        p = sd.verify_plan(_desc(4, 8 * G, 8, 128, B, 4096, rope_mode=L.ROPE_SEQUENTIAL))
+        table = 2 * B * 64 * 8
+        fits = 3 * 32768 + 512 + table + LDS_RESERVE <= LDS_PER_CU
+        assert fits == (B <= 62), B
+        assert p["impl"] == (L.IMPL_MFMA if fits else L.IMPL_VALU), (B, p)
