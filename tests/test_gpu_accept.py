@@ -157,6 +157,14 @@ def test_without_stages_next_token_is_minus_one_and_no_workspace_is_needed():
         assert st.cpu().tolist() == [0] * NB
 
 
+def test_largest_batch():
+    # batch 65535 (the largest the acceptance takes: one grid row per
+    # sequence), every sequence checked against the oracle
+    inp = synth.make_accept_inputs(65535, 2, 40, seed=2024)
+    n, _ = _check(inp, 2, 19, 4)
+    assert (n == 0).any() and (n == 2).any()
+
+
 def test_empty_residual_draws_from_target():
     # p = q / 2 (not normalised): a stage rejects when u >= 1/2, and the
     # residual max(0, p - q) is then zero everywhere, so the draw uses p.

@@ -85,6 +85,13 @@ def test_full_size_vocab():
     assert n.max() >= w.gamma // 2
 
 
+def test_large_batch():
+    # batch 65535 (as the standard acceptance's largest), every sequence checked
+    p, e, x, tau = _inputs(65535, 2, 40, 2, seed=2025)
+    n, _ = _check(p, e, x, tau, 2)
+    assert len(set(n.tolist())) == 3
+
+
 def test_ties_across_chunks_go_to_the_smaller_index():
     # equal ratios p/E from different (p, E) pairs, placed in different chunks
     NB, B, V = 4, 4, 4 * 8192 + 5

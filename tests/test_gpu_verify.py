@@ -308,6 +308,25 @@ def test_mfma_and_valu_agree_and_runs_are_deterministic():
     assert (a1.float() - v1.float()).abs().max().item() < 2e-2
 
 
+def test_largest_batch_the_grid_takes():
+    # The attention kernel's grid is (KV heads, batch x row groups, splits) and
+    # its y dimension stops at 65535: a batch of 65535 with one row group per
+    # KV head (2 heads per KV head x 2B = 8 rows), ragged prompts including 0,
+    # checked on sampled sequences at both ends and in the middle.  Both
+    # kernels; the next larger batch is refused on the host.
+    w = _w(NB=65535, Hq=2, Hkv=1, d=64, P=128, p_lo=0, B=4)
+    t = gpu_inputs(w, 131, on_device=True)
+    b_idx = [0, 1, 2, 32767, 65532, 65533, 65534]
+    for impl in (sd.IMPL_MFMA, sd.IMPL_VALU):
+        _check(t, w, f"batch 65535 impl={impl}", impl=impl, b_idx=b_idx)
+    big = dataclasses.replace(w, NB=65536)
+    desc = sd.make_desc(torch.empty((65536, 8, 2, 64), dtype=torch.bfloat16),
+                        torch.empty((65536, 8, 1, 64), dtype=torch.bfloat16),
+                        torch.empty((65536, 1, 128, 64), dtype=torch.bfloat16), rope_base=big.rope_base)
+    with pytest.raises(sd.SimsdError):
+        sd.verify_workspace_bytes(desc)
+
+
 def test_empty_inputs_are_noops():
     w = _w(NB=2, P=64, B=0)
     t = gpu_inputs(w, 81)
