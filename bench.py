@@ -202,6 +202,64 @@ def ablation_measure(torch, sd, w, sets, dev, stream, n=20):
     return res
 
 
+def c5_measure(torch, sd, synth, dev, stream, steps=20, warmup=3):
+    """The verification-plus-acceptance workload at batch 64 (32/8 heads,
+    head dim 128, prompts uniform in [2048, 16384], B = gamma = 16,
+    accept_prefix over [64][16][151936]): one step is a verify call and an
+    accept_prefix call with its residual draw, two input sets alternating.
+    Kernel-bound events on the verify call (attention kernel start to merge
+    end), an event after the acceptance."""
+    w = synth.WORKLOADS["sdar8b_var16k_b16_accept"]
+    gamma = w.gamma
+    sets = []
+    for i in range(2):
+        t = synth.make_verify_inputs(w, 5005 + 100 * i, device=dev)
+        a = synth.make_accept_inputs(w.NB, w.B, w.vocab, seed=6006 + 100 * i, device=dev)
+        out = torch.empty_like(t["q_blk"])
+        desc = sd.make_desc(t["q_blk"], t["k_blk"], t["k_cache"], rope_base=w.rope_base)
+        ws = torch.empty(max(sd.verify_workspace_bytes(desc), 256), dtype=torch.uint8, device=dev)
+        st = torch.empty((w.NB,), dtype=torch.int32, device=dev)
+        call = sd.bind_verify(t["q_blk"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], t["tau"],
+                              t["prompt_len"], None, out=out, status=st, workspace=ws, stream=stream,
+                              rope_base=w.rope_base)
+        n_acc = torch.empty((w.NB,), dtype=torch.int32, device=dev)
+        nxt = torch.empty_like(n_acc)
+        ast = torch.empty_like(n_acc)
+        aws = torch.empty(max(sd.accept_workspace_bytes(w.NB, w.B, w.vocab), 256), dtype=torch.uint8, device=dev)
+        acc = sd.bind_accept(a["p"], a["q"], a["draft_tok"], a["tau"], gamma, n_accepted=n_acc, next_token=nxt,
+                             status=ast, workspace=aws, stream=stream)
+        sets.append(dict(t=t, call=call, acc=acc, st=st, ast=ast, kv=w.kv_bytes(t["prompt_len"])))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        e[1].record(stream)
+    for i in range(warmup):
+        sets[i % 2]["call"]()
+        sets[i % 2]["acc"](4321, i)
+    torch.cuda.synchronize()
+    for k, s_ in enumerate(sets):
+        if int(s_["st"].abs().sum()) or int(s_["ast"].abs().sum()):
+            raise RuntimeError(f"batch-64 input set {k}: device status flags set")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        s_ = sets[i % 2]
+        s_["call"].timed(evs[i][0], evs[i][1])
+        s_["acc"](4321, i)
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    v_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+    a_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+    kv = [sets[i % 2]["kv"] / (v_us[i] * 1e-6) / 1e9 for i in range(steps)]
+    us_step = wall * 1e6 / steps
+    return {"workload": w.name, "batch": w.NB, "B": w.B, "gamma": gamma, "vocab": w.vocab,
+            "us_per_step": us_step, "candidates_per_s": w.NB * gamma / (us_step * 1e-6),
+            "verify_us": {"mean": sum(v_us) / steps, "median": sorted(v_us)[steps // 2]},
+            "accept_us": {"mean": sum(a_us) / steps, "median": sorted(a_us)[steps // 2]},
+            "kv_gbs_mean": sum(kv) / steps, "kv_frac": sum(kv) / steps / HBM_PEAK_GBS,
+            "kv_bytes_sets": [s_["kv"] for s_ in sets]}
+
+
 def copy_calibration(torch, dev, mib, steps, warmup):
     """A plain copy of known size: each launch reads and writes mib MiB once."""
     n = (mib << 20) // 4
@@ -545,12 +603,13 @@ def main():
     commit_times = commit_measure(torch, sd, w, sets, dev, stream, args.steps)
     mfma_ceiling = mfma_probe_measure(torch, sd, dev, stream)
     ablation = ablation_measure(torch, sd, w, sets, dev, stream)
+    nb = w.NB
+    t_host = {k: v[:nb].cpu() for k, v in sets[0]["t"].items()}
+    a_host = {k: v[:nb].cpu() for k, v in sets[0]["a"].items()}
+    c5 = c5_measure(torch, sd, synth, dev, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
-        nb = w.NB
-        t_host = {k: v[:nb].cpu() for k, v in sets[0]["t"].items()}
-        a_host = {k: v[:nb].cpu() for k, v in sets[0]["a"].items()}
         cpu = cpu_baseline(t_host, a_host, w)
 
     rec = {
@@ -586,6 +645,7 @@ def main():
         "projections": projections,
         "commit_step": commit_times,
         "mfma_probe": mfma_ceiling,
+        "verify_accept_batch64": c5,
         "ablation_no_rope_copy": ablation,
     }
     print(json.dumps(rec), flush=True)
