@@ -68,7 +68,7 @@ class VerifyDesc(ctypes.Structure):
 
 class VerifyPlan(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in ("impl", "threads", "rows_wg", "row_groups", "ksplit", "row_tiles", "nstage",
-                                       "qsep", "blk_rows", "nsplit", "chunk", "lds_bytes", "kv_stream")]
+                                       "qsep", "blk_rows", "nsplit", "chunk", "lds_bytes", "kv_stream", "lpt")]
 
 
 # name -> (restype, argtypes); every function declared in include/simsd.h.

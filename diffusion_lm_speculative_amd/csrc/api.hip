@@ -14,6 +14,7 @@ constexpr size_t kLdsPerCu = 163840;  // bytes of LDS per CU (and per workgroup 
 constexpr int kMaxChunk = 8192;     // default split length cap (tail of ragged prompts)
 constexpr int kMinSplitTiles = 16;  // default splits of fewer tiles cost more in the merge than they save
 constexpr int kMaxQHeads = 65536;   // query heads per layer accepted by the planner
+constexpr int kLptMaxItems = 256;   // (sequence, split) items per KV head ranked longest first
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -151,6 +152,20 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   pl.nsplit = static_cast<int>(nsplit);
   const int64_t grid = nsplit * pl.nrg * static_cast<int64_t>(pl.NB) * pl.Hkv;
   if (grid > 0x7fffffffLL) return SIMSD_ERR_SHAPE;
+  // Longest work first when the grid takes more than one round of
+  // workgroups: with ragged prompts the (sequence, split) items differ in
+  // length, and in dispatch order long ones would start late (batch 64,
+  // prompts 2048..16384, two splits: 1024 workgroups over 256 CUs took 487.5
+  // us from the first start to the last end, tiles per CU 151..378 against
+  // 280 on average).  Each workgroup ranks the items of its KV head itself,
+  // so the ranking stays cheap only for a modest count of them.
+  pl.lpt = 0;
+  if (pl.impl == SIMSD_IMPL_MFMA) {
+    const size_t per_wg = mfma_lds_bytes(pl.d, pl.nstage, pl.tab_rows, pl.rows_wg, pl.qsep != 0, pl.blk_rows) + 1024;
+    const int64_t slots = kNumCUs * static_cast<int64_t>(kLdsPerCu / per_wg);
+    const int64_t items = static_cast<int64_t>(pl.NB) * nsplit;
+    if (grid > slots && items <= kLptMaxItems) pl.lpt = 1;
+  }
   // the MFMA kernel's grid is (Hkv, NB * nrg, nsplit): y and z stay below 2^16
   if (pl.impl == SIMSD_IMPL_MFMA && (pl.nsplit > 65535 || static_cast<int64_t>(pl.NB) * pl.nrg > 65535))
     return SIMSD_ERR_SHAPE;
@@ -213,7 +228,7 @@ int linear_checks(const void* x, const void* w, int64_t M, int64_t N, int64_t K)
 
 extern "C" {
 
-int simsd_abi_version(void) { return 8; }
+int simsd_abi_version(void) { return 9; }
 
 const char* simsd_strerror(int code) {
   switch (code) {
@@ -259,6 +274,7 @@ int simsd_verify_plan_info(const simsd_verify_desc* desc, simsd_verify_plan* pla
   o.nsplit = pl.nsplit;
   o.chunk = pl.chunk;
   o.kv_stream = mfma ? pl.kv_stream : 0;
+  o.lpt = mfma ? pl.lpt : 0;
   o.lds_bytes =
       mfma ? static_cast<int32_t>(mfma_lds_bytes(pl.d, pl.nstage, pl.tab_rows, pl.rows_wg, pl.qsep != 0, pl.blk_rows))
            : 0;

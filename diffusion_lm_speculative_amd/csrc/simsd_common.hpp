@@ -172,6 +172,7 @@ struct Plan {
   int qsep;                           // MFMA: query rows staged in their own LDS region
   int blk_rows;                       // MFMA: block K/V rows in their own LDS region (0: through the ring)
   int kv_stream;                      // MFMA: K/V tiles loaded non-temporally (the call streams >= the last-level cache)
+  int lpt;                            // MFMA: workgroups take their items longest first
   int rope_seq;                       // D~_k at pos(D_k) + B instead of pos(D_k)
   int tab_rows;                       // distinct block positions: B, or 2B with rope_seq
   float scale_log2;                   // softmax scale * log2(e)

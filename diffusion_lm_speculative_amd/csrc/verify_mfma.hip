@@ -195,10 +195,43 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   // the splits go out in order, so the ragged last splits come last.
   const int kvh = blockIdx.x;
   int b = blockIdx.y, rg = 0;
-  const int s = blockIdx.z;
+  int s = blockIdx.z;
   if (pl.nrg > 1) {
     rg = b % pl.nrg;
     b /= pl.nrg;
+  }
+  // Longest work first (pl.lpt: more workgroups than the CUs hold at once).
+  // The workgroups of one KV head go out in (split, sequence) order; each
+  // takes the (sequence, split) item whose rank by key count (longest first,
+  // ties in dispatch order) is its own position in that order, so the long
+  // items start first and the short ones fill in behind them.  Every
+  // workgroup computes the same ranking from the prompt lengths, in the LDS
+  // of the tile ring before any tile is issued.  The row groups of an item
+  // keep their adjacent positions.
+  if (pl.lpt) {
+    const int items = pl.NB * pl.nsplit;
+    int* lk = reinterpret_cast<int*>(smem);  // keys of each item, then the pick
+    for (int t = tid; t < items; t += NT) {
+      const int bt = t % pl.NB, st = t / pl.NB;
+      const int plen_t = a.prompt_len ? a.prompt_len[bt] : pl.p_max;
+      lk[t] = min(max(plen_t - st * pl.chunk, 0), pl.chunk);
+    }
+    __syncthreads();
+    const int mine = s * pl.NB + b;
+    for (int t = tid; t < items; t += NT) {
+      const int kt = lk[t];
+      int r = 0;
+      for (int u = 0; u < items; ++u) {
+        const int ku = lk[u];
+        r += (ku > kt || (ku == kt && u < t)) ? 1 : 0;
+      }
+      if (r == mine) lk[items] = t;
+    }
+    __syncthreads();
+    const int item = lk[items];
+    __syncthreads();  // every wave holds its item before the ring is filled
+    b = item % pl.NB;
+    s = item / pl.NB;
   }
 
   const int B = pl.B, twoB = pl.twoB;

@@ -149,6 +149,11 @@ typedef struct {
   int32_t kv_stream;  /* MFMA: 1 = the prompt K/V tiles are loaded non-temporal,
                          chosen when NB * Hkv * p_max * d * 2 * 2 bytes (K and V
                          in bf16) reach 256 MiB, the last-level cache (else 0) */
+  int32_t lpt;        /* MFMA: 1 = the workgroups of a KV head take their
+                         (sequence, split) items longest first by prompt
+                         length, chosen when the grid needs more than one
+                         round of workgroups and a KV head has at most 256
+                         items (else 0) */
 } simsd_verify_plan;
 
 int simsd_verify_plan_info(const simsd_verify_desc* desc, simsd_verify_plan* plan);
@@ -455,7 +460,7 @@ int simsd_mfma_probe(int32_t workgroups, int32_t iters, float* sink, void* strea
 /* Human-readable text for a return code (static storage). */
 const char* simsd_strerror(int code);
 
-/* ABI version of this header: 8. */
+/* ABI version of this header: 9. */
 int simsd_abi_version(void);
 
 #ifdef __cplusplus

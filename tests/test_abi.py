@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.simsd_abi_version() == 8
+    assert lib.simsd_abi_version() == 9
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert lib.simsd_strerror(code)
     assert lib.simsd_strerror(-99) == b"unknown error code"

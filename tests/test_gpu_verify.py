@@ -308,6 +308,21 @@ def test_mfma_and_valu_agree_and_runs_are_deterministic():
     assert (a1.float() - v1.float()).abs().max().item() < 2e-2
 
 
+@pytest.mark.parametrize("label,ov", [("rows128", dict(NB=64, Hq=8, Hkv=2, B=16)),
+                                      ("rows64", dict(NB=64, Hq=8, Hkv=2, B=8)),
+                                      ("two_row_groups", dict(NB=32, Hq=16, Hkv=2, B=16))])
+def test_longest_first_item_order(label, ov):
+    # Ragged prompts (0..2048, ties and empty splits included) in four splits of
+    # 512 keys, more workgroups than the CUs hold at once: each workgroup takes
+    # the (sequence, split) item of its rank by length, longest first.  Every
+    # sequence is checked.
+    w = _w(d=128, P=2048, p_lo=0, **ov)
+    t = gpu_inputs(w, 141 + w.B + w.Hq)
+    plan = sd.verify_plan(sd.make_desc(t["q_blk"], t["k_blk"], t["k_cache"], rope_base=w.rope_base, kv_chunk=512))
+    assert plan["lpt"] == 1 and plan["nsplit"] == 4, plan
+    _check(t, w, f"longest first {label}", kv_chunk=512)
+
+
 def test_largest_batch_the_grid_takes():
     # The attention kernel's grid is (KV heads, batch x row groups, splits) and
     # its y dimension stops at 65535: a batch of 65535 with one row group per

@@ -152,3 +152,14 @@ def test_sequential_positions_run_on_the_matrix_cores_up_to_b62_at_head_dim_128(
         fits = 3 * 32768 + 512 + table + LDS_RESERVE <= LDS_PER_CU
         assert fits == (B <= 62), B
         assert p["impl"] == (L.IMPL_MFMA if fits else L.IMPL_VALU), (B, p)
+
+
+def test_longest_first_only_where_the_grid_takes_several_rounds():
+    # the batch-64 ragged workload (1024 workgroups over 256 CUs) ranks its
+    # items; the one-round workloads keep the plain dispatch order
+    lpt = {name: _plan_of(w)["lpt"] for name, w in synth.WORKLOADS.items()}
+    assert lpt == {"tiny_fp32": 0, "sdar8b_p1024_b4": 0, "sdar8b_p4096_b8": 0, "sdar8b_p8192_b32": 0,
+                   "sdar8b_var16k_b16_accept": 1}, lpt
+    # more than 256 items per KV head: not ranked
+    p = sd.verify_plan(_desc(300, 32, 8, 128, 16, 16384, kv_chunk=8192))
+    assert p["nsplit"] == 2 and p["lpt"] == 0
