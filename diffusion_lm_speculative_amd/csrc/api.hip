@@ -66,16 +66,28 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
   }
 
   if (pl.impl == SIMSD_IMPL_MFMA) {
-    // 16-row tiles per workgroup: 1, 2 or 4 (one per row wave), or 8 (four
-    // row waves of two tiles each); each tile's keys are split over 4 or 2
-    // waves, so a workgroup runs 4 to 8 waves.  More rows take more row
-    // groups, which read the same K/V split on one XCD at about the same time.
+    // 16-row tiles per workgroup: 1, 2 or 4 (one per row wave), 8 (four row
+    // waves of two tiles each, each tile's keys split over two waves) or, at
+    // head dim 128, 16 (eight row waves of two tiles, each over all keys of
+    // a tile); a workgroup runs 4 to 8 waves.  More rows take more row
+    // groups, which read the same K/V split on one XCD at about the same
+    // time.  Two groups of 128 rows pull every tile into two CUs' LDS, one
+    // group of 256 into one (the grid then takes twice the splits): batch 8 x
+    // 8192 keys, B = 32, 115-118 against 121-125 us per call.
     const int tiles = (pl.M + 15) / 16;
+    const int max16 = pl.d == 128 ? 16 : 8;
     int nt16 = 1;
-    while (nt16 < tiles && nt16 < 8) nt16 *= 2;
-    const int rw = nt16 >= 8 ? 4 : nt16;
+    while (nt16 < tiles && nt16 < max16) nt16 *= 2;
+    // 256 rows only beside a 4-stage ring (their query rows borrow two
+    // stages in the prologue; with three the step's registers spill), and
+    // only where they pad no more rows than groups of 128 would: up to 256
+    // rows, or a multiple of 256.
+    if (nt16 == 16 && (mfma_lds_bytes(pl.d, 4, pl.tab_rows, 256, false, 0) + 1024 > kLdsPerCu ||
+                       (tiles > 16 && tiles % 16 != 0)))
+      nt16 = 8;
+    const int rw = nt16 >= 16 ? 8 : (nt16 >= 8 ? 4 : nt16);
     pl.rowt = nt16 >= 8 ? 2 : 1;
-    pl.ksplit = rw >= 4 ? 2 : 4;
+    pl.ksplit = nt16 >= 16 ? 1 : (rw >= 4 ? 2 : 4);
     pl.threads = rw * pl.ksplit * 64;
     pl.rows_wg = nt16 * 16;
     // Four ring stages with the query rows staged in their own LDS region
@@ -92,8 +104,9 @@ int make_plan(const simsd_verify_desc& d, Plan& pl) {
     // when it fits beside the ring without costing a workgroup per CU; the
     // ring then streams prompt tiles only, and the block keys are done while
     // the first of those are in flight.  Only beside a 4-stage ring: where
-    // three stages are all that fit, such a region does not fit either.
-    if (pl.nstage == 4 && pl.twoB > 0 && pl.twoB <= kKeyTile) {
+    // three stages are all that fit, such a region does not fit either.  Not
+    // for 256 rows, whose waves take the block keys through the ring.
+    if (pl.nstage == 4 && pl.twoB > 0 && pl.twoB <= kKeyTile && pl.rows_wg <= 128) {
       const int rows = (pl.twoB + 15) / 16 * 16;
       const size_t base = mfma_lds_bytes(pl.d, pl.nstage, pl.tab_rows, pl.rows_wg, pl.qsep != 0, 0) + 1024;
       const size_t with = mfma_lds_bytes(pl.d, pl.nstage, pl.tab_rows, pl.rows_wg, pl.qsep != 0, rows) + 1024;

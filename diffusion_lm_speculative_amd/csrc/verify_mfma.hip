@@ -134,10 +134,12 @@ struct Smem {
   // start of the block rows' region (the table follows it)
   static constexpr int blk(int rows_wg) { return QREG + (QSEP ? rows_wg * Layout<HD>::ROWB : 0); }
   // Byte offset of query row lr (0 <= lr < rows per workgroup) of the staging area.
+  // Without a region of their own the rows borrow ring stages from the last
+  // one down, 2*KT rows per stage: its K tile, then its V tile.
   static constexpr int qrow(int lr) {
     return QSEP ? QREG + lr * Layout<HD>::ROWB
-                : (lr < KT ? KREG : VREG - KT * Layout<HD>::ROWB) + (NSTAGE - 1) * Layout<HD>::TILEB +
-                      lr * Layout<HD>::ROWB;
+                : ((lr % (2 * KT)) < KT ? KREG : VREG - KT * Layout<HD>::ROWB) +
+                      (NSTAGE - 1 - lr / (2 * KT)) * Layout<HD>::TILEB + (lr % (2 * KT)) * Layout<HD>::ROWB;
   }
 };
 
@@ -157,7 +159,8 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   constexpr int KREG = S::KREG;
   constexpr int VREG = S::VREG;
   constexpr int BKREG = S::blk(ROWS);
-  constexpr int NPRO = QSEP ? NSTAGE : NSTAGE - 1;  // ring tiles issued before the query rows are read
+  constexpr int QST = (ROWS + 2 * KT - 1) / (2 * KT);  // ring stages the query rows borrow (without QSEP)
+  constexpr int NPRO = QSEP ? NSTAGE : NSTAGE - QST;  // ring tiles issued before the query rows are read
   constexpr int QI = ROWS / L::RPI;              // 1 KiB loads of the workgroup's query rows
   constexpr int XSTR = HD + 4;                   // floats per row of the key-split exchange buffer
   static_assert(KSPLIT == 1 || KSPLIT == 2 || KSPLIT == 4, "key split");
@@ -165,8 +168,9 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   static_assert(LPW * NW == 2 * L::IPT, "tile loads must split evenly over waves");
   static_assert(NSTAGE * LPW <= 63, "too many loads in flight for vmcnt");
   static_assert((NSTAGE - 1) * L::TILEB < 65536, "stage offsets must fit the LDS immediate");
-  static_assert(QSEP || ROWS <= 2 * KT, "query rows must fit the last stage");
+  static_assert(QSEP || QST < NSTAGE, "query rows must leave a ring stage to the prologue");
   static_assert(ROWT == 1 || ROWT == 2, "row tiles per wave");
+  static_assert(KSPLIT > 1 || (!BSEP && ROWT == 2 && NSUB == 4), "one key split: 32 rows a wave, block keys in the ring");
   static_assert((KSPLIT - 1) * ROWS * XSTR * 4 <= 2 * NSTAGE * L::TILEB, "exchange buffer fits the ring");
   static_assert(NT % HALF == 0, "each lane keeps one RoPE frequency");
   // Probabilities are taken relative to a per-row reference set at the
@@ -529,8 +533,10 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     return bt == 0 ? (dbits | (mbits << B)) : (mbits >> (64 - B));
   };
   if (!QSEP) {
-    lds_barrier<63>();  // every wave holds its query rows: the last stage is free
-    if (NSTAGE - 1 < T) issue(NSTAGE - 1, NSTAGE - 1, c1);
+    lds_barrier<63>();  // every wave holds its query rows: the stages they borrowed are free
+#pragma unroll
+    for (int t2 = NPRO; t2 < NSTAGE; ++t2)
+      if (t2 < T) issue(t2, t2, c1);
   }
 
   // ---- loop-invariant LDS offsets of this lane's operand reads
@@ -619,6 +625,38 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       }
   };
 
+  // One key split (all 64 keys of a tile per wave, 32 rows): the K operands
+  // of 16-key subtile i, and the V^T operands of 32-key half uu, of the tile
+  // in stage ST.  Read a subtile or a half at a time: the whole tile's
+  // operands at once would not fit beside the accumulators of 32 rows.
+  auto ksub = [&](auto stage_c, int st, int i, bf16x8 (&ko)[KSTEPS]) __attribute__((always_inline)) {
+    constexpr int SC = decltype(stage_c)::value;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if constexpr (SC >= 0)
+        ko[kk] = *reinterpret_cast<const bf16x8*>(smem + kofs[kk] + (SC * L::TILEB + i * 16 * L::ROWB));
+      else
+        ko[kk] = *reinterpret_cast<const bf16x8*>(smem + (kofs[kk] + st * L::TILEB) + i * 16 * L::ROWB);
+    }
+  };
+  auto vhalf = [&](auto stage_c, int st, int uu, bf16x8 (&vo)[DTILES]) __attribute__((always_inline)) {
+    constexpr int SC = decltype(stage_c)::value;
+    constexpr int SO = SC >= 0 ? SC * L::TILEB : 0;
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) {
+      const uint32_t va = SC >= 0 ? vadr[dt] : vadr[dt] + st * L::TILEB;
+      bf16x4 lo, hi;
+      if (uu == 0) {
+        lo = tr_read<SO>(va);
+        hi = tr_read<SO + 16 * L::ROWB>(va);
+      } else {
+        lo = tr_read<SO + 32 * L::ROWB>(va);
+        hi = tr_read<SO + 48 * L::ROWB>(va);
+      }
+      vo[dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+
   // Rotate block K rows row0 .. row0 + nvalid - 1, held from Kb on (K
   // swizzle), in place.
   auto rotate_rows = [&](unsigned char* Kb, int nvalid, int row0) __attribute__((always_inline)) {
@@ -645,13 +683,12 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     lds_barrier<63>();
   };
 
-  // Softmax of the scores and O^T += V^T P^T, for every row tile (each V^T
-  // operand feeds ROWT MFMAs).  MODE 0: every key visible; MODE 1: key k of
-  // the tile visible for row tile rt when bit k of cmask[rt] is set.
-  auto finish = [&](auto mode_c, const f32x4 (&sacc)[ROWT][NSUB], const bf16x8 (&vop)[DTILES][NU],
-                    const uint64_t (&cmask)[ROWT]) __attribute__((always_inline)) {
+  // Softmax of the scores into the P^T operands, for every row tile.  MODE 0:
+  // every key visible; MODE 1: key k of the tile visible for row tile rt when
+  // bit k of cmask[rt] is set.
+  auto softmax = [&](auto mode_c, const f32x4 (&sacc)[ROWT][NSUB], const uint64_t (&cmask)[ROWT],
+                     bf16x8 (&pop)[ROWT][NU]) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode_c)::value;
-    bf16x8 pop[ROWT][NU];
     // The probabilities are taken against the current reference right away,
     // alongside the maximum, for every row tile: the exponentials then do not
     // wait for the vote.  A row's first visible key sets its reference and a
@@ -730,6 +767,13 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
         pop[rt][uu] = bf16x8{pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
       }
     }
+  };
+  // Softmax and O^T += V^T P^T, for every row tile (each V^T operand feeds
+  // ROWT MFMAs).
+  auto finish = [&](auto mode_c, const f32x4 (&sacc)[ROWT][NSUB], const bf16x8 (&vop)[DTILES][NU],
+                    const uint64_t (&cmask)[ROWT]) __attribute__((always_inline)) {
+    bf16x8 pop[ROWT][NU];
+    softmax(mode_c, sacc, cmask, pop);
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt)
 #pragma unroll
@@ -808,6 +852,43 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
         lds_barrier<0>();
       if (t + NSTAGE - 1 < T) issue(K == 0 ? NSTAGE - 1 : K - 1, t + NSTAGE - 1, c1);
       if (t < nbt) rotate_block(K, t);
+    }
+    if constexpr (KSPLIT == 1) {
+      // scores subtile by subtile, the softmax, then P V half by half (the
+      // V reads of the first half go out under the softmax)
+#pragma unroll
+      for (int i = 0; i < NSUB; ++i) {
+        bf16x8 ko[KSTEPS];
+        ksub(stage_c, K, i, ko);
+        f32x4 sa[ROWT];
+#pragma unroll
+        for (int rt = 0; rt < ROWT; ++rt) sa[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+          for (int rt = 0; rt < ROWT; ++rt) sa[rt] = mfma(ko[kk], qop[rt][kk], sa[rt]);
+#pragma unroll
+        for (int rt = 0; rt < ROWT; ++rt) sb[rt][i] = sa[rt];
+      }
+      uint64_t cm[ROWT] = {};
+      if (decltype(mode_c)::value != 0) {
+        const int nk = c1 - (c0 + (t - nbt) * KT);  // keys of a prompt tile below c1
+        const uint64_t tail = nk >= KT ? ~0ull : (1ull << nk) - 1ull;
+#pragma unroll
+        for (int rt = 0; rt < ROWT; ++rt) cm[rt] = t < nbt ? block_vis(rt, t) : tail;
+      }
+      bf16x8 pop[ROWT][NU];
+      softmax(mode_c, sb, cm, pop);
+#pragma unroll
+      for (int uu = 0; uu < NU; ++uu) {
+        bf16x8 vo[DTILES];
+        vhalf(stage_c, K, uu, vo);
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+          for (int rt = 0; rt < ROWT; ++rt) acc[rt][dt] = mfma(vo[dt], pop[rt][uu], acc[rt][dt]);
+      }
+      return;
     }
     bf16x8 kop[NSUB][KSTEPS];
     kread(stage_c, K, kop);
@@ -945,7 +1026,9 @@ hipError_t launch_cfg(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEv
 // Rows per workgroup -> (row waves, key splits, row tiles per wave): up to 64
 // rows one 16-row tile per wave with the keys split over 4 or 2 waves; 128
 // rows four row waves of two row tiles each, keys split over 2 waves, so
-// every K and V operand read from LDS feeds two MFMAs.
+// every K and V operand read from LDS feeds two MFMAs; 256 rows (head dim
+// 128) eight row waves of two row tiles, each over all keys of a tile, so
+// that one workgroup, not two, streams each K/V split.
 template <int HD, int NSTAGE, bool QSEP, bool BSEP, bool KVNT>
 hipError_t launch_rows(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassEvents ev) {
   switch (pl.rows_wg / 16) {
@@ -953,6 +1036,12 @@ hipError_t launch_rows(const Plan& pl, const VerifyArgs& a, hipStream_t s, PassE
     case 2: return launch_cfg<HD, 2, 4, NSTAGE, QSEP, 1, BSEP, KVNT>(pl, a, s, ev);
     case 4: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 1, BSEP, KVNT>(pl, a, s, ev);
     case 8: return launch_cfg<HD, 4, 2, NSTAGE, QSEP, 2, BSEP, KVNT>(pl, a, s, ev);
+    case 16:
+      // the query rows borrow two of four ring stages; the block keys stream
+      // through the ring
+      if constexpr (HD == 128 && NSTAGE == 4 && !QSEP && !BSEP)
+        return launch_cfg<HD, 8, 1, NSTAGE, false, 2, false, KVNT>(pl, a, s, ev);
+      return hipErrorInvalidConfiguration;
     default: return hipErrorInvalidConfiguration;
   }
 }

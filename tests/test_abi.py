@@ -101,9 +101,12 @@ def test_mfma_grid_limits(lib):
     # the MFMA grid is (Hkv, batch x row groups, splits): y and z must stay below 2^16
     assert _ws(lib, batch=65535, B=4, n_q_heads=8, n_kv_heads=2, p_max=64)[0] == 0
     assert _ws(lib, batch=65536, B=4, n_q_heads=8, n_kv_heads=2, p_max=64, impl=L.IMPL_MFMA)[0] == L.ERR_SHAPE
-    # 128 rows per workgroup: 8 query heads per KV head x 2B = 64 -> 512 rows, 4 row groups
-    assert _ws(lib, batch=16383, B=32, n_q_heads=8, n_kv_heads=1, p_max=64, impl=L.IMPL_MFMA)[0] == 0
-    assert _ws(lib, batch=16384, B=32, n_q_heads=8, n_kv_heads=1, p_max=64, impl=L.IMPL_MFMA)[0] == L.ERR_SHAPE
+    # 256 rows per workgroup: 8 query heads per KV head x 2B = 64 -> 512 rows, 2 row groups
+    assert _ws(lib, batch=32767, B=32, n_q_heads=8, n_kv_heads=1, p_max=64, impl=L.IMPL_MFMA)[0] == 0
+    assert _ws(lib, batch=32768, B=32, n_q_heads=8, n_kv_heads=1, p_max=64, impl=L.IMPL_MFMA)[0] == L.ERR_SHAPE
+    # 128 rows per workgroup: 4 query heads per KV head x 2B = 96 -> 384 rows, 3 row groups
+    assert _ws(lib, batch=21845, B=48, n_q_heads=4, n_kv_heads=1, p_max=64, impl=L.IMPL_MFMA)[0] == 0
+    assert _ws(lib, batch=21846, B=48, n_q_heads=4, n_kv_heads=1, p_max=64, impl=L.IMPL_MFMA)[0] == L.ERR_SHAPE
     # splits of 64 keys: 65535 of them fit, one more does not
     assert _ws(lib, batch=1, p_max=64 * 65535, kv_chunk=64, impl=L.IMPL_MFMA)[0] == 0
     assert _ws(lib, batch=1, p_max=64 * 65536, kv_chunk=64, impl=L.IMPL_MFMA)[0] == L.ERR_SHAPE

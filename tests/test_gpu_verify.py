@@ -75,7 +75,7 @@ SMALL = [
     ("d64_g1", dict(NB=2, Hq=4, Hkv=4, d=64, P=200, B=3)),
     ("b1", dict(NB=3, P=130, B=1)),
     ("b64_g1", dict(NB=1, Hq=2, Hkv=2, P=100, B=64)),
-    ("b32_g4", dict(NB=1, Hq=8, Hkv=2, P=150, B=32)),       # 256 rows: two row tiles per wave
+    ("b32_g4", dict(NB=1, Hq=8, Hkv=2, P=150, B=32)),       # 256 rows: one group of eight row waves
     ("b64_g4", dict(NB=1, Hq=4, Hkv=1, P=70, B=64)),        # 512 rows: two row groups
     ("g8_b2", dict(NB=2, Hq=16, Hkv=2, P=64, B=2)),
     ("var_len", dict(NB=6, P=500, B=4, p_lo=0)),
@@ -310,7 +310,8 @@ def test_mfma_and_valu_agree_and_runs_are_deterministic():
 
 @pytest.mark.parametrize("label,ov", [("rows128", dict(NB=64, Hq=8, Hkv=2, B=16)),
                                       ("rows64", dict(NB=64, Hq=8, Hkv=2, B=8)),
-                                      ("two_row_groups", dict(NB=32, Hq=16, Hkv=2, B=16))])
+                                      ("rows256", dict(NB=64, Hq=16, Hkv=2, B=16)),
+                                      ("two_row_groups", dict(NB=32, Hq=16, Hkv=2, B=32))])
 def test_longest_first_item_order(label, ov):
     # Ragged prompts (0..2048, ties and empty splits included) in four splits of
     # 512 keys, more workgroups than the CUs hold at once: each workgroup takes
@@ -321,6 +322,36 @@ def test_longest_first_item_order(label, ov):
     plan = sd.verify_plan(sd.make_desc(t["q_blk"], t["k_blk"], t["k_cache"], rope_base=w.rope_base, kv_chunk=512))
     assert plan["lpt"] == 1 and plan["nsplit"] == 4, plan
     _check(t, w, f"longest first {label}", kv_chunk=512)
+
+
+# 256 rows per workgroup (head dim 128): eight row waves, each over all 64 keys
+# of a tile for its 32 rows, and the query rows staged in the two last ring
+# stages during the prologue.  Padded rows (160 real), block keys only,
+# block-dominated prompts, eight query heads per KV head, two groups of 256,
+# forced splits with ragged ends, custom positions and the all-visible mode.
+ROWS256 = [
+    ("m160", dict(NB=2, Hq=8, Hkv=2, P=200, B=20)),
+    ("m256_p0", dict(NB=2, Hq=8, Hkv=2, P=0, p_lo=0, B=32)),
+    ("m256_p17", dict(NB=3, Hq=8, Hkv=2, P=17, p_lo=0, B=32)),
+    ("m256_g8", dict(NB=3, Hq=16, Hkv=2, P=333, p_lo=0, B=16)),
+    ("m512", dict(NB=2, Hq=16, Hkv=2, P=150, B=32)),
+]
+
+
+@pytest.mark.parametrize("label,ov", ROWS256, ids=[s[0] for s in ROWS256])
+def test_rows256_workgroups(label, ov):
+    w = _w(**ov)
+    t = gpu_inputs(w, 61 + len(label))
+    plan = sd.verify_plan(sd.make_desc(t["q_blk"], t["k_blk"], t["k_cache"], rope_base=w.rope_base))
+    assert plan["rows_wg"] == 256 and plan["ksplit"] == 1 and plan["qsep"] == 0 and plan["blk_rows"] == 0, plan
+    _check(t, w, f"rows256 {label}", impl=sd.IMPL_MFMA)
+    if w.P > 64:
+        _check(t, w, f"rows256 {label} chunk=64", impl=sd.IMPL_MFMA, kv_chunk=64)
+    if label == "m256_p17":
+        g = torch.Generator().manual_seed(17)
+        pos_d = torch.stack([torch.randperm(w.B, generator=g) * 7 + 15000 for _ in range(w.NB)])
+        _check(t, w, f"rows256 {label} pos_d", impl=sd.IMPL_MFMA, pos_d=pos_d.to(torch.int32).to(dev()))
+        _check(t, w, f"rows256 {label} full", impl=sd.IMPL_MFMA, mask_mode=sd.MASK_FULL)
 
 
 def test_largest_batch_the_grid_takes():

@@ -46,7 +46,7 @@ def _lib_loaded():
     # they save; the 16k prompts are split at the 8192-key cap)
     ("sdar8b_p1024_b4", (32, 1, 4, 1, 4, 1, 16, 1)),
     ("sdar8b_p4096_b8", (64, 1, 2, 1, 4, 1, 16, 1)),
-    ("sdar8b_p8192_b32", (128, 2, 2, 2, 4, 0, 0, 2)),
+    ("sdar8b_p8192_b32", (256, 1, 1, 2, 4, 0, 0, 4)),
     ("sdar8b_var16k_b16_accept", (128, 1, 2, 2, 4, 0, 32, 2)),
 ])
 def test_benchmark_workload_plans(name, expect):
@@ -95,8 +95,31 @@ def test_plan_invariants_over_shapes(d, rope_mode):
             assert r % 16 == 0 and 2 * B <= r < 2 * B + 16 and 2 * B <= 64 and p["nstage"] == 4, (B, G, p)
             without = _lds_without_block_region(p, d) + LDS_RESERVE
             assert LDS_PER_CU // (p["lds_bytes"] + LDS_RESERVE) == LDS_PER_CU // without, (B, G, p)
+        if p["rows_wg"] == 256:
+            assert d == 128 and p["ksplit"] == 1 and p["row_tiles"] == 2 and p["threads"] == 512, (B, G, p)
+            assert p["nstage"] == 4 and p["qsep"] == 0 and r == 0, (B, G, p)
         seen.add(r > 0)
     assert seen == {True, False}
+
+
+def test_rows_per_workgroup():
+    # G x 2B rows per KV head: one group of the smallest power-of-two form up to
+    # 128 rows; at head dim 128 one group of 256 for 129..256 rows and groups of
+    # 256 for multiples of 256, else groups of 128 (no more padded rows than
+    # those); groups of 128 where a 256-row group would need a 3-stage ring
+    # (the table of the positions without the RoPE copy at B = 32)
+    def form(G, B, d=128, **kw):
+        p = sd.verify_plan(_desc(4, 8 * G, 8, d, B, 4096, **kw))
+        return p["rows_wg"], p["row_groups"]
+    assert form(4, 8) == (64, 1)
+    assert form(4, 16) == (128, 1)
+    assert form(4, 17) == (256, 1)   # 136 rows
+    assert form(4, 32) == (256, 1)
+    assert form(8, 32) == (256, 2)
+    assert form(4, 48) == (128, 3)   # 384 rows
+    assert form(2, 64) == (128, 2)   # 256 rows, but the 64-position table leaves only 3 stages
+    assert form(4, 32, d=64) == (128, 2)
+    assert form(4, 32, rope_mode=L.ROPE_SEQUENTIAL) == (128, 2)
 
 
 def test_default_splits_keep_at_least_16_tiles():
