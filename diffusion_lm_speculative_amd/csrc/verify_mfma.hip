@@ -826,11 +826,28 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
     finish(IC<1>{}, sb, vop, cm);
   }
   const int nfull = (c1 - c0) / KT;  // whole prompt tiles: nbt .. nbt + nfull - 1
-  if (T >= NSTAGE)
-    lds_barrier<(NSTAGE - 1) * LPW>();  // tile 0 landed
-  else
-    lds_barrier<0>();
-  if (nbt > 0) rotate_block(0, 0);
+  // Wide blocks (two row tiles a wave: the step is bound by the work inside
+  // the CU, not by memory) take one barrier per pair of tiles: tiles t and
+  // t+1 are waited for together at even steps, so two are in flight while
+  // two are in use.
+  constexpr bool kPairs = ROWT == 2 && NSTAGE == 4;
+  if constexpr (kPairs) {
+    const int ahead = min(T, NSTAGE) - 2;  // tiles issued beyond tiles 0 and 1
+    if (ahead >= 2)
+      lds_barrier<2 * LPW>();
+    else if (ahead == 1)
+      lds_barrier<LPW>();
+    else
+      lds_barrier<0>();  // tiles 0 and 1 landed
+    if (nbt > 0) rotate_block(0, 0);
+    if (nbt > 1) rotate_block(1, 1);
+  } else {
+    if (T >= NSTAGE)
+      lds_barrier<(NSTAGE - 1) * LPW>();  // tile 0 landed
+    else
+      lds_barrier<0>();
+    if (nbt > 0) rotate_block(0, 0);
+  }
   // Step t waits for tile t only (the barrier also frees the stage of tile
   // t-1, refilled at once), then reads K and V of tile t and runs its score
   // MFMAs, softmax and PV MFMAs, so three tiles stay in flight behind the one
@@ -842,7 +859,15 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
   auto step = [&](auto mode_c, auto stage_c, int t) __attribute__((always_inline)) {
     constexpr int SC = decltype(stage_c)::value;
     const int K = SC >= 0 ? SC : t % NSTAGE;
-    if (t > 0) {
+    if constexpr (kPairs) {
+      // even steps wait for tiles t and t+1 (nothing else is in flight) and
+      // refill the stages of t-2 and t-1; odd steps pass straight on
+      if (t > 0 && (t & 1) == 0) {
+        lds_barrier<0>();
+        if (t + 2 < T) issue((K + NSTAGE - 2) % NSTAGE, t + 2, c1);
+        if (t + 3 < T) issue((K + NSTAGE - 1) % NSTAGE, t + 3, c1);
+      }
+    } else if (t > 0) {
       const int later = T - 1 - t;  // tiles after t that may still be in flight (at most NSTAGE - 2)
       if (later >= NSTAGE - 2)
         lds_barrier<(NSTAGE - 2) * LPW>();
@@ -854,8 +879,7 @@ __global__ __launch_bounds__(RW * KSPLIT * 64) void verify_mfma_kernel(Plan pl, 
       if (t < nbt) rotate_block(K, t);
     }
     if constexpr (KSPLIT == 1) {
-      // scores subtile by subtile, the softmax, then P V half by half (the
-      // V reads of the first half go out under the softmax)
+      // scores subtile by subtile, the softmax, then P V half by half
 #pragma unroll
       for (int i = 0; i < NSUB; ++i) {
         bf16x8 ko[KSTEPS];

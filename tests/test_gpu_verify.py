@@ -185,7 +185,7 @@ def _tied_tau(kind, NB, B, g):
 
 @pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
 @pytest.mark.parametrize("kind", ["all1", "steps", "random"])
-@pytest.mark.parametrize("B,P", [(4, 17), (8, 0), (16, 130)])
+@pytest.mark.parametrize("B,P", [(4, 17), (8, 0), (16, 130), (32, 70)])
 def test_tied_stage_labels(kind, B, P, impl):
     w = _w(NB=3, Hq=8, Hkv=2, P=P, p_lo=0, B=B)
     t = gpu_inputs(w, 101 + B + P)
@@ -251,20 +251,21 @@ def test_cache_rows_past_prompt_len_are_never_read(impl):
 
 @pytest.mark.parametrize("impl", [sd.IMPL_MFMA, sd.IMPL_VALU])
 @pytest.mark.parametrize("big", [12.0, 200.0])
-def test_late_keys_far_above_the_first_tiles(impl, big):
+@pytest.mark.parametrize("B", [4, 32])
+def test_late_keys_far_above_the_first_tiles(impl, big, B):
     # A few late prompt keys score far above everything before them (by
     # hundreds of log2 units for big=200): probabilities taken relative to an
     # early reference would overflow, so the result must still match.  The
     # block rows sit at RoPE position 0, where the rotation is exact, so the
     # bf16 query operand carries no rounding that keys this long would
-    # magnify beyond the bf16 tolerance.
-    w = _w(NB=2, Hq=8, Hkv=2, P=600, B=4)
+    # magnify beyond the bf16 tolerance.  B = 32: 256 rows per workgroup.
+    w = _w(NB=2, Hq=8, Hkv=2, P=600, B=B)
     t = gpu_inputs(w, 101)
     t["k_cache"][:, :, 590:593] = big
     t["k_cache"][1, :, 300] = -big
-    pos_d = torch.zeros((2, 4), dtype=torch.int32, device=dev())
+    pos_d = torch.zeros((2, B), dtype=torch.int32, device=dev())
     for kv_chunk in (0, 128, 640):
-        out, lse, _ = _check(t, w, f"late big keys {big} chunk={kv_chunk}", impl=impl, kv_chunk=kv_chunk,
+        out, lse, _ = _check(t, w, f"late big keys {big} B={B} chunk={kv_chunk}", impl=impl, kv_chunk=kv_chunk,
                              pos_d=pos_d)
         assert torch.isfinite(out).all() and torch.isfinite(lse).all()
 
@@ -273,8 +274,8 @@ def test_late_keys_far_above_the_first_tiles(impl, big):
 def test_scores_rising_in_steps_across_tiles(impl):
     # keys whose scores climb tile after tile, each step a few tens of log2
     # units: the row's reference has to move up several times within one
-    # split, and the rows of the wider block (128 rows per workgroup) too
-    for B, Hq in ((4, 8), (16, 8)):
+    # split, and the rows of the wider blocks (128 and 256 rows per workgroup) too
+    for B, Hq in ((4, 8), (16, 8), (32, 8)):
         w = _w(NB=2, Hq=Hq, Hkv=2, P=900, p_lo=800, B=B)
         t = gpu_inputs(w, 111 + B)
         for i in range(1, 9):
