@@ -1,9 +1,9 @@
 """GPU parity of simsd_verify_attn (through the C ABI) against the fp64 oracle.
 
 Small cases cover several key tiles, ragged tails, forced prompt splits,
-every MFMA row-tiling variant, d = 64 and 128, B = 1 .. 64, variable prompt
-lengths (including 0), custom RoPE positions, the all-visible mode and
-faulted sequences.  The SDAR-shaped workloads run at full size in the
+every MFMA row-tiling variant (up to 256 rows a workgroup), d = 64 and 128,
+B = 1 .. 64, variable prompt lengths (including 0), custom RoPE positions,
+the all-visible mode and faulted sequences.  The SDAR-shaped workloads run at full size in the
 launch configuration the benchmark times, compared on sampled sequences.
 Block-dominated cases (P = 0, 1, 17) and fp32 runs at SDAR head shapes make
 mask and RoPE mistakes visible despite the bf16 tolerance.
@@ -353,6 +353,21 @@ def test_rows256_workgroups(label, ov):
         pos_d = torch.stack([torch.randperm(w.B, generator=g) * 7 + 15000 for _ in range(w.NB)])
         _check(t, w, f"rows256 {label} pos_d", impl=sd.IMPL_MFMA, pos_d=pos_d.to(torch.int32).to(dev()))
         _check(t, w, f"rows256 {label} full", impl=sd.IMPL_MFMA, mask_mode=sd.MASK_FULL)
+
+
+@pytest.mark.parametrize("label,ov", [("rows128", dict(Hq=8, Hkv=2, B=16)), ("rows256", dict(Hq=8, Hkv=2, B=32))])
+def test_wide_block_tile_counts(label, ov):
+    # The wide forms (two row tiles a wave) wait for their tiles in pairs.
+    # Prompts of 0 .. 522 keys give 1 to 10 tiles in one split (the block
+    # tiles first), odd and even counts with ragged ends, and splits of three
+    # tiles give 1 to 4 per split.
+    w = _w(NB=9, P=522, p_lo=0, **ov)
+    t = gpu_inputs(w, 171 + w.B)
+    t["prompt_len"][:] = torch.tensor([0, 1, 64, 65, 128, 190, 256, 300, 522], dtype=torch.int32)
+    plan = sd.verify_plan(sd.make_desc(t["q_blk"], t["k_blk"], t["k_cache"], rope_base=w.rope_base))
+    assert plan["row_tiles"] == 2 and plan["nstage"] == 4, plan
+    for kv_chunk in (0, 192):
+        _check(t, w, f"wide tiles {label} chunk={kv_chunk}", impl=sd.IMPL_MFMA, kv_chunk=kv_chunk)
 
 
 def test_largest_batch_the_grid_takes():
