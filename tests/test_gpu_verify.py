@@ -328,7 +328,7 @@ def test_longest_first_item_order(label, ov):
 # 256 rows per workgroup (head dim 128): eight row waves, each over all 64 keys
 # of a tile for its 32 rows, and the query rows staged in the two last ring
 # stages during the prologue.  Padded rows (160 real), block keys only,
-# block-dominated prompts, eight query heads per KV head, two groups of 256,
+# block-dominated prompts, eight query heads per KV head, two groups of 256, two block tiles,
 # forced splits with ragged ends, custom positions and the all-visible mode.
 ROWS256 = [
     ("m160", dict(NB=2, Hq=8, Hkv=2, P=200, B=20)),
@@ -336,6 +336,7 @@ ROWS256 = [
     ("m256_p17", dict(NB=3, Hq=8, Hkv=2, P=17, p_lo=0, B=32)),
     ("m256_g8", dict(NB=3, Hq=16, Hkv=2, P=333, p_lo=0, B=16)),
     ("m512", dict(NB=2, Hq=16, Hkv=2, P=150, B=32)),
+    ("m160_b40", dict(NB=2, Hq=4, Hkv=2, P=150, B=40)),    # two block tiles ahead of the prompt
 ]
 
 
